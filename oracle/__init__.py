@@ -1,0 +1,187 @@
+"""CPU oracle for the sparse-attention decode step.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The GPU library never imports,
+links or calls it, and it imports nothing from the GPU library.
+
+``oracle.c`` holds the plain double-precision definitions (indexer score,
+top-k by a full sort, softmax attention, the composed step); this module
+compiles it with gcc into ``liboracle.so`` on first use and exposes numpy
+wrappers. ``brute.py`` holds pure-Python O(N^2) and closed-form checks for tiny
+inputs that pin the C code.
+
+Sources: "feat: Add DeepSeek-V4 CSA attention kernels" (aws-neuron
+nki-library pull request 13), section "How the algorithm works", steps 2-4;
+"DeepSelect" project page (deepseek-ai/DeepSelect), algorithm and scenario
+paragraphs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+BF16 = 0
+F32 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP) into liboracle.so."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = build(force=False)
+            lib = ctypes.CDLL(path)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            lib.oracle_bf16_decode.argtypes = [P, P, ctypes.c_int64]
+            lib.oracle_bf16_decode.restype = None
+            lib.oracle_indexer.argtypes = [P, P, P, P, I, I, I, I]
+            lib.oracle_indexer.restype = None
+            lib.oracle_topk.argtypes = [P, I, I, I, I, P, I]
+            lib.oracle_topk.restype = I
+            lib.oracle_attend.argtypes = [P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double]
+            lib.oracle_attend.restype = I
+            lib.oracle_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                        ctypes.c_double]
+            lib.oracle_step.restype = I
+            lib.oracle_set_threads.argtypes = [I]
+            lib.oracle_set_threads.restype = None
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = I
+            _lib = lib
+    return _lib
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP thread count used by the C oracle (it only splits rows)."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    """Threads the C oracle's parallel loops will use."""
+    return int(_load().oracle_max_threads())
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    bits = _c(bits, np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    _load().oracle_bf16_decode(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+def indexer(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Indexer scores. q_idx uint16(bf16) [B,H,D], k_idx uint16 [B,N,D],
+    w float32 [B,H] -> float32 [B,N]."""
+    q_idx = _c(q_idx, np.uint16)
+    k_idx = _c(k_idx, np.uint16)
+    w = _c(w, np.float32)
+    B, H, D = q_idx.shape
+    N = k_idx.shape[1]
+    assert k_idx.shape == (B, N, D) and w.shape == (B, H)
+    s = np.empty((B, N), np.float32)
+    _load().oracle_indexer(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(s), B, N, H, D)
+    return s
+
+
+def topk(scores: np.ndarray, k: int, index_order: bool = False) -> np.ndarray:
+    """Top-k indices per row. scores: float32 [B,N] or uint16 bf16 bits [B,N].
+    Order: value desc then index asc, or ascending index if index_order."""
+    scores = np.ascontiguousarray(scores)
+    if scores.dtype == np.uint16:
+        dt = BF16
+    elif scores.dtype == np.float32:
+        dt = F32
+    else:
+        raise TypeError("scores must be float32 or uint16 (bf16 bits)")
+    B, N = scores.shape
+    idx = np.empty((B, k), np.int32)
+    rc = _load().oracle_topk(_ptr(scores), dt, B, N, int(k), _ptr(idx), int(bool(index_order)))
+    if rc != 0:
+        raise ValueError("oracle_topk: invalid arguments")
+    return idx
+
+
+def attend(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win: np.ndarray | None,
+           scale: float) -> np.ndarray:
+    """Sparse attention. q uint16 [B,Hq,D], kv uint16 [B,N,D], idx int32 [B,k],
+    win uint16 [B,W,D] or None -> float64 [B,Hq,D]."""
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    idx = _c(idx, np.int32)
+    B, Hq, D = q.shape
+    N = kv.shape[1]
+    k = idx.shape[1]
+    if win is None or win.size == 0:
+        W = 0
+        win = np.zeros((1,), np.uint16)
+    else:
+        win = _c(win, np.uint16)
+        W = win.shape[1]
+        assert win.shape == (B, W, D)
+    out = np.empty((B, Hq, D), np.float64)
+    rc = _load().oracle_attend(_ptr(q), _ptr(kv), _ptr(idx), _ptr(win), _ptr(out),
+                               B, N, k, W, Hq, D, float(scale))
+    if rc != 0:
+        raise ValueError("oracle_attend: index out of range or empty row set")
+    return out
+
+
+def step(q_idx, k_idx, w, q, kv, win, k: int, scale: float):
+    """Whole decode step; returns (scores float32 [B,N], idx int32 [B,k] in
+    value-desc order, out float64 [B,Hq,D])."""
+    q_idx = _c(q_idx, np.uint16)
+    k_idx = _c(k_idx, np.uint16)
+    w = _c(w, np.float32)
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    B, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq, D = q.shape[1], q.shape[2]
+    if win is None or win.size == 0:
+        W = 0
+        win = np.zeros((1,), np.uint16)
+    else:
+        win = _c(win, np.uint16)
+        W = win.shape[1]
+    scores = np.empty((B, N), np.float32)
+    idx = np.empty((B, k), np.int32)
+    out = np.empty((B, Hq, D), np.float64)
+    rc = _load().oracle_step(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv), _ptr(win),
+                             _ptr(scores), _ptr(idx), _ptr(out), B, N, H, DI, int(k), W, Hq, D,
+                             float(scale))
+    if rc != 0:
+        raise ValueError("oracle_step: invalid arguments")
+    return scores, idx, out

@@ -1,0 +1,232 @@
+/*
+ * CPU oracle for the sparse-attention decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * definition that the GPU library is checked against. Nothing in the GPU
+ * library includes, links or calls it; only the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark load it. It shares no code, header,
+ * table or helper with the HIP sources.
+ *
+ * Sources (cited by page title and section):
+ *  [CSA]  "feat: Add DeepSeek-V4 CSA attention kernels" (aws-neuron
+ *         nki-library pull request 13), section "How the algorithm works",
+ *         the step table (steps 2, 3, 4), and the paragraph after the GpSimd
+ *         bullet list (K and V are the same embedding).
+ *  [DS]   "DeepSelect" project page (deepseek-ai/DeepSelect), the algorithm
+ *         and scenario paragraphs (top-k by score, sorted_index and
+ *         return_value options).
+ *  [PTB]  "Implementation: Deepspeedai DeepSpeed Inference PT Binding",
+ *         Usage Examples (norm_factor = 1/sqrt(head_dim) scales q.k).
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - indexer: ReLU is applied per head to the q.k product, then the result is
+ *    multiplied by that head's weight, then summed over heads; no other scale.
+ *  - scores are accumulated in double and rounded once to float.
+ *  - top-k order: value descending, ties broken by lower index; -0 == +0.
+ *  - attention: rows = selected compressed rows followed by the W window
+ *    rows; the same row serves as key and value; plain softmax, no mask.
+ *
+ * Every floating-point step runs in double. bf16 inputs are decoded exactly.
+ * OpenMP, when enabled, only splits independent batch rows; the result does
+ * not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Thread count for the row-parallel loops (1 when built without OpenMP). */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* bf16 is the top half of an IEEE binary32: widening is exact. */
+static double bf16_value(uint16_t bits) {
+  uint32_t w = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+void oracle_bf16_decode(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_value(in[i]);
+}
+
+/*
+ * Lightning-indexer score [CSA, step 2]:
+ *   s[b,j] = sum_h w[b,h] * max(0, sum_d q[b,h,d] * k[b,j,d])
+ * q: bf16 [B,H,D], k: bf16 [B,N,D], w: float [B,H], s: float [B,N].
+ */
+void oracle_indexer(const uint16_t* q, const uint16_t* k, const float* w,
+                    float* s, int B, int N, int H, int D) {
+#pragma omp parallel for schedule(static)
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j < N; ++j) {
+      const uint16_t* krow = k + ((int64_t)b * N + j) * D;
+      double total = 0.0;
+      for (int h = 0; h < H; ++h) {
+        const uint16_t* qrow = q + ((int64_t)b * H + h) * D;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += bf16_value(qrow[d]) * bf16_value(krow[d]);
+        double relu = dot > 0.0 ? dot : 0.0;
+        total += (double)w[(int64_t)b * H + h] * relu;
+      }
+      s[(int64_t)b * N + j] = (float)total;
+    }
+  }
+}
+
+/*
+ * Top-k [CSA step 3; DS]: the k positions with the largest score. The order
+ * used is the one a stable sort by descending value gives: a larger value
+ * comes first, and of two equal values the lower index comes first. The
+ * comparison is between IEEE values, so -0.0 and +0.0 are equal.
+ */
+typedef struct {
+  double v;
+  int32_t i;
+} keyed_t;
+
+static int by_value_desc_then_index(const void* pa, const void* pb) {
+  const keyed_t* a = (const keyed_t*)pa;
+  const keyed_t* b = (const keyed_t*)pb;
+  if (a->v > b->v) return -1;
+  if (a->v < b->v) return 1;
+  return (a->i > b->i) - (a->i < b->i);
+}
+
+static int by_index(const void* pa, const void* pb) {
+  int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+  return (a > b) - (a < b);
+}
+
+/* One row: vals[N] (already decoded) -> idx[k]. index_order: 0 gives the
+ * (value desc, index asc) order, 1 gives ascending index order. */
+static void topk_row(const double* vals, int N, int k, int32_t* idx,
+                     int index_order, keyed_t* tmp) {
+  for (int j = 0; j < N; ++j) {
+    tmp[j].v = vals[j];
+    tmp[j].i = j;
+  }
+  qsort(tmp, (size_t)N, sizeof(keyed_t), by_value_desc_then_index);
+  for (int t = 0; t < k; ++t) idx[t] = tmp[t].i;
+  if (index_order) qsort(idx, (size_t)k, sizeof(int32_t), by_index);
+}
+
+/* dtype: 0 = bf16 bits (uint16), 1 = float32. Returns 0, or -1 on bad args. */
+int oracle_topk(const void* scores, int dtype, int B, int N, int k,
+                int32_t* idx, int index_order) {
+  if (B < 1 || N < 1 || k < 1 || k > N || (dtype != 0 && dtype != 1)) return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* vals = (double*)malloc(sizeof(double) * (size_t)N);
+    keyed_t* tmp = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)N);
+    if (!vals || !tmp) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < N; ++j) {
+          int64_t at = (int64_t)b * N + j;
+          vals[j] = dtype == 0 ? bf16_value(((const uint16_t*)scores)[at])
+                               : (double)((const float*)scores)[at];
+        }
+        topk_row(vals, N, k, idx + (int64_t)b * k, index_order, tmp);
+      }
+    }
+    free(vals);
+    free(tmp);
+  }
+  return bad ? -1 : 0;
+}
+
+/*
+ * Sparse multi-query attention for one decode token [CSA step 4; PTB]:
+ *   R_b = rows kv[b, idx[b,0..k)] followed by rows win[b, 0..W)
+ *   z[h,r] = scale * q[b,h,:] . R_b[r,:]
+ *   p[h,:] = softmax over r of z[h,:]
+ *   out[b,h,:] = sum_r p[h,r] * R_b[r,:]          (the row is key and value)
+ * q: bf16 [B,Hq,D]; kv: bf16 [B,N,D]; idx: int32 [B,k] with values in [0,N);
+ * win: bf16 [B,W,D] (unused when W == 0); out: double [B,Hq,D].
+ * Returns 0, or -1 if an index is out of range.
+ */
+int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                  const uint16_t* win, double* out, int B, int N, int k, int W,
+                  int Hq, int D, double scale) {
+  for (int64_t t = 0; t < (int64_t)B * k; ++t)
+    if (idx[t] < 0 || idx[t] >= N) return -1;
+  const int R = k + W;
+  if (R < 1) return -1;
+#pragma omp parallel
+  {
+    double* rows = (double*)malloc(sizeof(double) * (size_t)R * (size_t)D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)R);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+#pragma omp for schedule(static)
+    for (int b = 0; b < B; ++b) {
+      for (int r = 0; r < R; ++r) {
+        const uint16_t* src =
+            r < k ? kv + ((int64_t)b * N + idx[(int64_t)b * k + r]) * D
+                  : win + ((int64_t)b * W + (r - k)) * D;
+        for (int d = 0; d < D; ++d) rows[(int64_t)r * D + d] = bf16_value(src[d]);
+      }
+      for (int h = 0; h < Hq; ++h) {
+        const uint16_t* qrow = q + ((int64_t)b * Hq + h) * D;
+        for (int d = 0; d < D; ++d) qd[d] = bf16_value(qrow[d]);
+        double m = -INFINITY;
+        for (int r = 0; r < R; ++r) {
+          double dot = 0.0;
+          for (int d = 0; d < D; ++d) dot += qd[d] * rows[(int64_t)r * D + d];
+          z[r] = scale * dot;
+          if (z[r] > m) m = z[r];
+        }
+        double l = 0.0;
+        for (int r = 0; r < R; ++r) {
+          z[r] = exp(z[r] - m);
+          l += z[r];
+        }
+        double* o = out + ((int64_t)b * Hq + h) * D;
+        for (int d = 0; d < D; ++d) {
+          double acc = 0.0;
+          for (int r = 0; r < R; ++r) acc += z[r] * rows[(int64_t)r * D + d];
+          o[d] = acc / l;
+        }
+      }
+    }
+    free(rows);
+    free(z);
+    free(qd);
+  }
+  return 0;
+}
+
+/*
+ * The whole decode step [CSA, steps 2 -> 3 -> 4]: indexer scores, then the
+ * top-k of each score row, then attention over the selected rows plus the
+ * window. scores [B,N] and idx [B,k] (value-desc order) are outputs too.
+ */
+int oracle_step(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                const uint16_t* q, const uint16_t* kv, const uint16_t* win,
+                float* scores, int32_t* idx, double* out, int B, int N, int H,
+                int DI, int k, int W, int Hq, int D, double scale) {
+  oracle_indexer(q_idx, k_idx, w, scores, B, N, H, DI);
+  if (oracle_topk(scores, 1, B, N, k, idx, 0) != 0) return -1;
+  return oracle_attend(q, kv, idx, win, out, B, N, k, W, Hq, D, scale);
+}

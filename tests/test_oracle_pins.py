@@ -1,0 +1,321 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: a library
+routine (torch's bf16 conversion, torch.matmul, torch.topk,
+scaled_dot_product_attention), a closed form, an invariant, or the O(N^2)
+rank definition of top-k in oracle/brute.py. Cases are chosen so that a
+dropped term, a wrong sign, a wrong index or a transposed operand in the
+oracle fails at least one of them.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+import workloads
+
+
+def bf16_bits(x: torch.Tensor) -> np.ndarray:
+    return workloads.bits16(x.to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_bf16_decode_matches_torch_on_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    man = bits & 0x7F
+    keep = ~((exp == 0xFF) & (man != 0))  # drop NaNs
+    bits = bits[keep]
+    got = oracle.bf16_decode(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64)
+    assert np.array_equal(got, ref.numpy())
+
+
+# ---------------------------------------------------------------- indexer
+
+def test_indexer_single_head_is_relu_of_matmul():
+    """H=1, w=1: the score is ReLU(K q), checked against torch.matmul in fp64."""
+    g = torch.Generator().manual_seed(11)
+    B, N, D = 3, 257, 128
+    q = torch.randn(B, 1, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    w = np.ones((B, 1), np.float32)
+    got = oracle.indexer(bf16_bits(q), bf16_bits(k), w)
+    ref = torch.relu(torch.matmul(k.double(), q.double().transpose(1, 2)))[..., 0]
+    ref32 = ref.float().numpy()
+    # The fp64 sums may differ in order; after rounding to fp32 at most 1 ulp apart.
+    assert np.all(np.abs(got - ref32) <= np.spacing(np.abs(ref32)) + 0.0)
+    assert (ref32 == 0).sum() > 100  # ReLU actually clipped many scores
+
+
+def _dyadic_bf16(g, shape, lo=-16, hi=16, denom=8):
+    """Values m/denom with integer m in [lo, hi): exact in bf16."""
+    m = torch.randint(lo, hi, shape, generator=g)
+    return (m.double() / denom)
+
+
+def test_indexer_one_hot_closed_form_exact():
+    """One-hot indexer queries q[b,h] = c_h * e_{d_h}: the score is
+    sum_h w[b,h] * max(0, c_h * K[b,j,d_h]), evaluated exactly with Fractions.
+    Distinct channels, signs and weights per (b,h) catch transposed or shifted
+    indices, a missing ReLU and a wrong head weight."""
+    g = torch.Generator().manual_seed(5)
+    B, N, H, D = 2, 33, 5, 16
+    K = _dyadic_bf16(g, (B, N, D))
+    chans = [[(3 * h + 7 * b + 1) % D for h in range(H)] for b in range(B)]
+    coefs = [[[1.0, -1.0, 0.5, 2.0, -0.25][(h + b) % 5] for h in range(H)] for b in range(B)]
+    Q = torch.zeros(B, H, D, dtype=torch.float64)
+    for b in range(B):
+        for h in range(H):
+            Q[b, h, chans[b][h]] = coefs[b][h]
+    wv = np.array([[(h + 1) / 8 + b / 4 for h in range(H)] for b in range(B)], np.float32)
+    got = oracle.indexer(bf16_bits(Q), bf16_bits(K), wv)
+    for b in range(B):
+        for j in range(N):
+            s = Fraction(0)
+            for h in range(H):
+                prod = Fraction(coefs[b][h]) * Fraction(float(K[b, j, chans[b][h]]))
+                s += Fraction(float(wv[b, h])) * max(Fraction(0), prod)
+            assert got[b, j] == float(s), (b, j)
+
+
+def test_indexer_relu_before_weight():
+    """The ReLU acts on q.k, then the weight multiplies: with a negative
+    weight the score is -ReLU(q.k), never ReLU(-q.k)."""
+    q = torch.zeros(1, 1, 8, dtype=torch.float64)
+    q[0, 0, 2] = 1.0
+    k = torch.zeros(1, 2, 8, dtype=torch.float64)
+    k[0, 0, 2] = 3.0
+    k[0, 1, 2] = -3.0
+    w = np.array([[-0.5]], np.float32)
+    got = oracle.indexer(bf16_bits(q), bf16_bits(k), w)
+    assert got.tolist() == [[-1.5, 0.0]]
+
+
+def test_indexer_weight_scaling_and_head_permutation():
+    g = torch.Generator().manual_seed(9)
+    B, N, H, D = 2, 129, 8, 128
+    q = torch.randn(B, H, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    w = torch.rand(B, H, generator=g).numpy().astype(np.float32)
+    s1 = oracle.indexer(bf16_bits(q), bf16_bits(k), w)
+    s2 = oracle.indexer(bf16_bits(q), bf16_bits(k), 2 * w)
+    assert np.array_equal(s2, 2 * s1)  # power-of-two scaling is exact
+    perm = torch.randperm(H, generator=g)
+    s3 = oracle.indexer(bf16_bits(q[:, perm]), bf16_bits(k), np.ascontiguousarray(w[:, perm]))
+    assert np.all(np.abs(s3 - s1) <= np.spacing(np.abs(s1)))
+    # Batch rows are independent: swapping batches swaps score rows.
+    s4 = oracle.indexer(bf16_bits(q.flip(0)), bf16_bits(k.flip(0)), np.ascontiguousarray(w[::-1]))
+    assert np.array_equal(s4, s1[::-1])
+
+
+def test_indexer_stress_construction_is_exact():
+    """The stress workload's indexer inputs reproduce its quantised score rows
+    exactly (first unit vector queries, weights 1/H)."""
+    s = workloads.StepShape(B=2, N=3000, H_I=64, D_I=128, k=16, W=0, H_q=16, D=128)
+    inp = workloads.stress_step_inputs(s, 5000)
+    got = oracle.indexer(bf16_bits(inp["q_idx"]), bf16_bits(inp["k_idx"]), inp["w"].numpy())
+    assert np.array_equal(got, inp["stress_scores"].float().numpy())
+
+
+# ---------------------------------------------------------------- top-k
+
+def _rows_with_ties(g, B, N, levels):
+    return (torch.randint(0, levels, (B, N), generator=g).float() - levels / 2) / 4
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_rank_definition(seed):
+    g = torch.Generator().manual_seed(100 + seed)
+    N = [1, 7, 64, 130, 250, 300][seed]
+    k = max(1, [1, 3, 17, 64, 250, 150][seed])
+    k = min(k, N)
+    x = _rows_with_ties(g, 3, N, levels=[2, 3, 5, 9, 40, 1000][seed])
+    # sprinkle signed zeros and infinities
+    if N > 4:
+        x[0, 0] = -0.0
+        x[0, 1] = 0.0
+        x[1, 2] = float("inf")
+        x[2, 3] = float("-inf")
+    got = oracle.topk(x.numpy(), k)
+    for b in range(x.shape[0]):
+        assert got[b].tolist() == brute.rank_select(x[b].tolist(), k)
+
+
+def test_topk_bf16_input_equals_decoded_input():
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(4, 2000, generator=g).to(torch.bfloat16)
+    a = oracle.topk(bf16_bits(x), 100)
+    b = oracle.topk(x.float().numpy(), 100)
+    assert np.array_equal(a, b)
+
+
+def test_topk_invariants_and_torch_values():
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(5, 20000, generator=g).to(torch.bfloat16).float()  # many ties
+    k = 333
+    idx = oracle.topk(x.numpy(), k)
+    for b in range(5):
+        sel = idx[b]
+        assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < 20000
+        mask = np.zeros(20000, bool)
+        mask[sel] = True
+        vals = x[b].numpy()
+        mn = vals[mask].min()
+        assert vals[~mask].max() <= mn
+        # tied values at the boundary: selected ones have the smaller indices
+        tied_sel = np.nonzero(mask & (vals == mn))[0]
+        tied_out = np.nonzero(~mask & (vals == mn))[0]
+        if tied_out.size:
+            assert tied_sel.max() < tied_out.min()
+        ref = torch.topk(x[b], k).values.numpy()
+        assert np.array_equal(np.sort(vals[sel]), np.sort(ref))
+    # the default order is value desc, index asc
+    v = x[0].numpy()[idx[0]]
+    assert np.all(np.diff(v) <= 0)
+
+
+def test_topk_special_rows():
+    N, k = 1000, 37
+    rows = np.stack([
+        np.full(N, 0.5, np.float32),                   # all equal
+        np.arange(N, dtype=np.float32),                # ascending
+        np.arange(N, 0, -1).astype(np.float32),        # descending
+    ])
+    idx = oracle.topk(rows, k, index_order=True)
+    assert idx[0].tolist() == list(range(k))
+    assert idx[1].tolist() == list(range(N - k, N))
+    assert idx[2].tolist() == list(range(k))
+    full = oracle.topk(rows, N, index_order=True)
+    assert all(full[b].tolist() == list(range(N)) for b in range(3))
+
+
+def test_topk_index_order_is_sorted_same_set():
+    g = torch.Generator().manual_seed(8)
+    x = torch.randn(3, 5000, generator=g)
+    a = oracle.topk(x.numpy(), 200, index_order=False)
+    b = oracle.topk(x.numpy(), 200, index_order=True)
+    assert np.array_equal(np.sort(a, axis=1), b)
+
+
+def test_topk_rejects_bad_k():
+    with pytest.raises(ValueError):
+        oracle.topk(np.zeros((1, 4), np.float32), 5)
+
+
+# ---------------------------------------------------------------- attention
+
+def _sdpa_ref(q, rows, scale):
+    """torch scaled_dot_product_attention in fp64; q [B,Hq,D], rows [B,R,D]."""
+    B, Hq, D = q.shape
+    qq = q.double().unsqueeze(2)                        # [B,Hq,1,D]
+    kk = rows.double().unsqueeze(1).expand(B, Hq, rows.shape[1], D)
+    out = torch.nn.functional.scaled_dot_product_attention(qq, kk, kk, scale=scale)
+    return out[:, :, 0, :].numpy()
+
+
+def test_attend_dense_equals_sdpa():
+    """k = N and W = 0 select every row: the result is dense MQA."""
+    g = torch.Generator().manual_seed(21)
+    B, N, Hq, D = 2, 96, 16, 128
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(N, generator=g) for _ in range(B)]).int()
+    scale = 1 / math.sqrt(D)
+    got = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), None, scale)
+    ref = _sdpa_ref(q, kv, scale)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attend_sparse_with_window_equals_sdpa_on_gathered_rows():
+    g = torch.Generator().manual_seed(22)
+    B, N, k, W, Hq, D = 3, 200, 40, 9, 16, 128
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    win = torch.randn(B, W, D, generator=g).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(N, generator=g)[:k] for _ in range(B)]).int()
+    scale = 0.07
+    got = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), scale)
+    rows = torch.cat([torch.stack([kv[b, idx[b].long()] for b in range(B)]), win], dim=1)
+    ref = _sdpa_ref(q, rows, scale)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attend_closed_forms():
+    g = torch.Generator().manual_seed(23)
+    B, N, Hq, D = 1, 10, 16, 128
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    kvd = kv.double().numpy()
+    # one row: the output is that row, for every head
+    out = oracle.attend(bf16_bits(q), bf16_bits(kv), np.array([[6]], np.int32), None, 0.3)
+    assert np.array_equal(out[0], np.broadcast_to(kvd[0, 6], (Hq, D)))
+    # zero query: uniform weights, the mean of the rows
+    z = torch.zeros_like(q)
+    idx = np.array([[1, 4, 9]], np.int32)
+    out = oracle.attend(bf16_bits(z), bf16_bits(kv), idx, None, 0.3)
+    assert np.max(np.abs(out[0] - kvd[0, [1, 4, 9]].mean(0))) < 1e-15
+    # two rows: logistic weights of the logit gap
+    idx = np.array([[2, 5]], np.int32)
+    scale = 0.11
+    out = oracle.attend(bf16_bits(q), bf16_bits(kv), idx, None, scale)
+    qd = q.double().numpy()[0]
+    for h in range(Hq):
+        z1 = scale * float(np.dot(qd[h], kvd[0, 2]))
+        z2 = scale * float(np.dot(qd[h], kvd[0, 5]))
+        a, b = brute.softmax_weights_two_rows(z1, z2)
+        assert np.max(np.abs(out[0, h] - (a * kvd[0, 2] + b * kvd[0, 5]))) < 1e-12
+
+
+def test_attend_window_rows_equal_selected_rows_and_permutation():
+    g = torch.Generator().manual_seed(24)
+    B, N, Hq, D = 2, 50, 16, 128
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    sel = torch.tensor([[3, 17, 40, 41, 8], [0, 1, 2, 49, 30]], dtype=torch.int32)
+    a = oracle.attend(bf16_bits(q), bf16_bits(kv), sel.numpy(), None, 0.2)
+    # the same rows handed over as the window (plus one selected row)
+    win = torch.stack([kv[b, sel[b, 1:].long()] for b in range(B)])
+    b_ = oracle.attend(bf16_bits(q), bf16_bits(kv), sel[:, :1].contiguous().numpy(),
+                       bf16_bits(win), 0.2)
+    assert np.max(np.abs(a - b_)) < 1e-13
+    perm = sel[:, torch.tensor([4, 2, 0, 3, 1])].contiguous()
+    c = oracle.attend(bf16_bits(q), bf16_bits(kv), perm.numpy(), None, 0.2)
+    assert np.max(np.abs(a - c)) < 1e-13
+
+
+def test_attend_rejects_out_of_range_index():
+    q = np.zeros((1, 16, 128), np.uint16)
+    kv = np.zeros((1, 4, 128), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.attend(q, kv, np.array([[4]], np.int32), None, 1.0)
+
+
+# ---------------------------------------------------------------- step
+
+def test_step_is_the_composition():
+    s = workloads.StepShape(B=2, N=300, H_I=8, D_I=128, k=20, W=5, H_q=16, D=128)
+    inp = workloads.step_inputs(s, 77000)
+    b = {k_: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.numpy()) for k_, v in inp.items()}
+    scores, idx, out = oracle.step(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"],
+                                   b["kv_win"], s.k, s.scale)
+    assert np.array_equal(scores, oracle.indexer(b["q_idx"], b["k_idx"], b["w"]))
+    assert np.array_equal(idx, oracle.topk(scores, s.k))
+    assert np.array_equal(out, oracle.attend(b["q"], b["kv_cmp"], idx, b["kv_win"], s.scale))
+
+
+def test_oracle_threads_do_not_change_results():
+    g = torch.Generator().manual_seed(31)
+    x = torch.randn(16, 3000, generator=g)
+    oracle.set_threads(1)
+    a = oracle.topk(x.numpy(), 50)
+    oracle.set_threads(4)
+    b = oracle.topk(x.numpy(), 50)
+    assert np.array_equal(a, b)

@@ -1,0 +1,146 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) sparse-attention decode-step library.
+ *
+ * One decode step of DeepSeek-style sparse attention runs in three stages:
+ *   1. lightning-indexer scoring of every compressed position,
+ *   2. top-k selection of the best-scoring positions,
+ *   3. multi-query attention over the selected compressed rows plus a window
+ *      of recent raw rows.
+ * The stages are described in "feat: Add DeepSeek-V4 CSA attention kernels"
+ * (aws-neuron nki-library pull request 13), section "How the algorithm
+ * works", steps 2-4; the top-k options follow the "DeepSelect" project page
+ * (sorted_index and return_value), and the attention scale follows the
+ * norm_factor of "Implementation: Deepspeedai DeepSpeed Inference PT
+ * Binding" (Usage Examples).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a HIP device pointer on the current device.
+ *    Tensors are dense, row-major, and 16-byte aligned.
+ *  - bf16 tensors hold IEEE bfloat16 bit patterns (2 bytes per element).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). All
+ *    work is enqueued on it and the call returns without waiting for the
+ *    device; outputs are ready once the stream reaches that point.
+ *  - Ownership: the caller owns every buffer, including the workspace `ws`
+ *    (size from the matching *_workspace_bytes call). The library allocates
+ *    and frees no device memory and keeps no state between calls. Buffers
+ *    must stay alive until the enqueued work completes. Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - Errors: every argument is checked on the host before anything is
+ *    enqueued. On a non-zero status nothing was launched. The device must be
+ *    gfx950, else DSA_ERROR_NOT_SUPPORTED. A failed kernel launch returns
+ *    DSA_ERROR_LAUNCH. No C++ exception crosses this interface.
+ *  - Results are deterministic: the same inputs give the same bits.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DSA_EXPORT __attribute__((visibility("default")))
+#else
+#define DSA_EXPORT
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DSA_BF16 = 0, DSA_F32 = 1 } dsa_dtype_t;
+
+typedef enum {
+  DSA_SUCCESS = 0,
+  DSA_ERROR_INVALID_VALUE = 1,       /* null pointer, bad size, misalignment */
+  DSA_ERROR_NOT_SUPPORTED = 2,       /* shape outside the compiled range, not gfx950 */
+  DSA_ERROR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_bytes value */
+  DSA_ERROR_LAUNCH = 4,              /* a kernel launch failed */
+  DSA_ERROR_DEVICE = 5               /* no usable HIP device */
+} dsa_status_t;
+
+/* Problem sizes of one decode step (the block shapes of "Launching a full
+ * block" in the CSA pull request). */
+typedef struct {
+  int32_t batch;     /* B: independent decode tokens (>= 1) */
+  int32_t n;         /* N: compressed positions per token (>= 1) */
+  int32_t idx_heads; /* H_I: indexer heads, 1..64 */
+  int32_t idx_dim;   /* D_I: indexer channels; must be 128 */
+  int32_t topk;      /* k: selected positions, 1 <= k <= min(N, 4096) */
+  int32_t window;    /* W: raw window rows, >= 0 */
+  int32_t q_heads;   /* H_q: query heads, a multiple of 16, 16..128 */
+  int32_t head_dim;  /* D: KV dim (K = V), 128 or 512 */
+  float scale;       /* softmax scale applied to q.k, e.g. 1/sqrt(D) */
+} dsa_dims_t;
+
+/*
+ * Lightning-indexer scores (CSA pull request, "How the algorithm works",
+ * step 2: a multi-query product, a ReLU and a per-head weight):
+ *   scores[b,j] = sum_{h<H_I} w[b,h] * max(0, sum_{d<D_I} q_idx[b,h,d] * k_idx[b,j,d])
+ * q_idx  bf16 [B, H_I, D_I]; k_idx bf16 [B, N, D_I]; w float [B, H_I];
+ * scores float [B, N] (output). Products are exact, sums run in float32
+ * with a fixed order. Requires D_I == 128 and 1 <= H_I <= 64.
+ */
+DSA_EXPORT dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, const float* w,
+                               float* scores, int B, int N, int H_I, int D_I,
+                               void* stream);
+
+/*
+ * Top-k selection (CSA pull request, step 3; "DeepSelect" project page):
+ * for each of the B rows of `scores` (dtype bf16 or float32, [B, N]) the k
+ * positions with the largest value, ties broken by the lower index. -0.0 and
+ * +0.0 compare equal; NaN inputs are not allowed (result unspecified).
+ *   out_idx  int32 [B, k]: the selected positions. Their order is
+ *            unspecified (but deterministic) when sorted_index == 0, and
+ *            ascending when sorted_index == 1.
+ *   out_val  [B, k] of the input dtype, or NULL: the scores at out_idx,
+ *            bit-identical copies of the input.
+ * Requires 1 <= k <= N and k <= 4096. ws/ws_bytes: workspace of at least
+ * dsa_topk_workspace_bytes(B, N, k, dtype) bytes; its contents on entry do
+ * not matter.
+ */
+DSA_EXPORT size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype);
+DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k,
+                      int32_t* out_idx, void* out_val, int sorted_index, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * Sparse multi-query attention (CSA pull request, step 4: gather the selected
+ * KV rows, add the sliding window, run multi-query attention; K and V are the
+ * same embedding, per "The top-k on the GPSIMD engine"):
+ *   R_b      = [kv_cmp[b, idx[b,i]] for i < k] followed by [kv_win[b,t] for t < W]
+ *   out[b,h] = softmax_r(scale * q[b,h] . R_b[r]) @ R_b
+ * q bf16 [B, H_q, D]; kv_cmp bf16 [B, N, D]; idx int32 [B, k] with values in
+ * [0, N) (out-of-range values are clamped, the result is then unspecified);
+ * kv_win bf16 [B, W, D] (may be NULL iff W == 0); out bf16 [B, H_q, D].
+ * Softmax statistics and accumulation run in float32; out is rounded to
+ * nearest even. Only dims->batch, n, topk, window, q_heads, head_dim, scale
+ * are read. Workspace: dsa_sparse_attend_workspace_bytes(dims) bytes.
+ */
+DSA_EXPORT size_t dsa_sparse_attend_workspace_bytes(const dsa_dims_t* dims);
+DSA_EXPORT dsa_status_t dsa_sparse_attend(const void* q, const void* kv_cmp, const int32_t* idx,
+                               const void* kv_win, void* out, const dsa_dims_t* dims,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole decode step: indexer scores -> top-k -> sparse attention, all on
+ * `stream` with no host synchronisation; the score rows and the selected
+ * indices stay in the workspace (as in the CSA pull request's Summary, where
+ * neither returns to the host). Arguments as in the three calls above.
+ * out_idx int32 [B, k] or NULL: when given, receives the selected positions
+ * in the order dsa_topk gives with sorted_index == 0. Workspace:
+ * dsa_decode_step_workspace_bytes(dims).
+ */
+DSA_EXPORT size_t dsa_decode_step_workspace_bytes(const dsa_dims_t* dims);
+DSA_EXPORT dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* w,
+                             const void* q, const void* kv_cmp, const void* kv_win,
+                             void* out, int32_t* out_idx, const dsa_dims_t* dims,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+DSA_EXPORT const char* dsa_status_string(dsa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,19 @@
+"""MI355X (gfx950) sparse-attention decode step: lightning-indexer scoring,
+exact top-k selection and sparse multi-query attention as hand-written HIP
+kernels behind the C ABI in include/dsa.h.
+
+Importing the package loads libdsa.so and raises if it has not been built.
+"""
+from .binding import (  # noqa: F401
+    DsaDims,
+    DsaError,
+    dsa_decode_step,
+    dsa_decode_step_workspace_bytes,
+    dsa_indexer_score,
+    dsa_sparse_attend,
+    dsa_sparse_attend_workspace_bytes,
+    dsa_topk,
+    dsa_topk_workspace_bytes,
+    make_dims,
+    status_string,
+)

@@ -1,0 +1,240 @@
+"""ctypes binding of libdsa (include/dsa.h), with the same entry-point names.
+
+This layer only marshals arguments: it checks tensor dtypes, shapes and
+devices, allocates outputs and workspaces through torch, passes raw device
+pointers and the current HIP stream, and turns a non-zero status into an
+exception. Every step of the computation runs in the HIP kernels of
+libdsa.so; if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_BF16 = 0
+DSA_F32 = 1
+
+EXPORTED = (
+    "dsa_indexer_score",
+    "dsa_topk_workspace_bytes",
+    "dsa_topk",
+    "dsa_sparse_attend_workspace_bytes",
+    "dsa_sparse_attend",
+    "dsa_decode_step_workspace_bytes",
+    "dsa_decode_step",
+    "dsa_status_string",
+)
+
+
+class DsaDims(ctypes.Structure):
+    """Mirror of dsa_dims_t."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("idx_heads", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("q_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class DsaError(RuntimeError):
+    """A non-zero dsa_status_t."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with indexer_top_gathered_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    D = ctypes.POINTER(DsaDims)
+    lib.dsa_indexer_score.argtypes = [P, P, P, P, I, I, I, I, P]
+    lib.dsa_indexer_score.restype = I
+    lib.dsa_topk_workspace_bytes.argtypes = [I, I, I, I]
+    lib.dsa_topk_workspace_bytes.restype = S
+    lib.dsa_topk.argtypes = [P, I, I, I, I, P, P, I, P, S, P]
+    lib.dsa_topk.restype = I
+    lib.dsa_sparse_attend_workspace_bytes.argtypes = [D]
+    lib.dsa_sparse_attend_workspace_bytes.restype = S
+    lib.dsa_sparse_attend.argtypes = [P, P, P, P, P, D, P, S, P]
+    lib.dsa_sparse_attend.restype = I
+    lib.dsa_decode_step_workspace_bytes.argtypes = [D]
+    lib.dsa_decode_step_workspace_bytes.restype = S
+    lib.dsa_decode_step.argtypes = [P, P, P, P, P, P, P, P, D, P, S, P]
+    lib.dsa_decode_step.restype = I
+    lib.dsa_status_string.argtypes = [I]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.dsa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DsaError(status, where)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if ws.dtype != torch.uint8 or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous uint8 device tensor")
+    return ws
+
+
+def make_dims(B, N, H_I, D_I, k, W, H_q, D, scale) -> DsaDims:
+    return DsaDims(int(B), int(N), int(H_I), int(D_I), int(k), int(W), int(H_q), int(D),
+                   float(scale))
+
+
+# ------------------------------------------------------------------ indexer
+
+def dsa_indexer_score(q_idx, k_idx, w, scores=None, stream=None):
+    """scores[b,j] = sum_h w[b,h] * relu(q_idx[b,h,:] . k_idx[b,j,:]) (float32 [B,N])."""
+    B, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, DI))
+    _need(w, "w", torch.float32, (B, H))
+    if scores is None:
+        scores = torch.empty((B, N), dtype=torch.float32, device=q_idx.device)
+    _need(scores, "scores", torch.float32, (B, N))
+    _check(LIB.dsa_indexer_score(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, N, H, DI,
+                                 _stream(stream)), "dsa_indexer_score")
+    return scores
+
+
+# ------------------------------------------------------------------ top-k
+
+def dsa_topk_workspace_bytes(B: int, N: int, k: int, dtype=torch.float32) -> int:
+    dt = DSA_BF16 if dtype == torch.bfloat16 else DSA_F32
+    return int(LIB.dsa_topk_workspace_bytes(int(B), int(N), int(k), dt))
+
+
+def dsa_topk(scores, k: int, return_values: bool = False, sorted_index: bool = False,
+             out_idx=None, out_val=None, ws=None, stream=None):
+    """Indices (int32 [B,k]) of the k largest scores per row, lower index
+    first among ties; values are bit copies when return_values."""
+    if scores.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("scores must be bfloat16 or float32")
+    _need(scores, "scores", scores.dtype)
+    B, N = scores.shape
+    dt = DSA_BF16 if scores.dtype == torch.bfloat16 else DSA_F32
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    _need(out_idx, "out_idx", torch.int32, (B, k))
+    if return_values and out_val is None:
+        out_val = torch.empty((B, k), dtype=scores.dtype, device=scores.device)
+    if out_val is not None:
+        _need(out_val, "out_val", scores.dtype, (B, k))
+    nbytes = LIB.dsa_topk_workspace_bytes(B, N, int(k), dt)
+    ws = _workspace(nbytes, scores.device, ws)
+    _check(LIB.dsa_topk(_ptr(scores), dt, B, N, int(k), _ptr(out_idx), _ptr(out_val),
+                        int(bool(sorted_index)), _ptr(ws), ws.numel(), _stream(stream)),
+           "dsa_topk")
+    return (out_idx, out_val) if out_val is not None else out_idx
+
+
+# ------------------------------------------------------------------ attention
+
+def dsa_sparse_attend_workspace_bytes(dims: DsaDims) -> int:
+    return int(LIB.dsa_sparse_attend_workspace_bytes(ctypes.byref(dims)))
+
+
+def dsa_sparse_attend(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, stream=None):
+    """bf16 [B,H_q,D] = softmax(scale * q R^T) R over R = kv_cmp[idx] ++ kv_win."""
+    B, Hq, D = q.shape
+    N = kv_cmp.shape[1]
+    k = idx.shape[1]
+    W = 0 if kv_win is None else kv_win.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(kv_cmp, "kv_cmp", torch.bfloat16, (B, N, D))
+    _need(idx, "idx", torch.int32, (B, k))
+    if kv_win is not None:
+        _need(kv_win, "kv_win", torch.bfloat16, (B, W, D))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, Hq, D))
+    dims = make_dims(B, N, 1, 128, k, W, Hq, D, scale)
+    ws = _workspace(LIB.dsa_sparse_attend_workspace_bytes(ctypes.byref(dims)), q.device, ws)
+    _check(LIB.dsa_sparse_attend(_ptr(q), _ptr(kv_cmp), _ptr(idx), _ptr(kv_win if W else None),
+                                 _ptr(out), ctypes.byref(dims), _ptr(ws), ws.numel(),
+                                 _stream(stream)), "dsa_sparse_attend")
+    return out
+
+
+# ------------------------------------------------------------------ fused step
+
+def dsa_decode_step_workspace_bytes(dims: DsaDims) -> int:
+    return int(LIB.dsa_decode_step_workspace_bytes(ctypes.byref(dims)))
+
+
+def dsa_decode_step(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, out=None,
+                    out_idx=None, ws=None, stream=None, return_idx: bool = False):
+    """Indexer scores -> top-k -> sparse attention in one enqueue sequence."""
+    B, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq, D = q.shape[1], q.shape[2]
+    W = 0 if kv_win is None else kv_win.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, DI))
+    _need(w, "w", torch.float32, (B, H))
+    _need(q, "q", torch.bfloat16, (B, Hq, D))
+    _need(kv_cmp, "kv_cmp", torch.bfloat16, (B, N, D))
+    if kv_win is not None:
+        _need(kv_win, "kv_win", torch.bfloat16, (B, W, D))
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, Hq, D))
+    if return_idx and out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if out_idx is not None:
+        _need(out_idx, "out_idx", torch.int32, (B, k))
+    dims = make_dims(B, N, H, DI, k, W, Hq, D, scale)
+    ws = _workspace(LIB.dsa_decode_step_workspace_bytes(ctypes.byref(dims)), q.device, ws)
+    _check(LIB.dsa_decode_step(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
+                               _ptr(kv_win if W else None), _ptr(out), _ptr(out_idx),
+                               ctypes.byref(dims), _ptr(ws), ws.numel(), _stream(stream)),
+           "dsa_decode_step")
+    return (out, out_idx) if out_idx is not None else out

@@ -1,0 +1,220 @@
+// C ABI of libdsa (declared in include/dsa.h): argument checks, the gfx950
+// check, workspace layout and kernel launches. Every check runs on the host
+// before anything is enqueued; no entry point waits for the device.
+#include <atomic>
+#include <cstring>
+
+#include "dsa_internal.h"
+
+namespace {
+
+using namespace dsa;
+
+constexpr int kMaxTopk = 4096;
+constexpr int kMaxDevices = 64;
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch[kMaxDevices];
+
+dsa_status_t check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return DSA_ERROR_DEVICE;
+  }
+  if (dev >= kMaxDevices) return DSA_ERROR_NOT_SUPPORTED;
+  int state = g_arch[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return DSA_ERROR_DEVICE;
+    }
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? DSA_SUCCESS : DSA_ERROR_NOT_SUPPORTED;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+dsa_status_t to_status(hipError_t e) { return e == hipSuccess ? DSA_SUCCESS : DSA_ERROR_LAUNCH; }
+
+// Shape checks of the indexer stage.
+dsa_status_t check_indexer_shape(int B, int N, int H, int DI) {
+  if (B < 1 || N < 1 || H < 1 || DI < 1) return DSA_ERROR_INVALID_VALUE;
+  if (DI != 128 || H > 64) return DSA_ERROR_NOT_SUPPORTED;
+  if ((long long)B * N > 0x7FFFFFFFLL) return DSA_ERROR_NOT_SUPPORTED;
+  return DSA_SUCCESS;
+}
+
+dsa_status_t check_topk_shape(int B, int N, int k, dsa_dtype_t dt) {
+  if (B < 1 || N < 1 || k < 1 || k > N) return DSA_ERROR_INVALID_VALUE;
+  if (dt != DSA_BF16 && dt != DSA_F32) return DSA_ERROR_INVALID_VALUE;
+  if (k > kMaxTopk) return DSA_ERROR_NOT_SUPPORTED;
+  if (B > 65535) return DSA_ERROR_NOT_SUPPORTED;
+  return DSA_SUCCESS;
+}
+
+// Attention shape checks (reads batch, n, topk, window, q_heads, head_dim, scale).
+dsa_status_t check_attend_dims(const dsa_dims_t* d) {
+  if (!d) return DSA_ERROR_INVALID_VALUE;
+  if (d->batch < 1 || d->n < 1 || d->topk < 1 || d->topk > d->n || d->window < 0 ||
+      d->q_heads < 1 || d->head_dim < 1)
+    return DSA_ERROR_INVALID_VALUE;
+  if (!(d->scale == d->scale) || d->scale == __builtin_inff() || d->scale == -__builtin_inff())
+    return DSA_ERROR_INVALID_VALUE;
+  if (d->head_dim != 128 && d->head_dim != 512) return DSA_ERROR_NOT_SUPPORTED;
+  if (d->q_heads % 16 != 0 || d->q_heads > 128) return DSA_ERROR_NOT_SUPPORTED;
+  if (d->topk > kMaxTopk || d->batch > 65535) return DSA_ERROR_NOT_SUPPORTED;
+  return DSA_SUCCESS;
+}
+
+// Workspace layout of the fused step.
+struct StepLayout {
+  size_t scores_off, idx_off, topk_off, attend_off, bytes;
+  TopkPlan tk;
+  AttendPlan at;
+};
+
+StepLayout step_layout(const dsa_dims_t& d) {
+  StepLayout L{};
+  L.tk = plan_topk(d.batch, d.n, d.topk, DSA_F32);
+  L.at = plan_attend(d);
+  size_t off = 0;
+  L.scores_off = off;
+  off = align_up(off + (size_t)d.batch * d.n * sizeof(float), 256);
+  L.idx_off = off;
+  off = align_up(off + (size_t)d.batch * d.topk * sizeof(int32_t), 256);
+  L.topk_off = off;
+  off = align_up(off + L.tk.bytes, 256);
+  L.attend_off = off;
+  off = align_up(off + L.at.bytes, 256);
+  L.bytes = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status_t s) {
+  switch (s) {
+    case DSA_SUCCESS: return "DSA_SUCCESS";
+    case DSA_ERROR_INVALID_VALUE: return "DSA_ERROR_INVALID_VALUE: invalid argument";
+    case DSA_ERROR_NOT_SUPPORTED: return "DSA_ERROR_NOT_SUPPORTED: shape or device not supported";
+    case DSA_ERROR_WORKSPACE_TOO_SMALL: return "DSA_ERROR_WORKSPACE_TOO_SMALL: workspace too small";
+    case DSA_ERROR_LAUNCH: return "DSA_ERROR_LAUNCH: kernel launch failed";
+    case DSA_ERROR_DEVICE: return "DSA_ERROR_DEVICE: no usable HIP device";
+  }
+  return "DSA_ERROR_UNKNOWN";
+}
+
+dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, const float* w,
+                               float* scores, int B, int N, int H_I, int D_I, void* stream) {
+  if (!q_idx || !k_idx || !w || !scores) return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(scores) ||
+      (reinterpret_cast<uintptr_t>(w) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
+  dsa_status_t s = check_indexer_shape(B, N, H_I, D_I);
+  if (s != DSA_SUCCESS) return s;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  return to_status(launch_indexer_score(static_cast<const uint16_t*>(q_idx),
+                                        static_cast<const uint16_t*>(k_idx), w, scores, B, N,
+                                        H_I, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
+  if (check_topk_shape(B, N, k, dtype) != DSA_SUCCESS) return 0;
+  return plan_topk(B, N, k, dtype).bytes;
+}
+
+dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k,
+                      int32_t* out_idx, void* out_val, int sorted_index, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (!scores || !out_idx || !ws) return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(scores) || !aligned16(ws) || (reinterpret_cast<uintptr_t>(out_idx) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
+  if (out_val && (reinterpret_cast<uintptr_t>(out_val) & (dtype == DSA_BF16 ? 1u : 3u)))
+    return DSA_ERROR_INVALID_VALUE;
+  if (sorted_index != 0 && sorted_index != 1) return DSA_ERROR_INVALID_VALUE;
+  dsa_status_t s = check_topk_shape(B, N, k, dtype);
+  if (s != DSA_SUCCESS) return s;
+  const TopkPlan plan = plan_topk(B, N, k, dtype);
+  if (ws_bytes < plan.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  return to_status(launch_topk(scores, dtype, B, N, k, out_idx, out_val, sorted_index, plan, ws,
+                               static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_sparse_attend_workspace_bytes(const dsa_dims_t* dims) {
+  if (check_attend_dims(dims) != DSA_SUCCESS) return 0;
+  // Never report 0 for a valid shape, so a zero result always means "invalid".
+  const size_t b = plan_attend(*dims).bytes;
+  return b ? b : 256;
+}
+
+dsa_status_t dsa_sparse_attend(const void* q, const void* kv_cmp, const int32_t* idx,
+                               const void* kv_win, void* out, const dsa_dims_t* dims, void* ws,
+                               size_t ws_bytes, void* stream) {
+  dsa_status_t s = check_attend_dims(dims);
+  if (s != DSA_SUCCESS) return s;
+  if (!q || !kv_cmp || !idx || !out || !ws || (dims->window > 0 && !kv_win))
+    return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(kv_cmp) || !aligned16(out) || !aligned16(ws) ||
+      (kv_win && !aligned16(kv_win)) || (reinterpret_cast<uintptr_t>(idx) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
+  const AttendPlan plan = plan_attend(*dims);
+  if (ws_bytes < (plan.bytes ? plan.bytes : 256)) return DSA_ERROR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  return to_status(launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp),
+                                 idx, static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out),
+                                 *dims, plan, ws, static_cast<hipStream_t>(stream)));
+}
+
+size_t dsa_decode_step_workspace_bytes(const dsa_dims_t* dims) {
+  if (check_attend_dims(dims) != DSA_SUCCESS) return 0;
+  if (check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim) != DSA_SUCCESS) return 0;
+  return step_layout(*dims).bytes;
+}
+
+dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* w, const void* q,
+                             const void* kv_cmp, const void* kv_win, void* out, int32_t* out_idx,
+                             const dsa_dims_t* dims, void* ws, size_t ws_bytes, void* stream) {
+  dsa_status_t s = check_attend_dims(dims);
+  if (s != DSA_SUCCESS) return s;
+  s = check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim);
+  if (s != DSA_SUCCESS) return s;
+  if (!q_idx || !k_idx || !w || !q || !kv_cmp || !out || !ws || (dims->window > 0 && !kv_win))
+    return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(kv_cmp) ||
+      !aligned16(out) || !aligned16(ws) || (kv_win && !aligned16(kv_win)) ||
+      (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(out_idx) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
+  const StepLayout L = step_layout(*dims);
+  if (ws_bytes < L.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + L.scores_off);
+  int32_t* sel = out_idx ? out_idx : reinterpret_cast<int32_t*>(base + L.idx_off);
+  const dsa_dims_t& d = *dims;
+  hipError_t e = launch_indexer_score(static_cast<const uint16_t*>(q_idx),
+                                      static_cast<const uint16_t*>(k_idx), w, scores, d.batch, d.n,
+                                      d.idx_heads, st);
+  if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+  e = launch_topk(scores, DSA_F32, d.batch, d.n, d.topk, sel, nullptr, 0, L.tk, base + L.topk_off, st);
+  if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+  e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp), sel,
+                    static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), d, L.at,
+                    base + L.attend_off, st);
+  return to_status(e);
+}
+
+}  // extern "C"

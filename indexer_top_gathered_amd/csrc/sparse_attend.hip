@@ -1,0 +1,283 @@
+// Sparse multi-query decode attention on gfx950 ("feat: Add DeepSeek-V4 CSA
+// attention kernels", "How the algorithm works", step 4: gather the
+// selected KV rows, add the sliding window, run multi-query attention; "The
+// top-k on the GPSIMD engine": K and V are one embedding, read once and
+// transposed on chip).
+//
+//   R_b = kv_cmp[b, idx[b, :]] ++ kv_win[b, :]          (k + W rows of D)
+//   out[b,h,:] = softmax_r(scale * q[b,h,:] . R_b[r,:]) @ R_b
+//
+// Each workgroup takes one batch row, a group of 16*WAVES query heads (16
+// per wave) and a contiguous split of the rows. Rows are staged 32 at a time
+// into LDS (row-major, padded), and each staged row is used twice:
+//   S^T = R Q^T  : MFMA A operand = 16 rows x 32 dims read straight from
+//                  LDS (ds_read_b128), B operand = the wave's query
+//                  fragments, kept in registers;
+//   O^T = R^T P^T: A operand = 16 dims x 32 rows from the same LDS tile via
+//                  ds_read_b64_tr_b16 (a 4x4 transposing read), B operand =
+//                  the probabilities, which the S^T result already holds in
+//                  the right lanes (lane 16g+m: rows 4g..4g+3 of head m).
+// A lane therefore owns one head throughout, so the running max, the
+// rescale factor and the running sum need no cross-lane traffic except two
+// reductions per tile. The online softmax runs in float32. A single split
+// writes bf16 output directly; several splits write (max, sum, unnormalised
+// O) partials that a combine kernel merges with the log-sum-exp rule.
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kTile = 32;  // rows per LDS tile
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
+    uint16_t* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
+    int N, int k, int W, int Hq, float scale, int rows_per_split, int splits) {
+  constexpr int THREADS = WAVES * kWave;
+  constexpr int HW = WAVES * 16;
+  constexpr int KSTEPS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int ROW_WORDS = D / 2 + 4;  // 16 bytes of padding per row
+  constexpr int CHUNKS = D / 8;         // 16-byte chunks per row
+  __shared__ uint32_t R[kTile * ROW_WORDS];
+
+  const int split = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+  const int h = hg * HW + wave * 16 + m;  // the head this lane owns
+  const int rows = k + W;
+  const int r0 = split * rows_per_split;
+  const int r1 = min(rows, r0 + rows_per_split);
+
+  // Query fragments (B operand of S^T): head h, dims 32*kk + 8g .. +8.
+  bf16x8 qf[KSTEPS];
+  const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g * 8);
+
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY;  // running max of the scaled logits of head h
+  float lrun = 0.0f;       // this lane's share of the running sum
+
+  const int32_t* irow = idx + (size_t)b * k;
+  const uint16_t* kvb = kv + (size_t)b * N * D;
+  const uint16_t* winb = win ? win + (size_t)b * W * D : nullptr;
+
+  for (int t0 = r0; t0 < r1; t0 += kTile) {
+    lds_barrier();  // the previous tile's reads are done
+    for (int c = tid; c < kTile * CHUNKS; c += THREADS) {
+      const int rr = c / CHUNKS;
+      const int ch = c % CHUNKS;
+      const int r = t0 + rr;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (r < r1) {
+        const uint16_t* src;
+        if (r < k) {
+          int j = irow[r];
+          j = j < 0 ? 0 : (j >= N ? N - 1 : j);
+          src = kvb + (size_t)j * D;
+        } else {
+          src = winb + (size_t)(r - k) * D;
+        }
+        v = *reinterpret_cast<const u32x4*>(src + ch * 8);
+      }
+      *reinterpret_cast<u32x4*>(&R[rr * ROW_WORDS + ch * 4]) = v;
+    }
+    lds_barrier();
+
+    // S^T for rows 0..15 and 16..31 of the tile.
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&R[m * ROW_WORDS + kk * 16 + g * 4]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&R[(16 + m) * ROW_WORDS + kk * 16 + g * 4]);
+      s0 = mfma16x16x32(a0, qf[kk], s0);
+      s1 = mfma16x16x32(a1, qf[kk], s1);
+    }
+    // Lane (m, g): s0[i] is row 4g+i, s1[i] is row 16+4g+i, head m.
+    float z[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = (t0 + 4 * g + i < r1) ? s0[i] * scale : -INFINITY;
+      z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? s1[i] * scale : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
+    const float alpha = __expf(mrun - mnew);
+    mrun = mnew;
+    u32x4 pw;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t b0 = f32_to_bf16_bits(__expf(z[2 * i] - mnew));
+      const uint32_t b1 = f32_to_bf16_bits(__expf(z[2 * i + 1] - mnew));
+      // the sum uses the rounded weights the MFMA sees
+      psum += bf16_bits_to_f32((uint16_t)b0) + bf16_bits_to_f32((uint16_t)b1);
+      pw[i] = b0 | (b1 << 16);
+    }
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    lrun = lrun * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt][0] *= alpha;
+      o[dt][1] *= alpha;
+      o[dt][2] *= alpha;
+      o[dt][3] *= alpha;
+    }
+
+    // O^T += R^T P^T. Within each 16-lane group, lane j points at row
+    // (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4) .. +4; the
+    // transposing read hands lane j the 4 rows at dim 16*dt + j.
+    const int ra = 4 * g + (m >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const int col = dt * 8 + 2 * (m & 3);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(&R[ra * ROW_WORDS + col]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(&R[(16 + ra) * ROW_WORDS + col]));
+      // Concatenate as whole vectors (element-wise inserts of bit-cast
+      // halves were folded into copies of element 0 by the compiler).
+      const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, cat), pb, o[dt]);
+    }
+  }
+
+  // Full sum over the four lane groups that share head m.
+  float l = lrun + __shfl_xor(lrun, 16);
+  l += __shfl_xor(l, 32);
+  // Lane (m, g) holds O[h][16*dt + 4g + i].
+  if (splits == 1) {
+    const float inv = 1.0f / l;
+    uint16_t* orow = out + ((size_t)b * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_bits(o[dt][0] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(o[dt][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(o[dt][2] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(o[dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + dt * 16 + g * 4) = make_uint2(lo, hi);
+    }
+  } else {
+    const size_t slot = ((size_t)b * splits + split) * Hq + h;
+    float* po = part_o + slot * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + dt * 16 + g * 4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (g == 0) part_ml[slot] = make_float2(mrun, l);
+  }
+}
+
+// Log-sum-exp merge of the split partials: one workgroup per (batch, head),
+// each thread owns 4 dims.
+template <int D>
+__global__ __launch_bounds__(D / 4) void attend_combine_kernel(
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+    uint16_t* __restrict__ out, int Hq, int splits) {
+  const int bh = blockIdx.x;
+  const int b = bh / Hq;
+  const int h = bh % Hq;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((size_t)b * splits + s) * Hq + h].x);
+  float L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int d = threadIdx.x * 4;
+  for (int s = 0; s < splits; ++s) {
+    const size_t slot = ((size_t)b * splits + s) * Hq + h;
+    const float2 ml = part_ml[slot];
+    const float f = __expf(ml.x - M);
+    L += ml.y * f;
+    const float4 v = *reinterpret_cast<const float4*>(part_o + slot * D + d);
+    acc.x += v.x * f;
+    acc.y += v.y * f;
+    acc.z += v.z * f;
+    acc.w += v.w * f;
+  }
+  const float inv = 1.0f / L;
+  const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc.x * inv) | ((uint32_t)f32_to_bf16_bits(acc.y * inv) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc.z * inv) | ((uint32_t)f32_to_bf16_bits(acc.w * inv) << 16);
+  *reinterpret_cast<uint2*>(out + ((size_t)b * Hq + h) * D + d) = make_uint2(lo, hi);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+template <int D, int WAVES>
+void launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                     const uint16_t* win, uint16_t* out, float* po, float2* pml,
+                     const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
+  dim3 grid(p.splits, d.q_heads / (16 * WAVES), d.batch);
+  hipLaunchKernelGGL((sparse_attend_kernel<D, WAVES>), grid, dim3(WAVES * kWave), 0, st, q, kv,
+                     idx, win, out, po, pml, d.n, d.topk, d.window, d.q_heads, d.scale,
+                     p.rows_per_split, p.splits);
+}
+
+}  // namespace
+
+AttendPlan plan_attend(const dsa_dims_t& d) {
+  AttendPlan p{};
+  const int rows = d.topk + d.window;
+  p.heads_per_wg = (d.q_heads % 64 == 0) ? 64 : (d.q_heads % 32 == 0 ? 32 : 16);
+  const int hgroups = d.q_heads / p.heads_per_wg;
+  const int tiles = (rows + kTile - 1) / kTile;
+  // About 256 workgroups in total, at least one tile per split.
+  long long want = (256 + (long long)d.batch * hgroups - 1) / ((long long)d.batch * hgroups);
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  const int tiles_per_split = (tiles + (int)want - 1) / (int)want;
+  p.rows_per_split = tiles_per_split * kTile;
+  p.splits = (rows + p.rows_per_split - 1) / p.rows_per_split;
+  if (p.splits > 1) {
+    p.part_o_off = 0;
+    p.part_ml_off = align_up((size_t)d.batch * p.splits * d.q_heads * d.head_dim * sizeof(float), 256);
+    p.bytes = align_up(p.part_ml_off + (size_t)d.batch * p.splits * d.q_heads * sizeof(float2), 256);
+  } else {
+    p.part_o_off = p.part_ml_off = 0;
+    p.bytes = 0;
+  }
+  return p;
+}
+
+hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                         const uint16_t* win, uint16_t* out, const dsa_dims_t& d,
+                         const AttendPlan& p, void* ws, hipStream_t st) {
+  float* po = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
+  float2* pml = p.splits > 1 ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
+  const int waves = p.heads_per_wg / 16;
+  if (d.head_dim == 512) {
+    if (waves == 4) launch_attend_t<512, 4>(q, kv, idx, win, out, po, pml, d, p, st);
+    else if (waves == 2) launch_attend_t<512, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    else launch_attend_t<512, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+  } else {
+    if (waves == 4) launch_attend_t<128, 4>(q, kv, idx, win, out, po, pml, d, p, st);
+    else if (waves == 2) launch_attend_t<128, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    else launch_attend_t<128, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int Hq = d.q_heads;
+  if (d.head_dim == 512)
+    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(d.batch * Hq), dim3(128), 0, st, po, pml, out, Hq, p.splits);
+  else
+    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(d.batch * Hq), dim3(32), 0, st, po, pml, out, Hq, p.splits);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/dsa.h declares, and rejects bad arguments on the host before
+touching a device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+LIB_PATH = os.path.join(ROOT, "indexer_top_gathered_amd", "libdsa.so")
+
+SUCCESS, INVALID, NOT_SUPPORTED, WS_SMALL, LAUNCH, DEVICE = range(6)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DSA_EXPORT[^;(]*?\b(dsa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB_PATH):
+        from indexer_top_gathered_amd import build
+        build.build()
+    from indexer_top_gathered_amd import binding
+    return binding
+
+
+def test_header_declares_the_four_calls():
+    syms = declared_symbols()
+    for name in ("dsa_indexer_score", "dsa_topk", "dsa_sparse_attend", "dsa_decode_step"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(raw, name), name
+    assert set(declared_symbols()) == set(lib.EXPORTED)
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.status_string(s).startswith("DSA_")
+    assert "UNKNOWN" in lib.status_string(99)
+
+
+P = 0x10000  # a fake, 16-byte aligned address: never dereferenced by these calls
+
+
+def _dims(lib, **kw):
+    base = dict(B=2, N=4096, H_I=8, D_I=128, k=256, W=64, H_q=16, D=128, scale=0.088)
+    base.update(kw)
+    return lib.make_dims(**base)
+
+
+def test_indexer_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    assert L.dsa_indexer_score(None, v(P), v(P), v(P), 1, 10, 8, 128, None) == INVALID
+    assert L.dsa_indexer_score(v(P), v(P), v(P), v(P + 8), 1, 10, 8, 128, None) == INVALID
+    assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 0, 10, 8, 128, None) == INVALID
+    assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 1, 10, 8, 64, None) == NOT_SUPPORTED
+    assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 1, 10, 65, 128, None) == NOT_SUPPORTED
+
+
+def test_topk_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    assert L.dsa_topk_workspace_bytes(4, 100, 101, 0) == 0
+    assert L.dsa_topk_workspace_bytes(4, 100, 0, 1) == 0
+    assert L.dsa_topk_workspace_bytes(4, 10000, 5000, 1) == 0  # k above 4096
+    need = L.dsa_topk_workspace_bytes(4, 100000, 512, 0)
+    assert need > 0
+    assert L.dsa_topk(v(P), 0, 4, 100, 101, v(P), None, 0, v(P), 1 << 20, None) == INVALID
+    assert L.dsa_topk(v(P), 2, 4, 100, 10, v(P), None, 0, v(P), 1 << 20, None) == INVALID
+    assert L.dsa_topk(None, 0, 4, 100, 10, v(P), None, 0, v(P), 1 << 20, None) == INVALID
+    assert L.dsa_topk(v(P + 2), 0, 4, 100, 10, v(P), None, 0, v(P), 1 << 20, None) == INVALID
+    assert L.dsa_topk(v(P), 0, 4, 100, 10, v(P), None, 2, v(P), 1 << 20, None) == INVALID
+    assert L.dsa_topk(v(P), 1, 4, 100, 10, v(P), v(P + 2), 0, v(P), 1 << 20, None) == INVALID
+    assert L.dsa_topk(v(P), 0, 4, 100000, 512, v(P), None, 0, v(P), need - 1, None) == WS_SMALL
+    assert L.dsa_topk(v(P), 0, 4, 10000, 5000, v(P), None, 0, v(P), 1 << 30, None) == NOT_SUPPORTED
+
+
+def test_attend_and_step_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    ok = _dims(lib)
+    assert lib.dsa_sparse_attend_workspace_bytes(ok) > 0
+    assert lib.dsa_decode_step_workspace_bytes(ok) > 0
+    for bad, code in [(dict(D=64), NOT_SUPPORTED), (dict(H_q=24), NOT_SUPPORTED),
+                      (dict(H_q=144), NOT_SUPPORTED), (dict(k=5000, N=6000), NOT_SUPPORTED),
+                      (dict(k=0), INVALID), (dict(k=5000), INVALID), (dict(W=-1), INVALID),
+                      (dict(scale=float("nan")), INVALID), (dict(B=0), INVALID)]:
+        d = _dims(lib, **bad)
+        assert lib.dsa_sparse_attend_workspace_bytes(d) == 0, bad
+        assert L.dsa_sparse_attend(v(P), v(P), v(P), v(P), v(P), ctypes.byref(d), v(P), 1 << 30,
+                                   None) == code, bad
+    d = _dims(lib, D_I=64)
+    assert lib.dsa_decode_step_workspace_bytes(d) == 0
+    assert L.dsa_decode_step(v(P), v(P), v(P), v(P), v(P), v(P), v(P), None, ctypes.byref(d),
+                             v(P), 1 << 30, None) == NOT_SUPPORTED
+    # window rows promised but no window tensor
+    assert L.dsa_sparse_attend(v(P), v(P), v(P), None, v(P), ctypes.byref(ok), v(P), 1 << 30,
+                               None) == INVALID
+    need = lib.dsa_decode_step_workspace_bytes(ok)
+    assert L.dsa_decode_step(v(P), v(P), v(P), v(P), v(P), v(P), v(P), None, ctypes.byref(ok),
+                             v(P), need - 1, None) == WS_SMALL
+    assert L.dsa_decode_step(v(P), v(P), v(P), v(P), v(P), v(P), v(P + 4), None,
+                             ctypes.byref(ok), v(P), need, None) == INVALID
+
+
+def test_valid_call_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is visible: this check is for hosts without one")
+    L = lib.LIB
+    v = ctypes.c_void_p
+    assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 1, 10, 8, 128, None) == DEVICE

@@ -1,0 +1,129 @@
+"""GPU parity of dsa_topk against the CPU oracle: given an identical score row
+the GPU index set, and the values when returned, must equal the oracle's
+exactly (order too when sorted_index is set)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_util import assert_topk_equal, assert_values_are_copies, host, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_case(scores: torch.Tensor, k: int, sorted_index=False, values=False, where=""):
+    say(f"[topk] {where} dtype={scores.dtype} shape={tuple(scores.shape)} k={k} "
+        f"sorted={sorted_index} values={values}")
+    import indexer_top_gathered_amd as dsa
+    res = dsa.dsa_topk(scores, k, return_values=values, sorted_index=sorted_index)
+    idx, val = (res if values else (res, None))
+    torch.cuda.synchronize()
+    ref = oracle.topk(host(scores), k, index_order=False)
+    assert_topk_equal(idx.cpu().numpy(), ref, sorted_index, where)
+    if values:
+        assert_values_are_copies(val, scores, idx, where)
+    return idx
+
+
+def _ties(B, N, levels, seed, dtype):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    x = torch.randint(0, levels, (B, N), generator=g, device=DEV).float() / 4 - levels / 8
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N,k", [(1, 1), (5, 5), (7, 3), (100, 1), (4096, 4096), (4097, 100),
+                                 (10001, 1000), (40000, 333), (131072, 512), (300000, 2048),
+                                 (50000, 4096)])
+def test_random_rows(dtype, N, k):
+    B = 3 if N < 200000 else 2
+    x = workloads.normal_rows(B, N, "bf16" if dtype == torch.bfloat16 else "f32", 1234 + N,
+                              device=DEV)
+    run_case(x, k, where=f"normal N={N}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("levels", [1, 2, 7, 256])
+def test_heavy_ties(dtype, levels):
+    x = _ties(4, 20011, levels, 77 + levels, dtype)
+    run_case(x, 1500, values=True, where=f"ties levels={levels}")
+    run_case(x, 1500, sorted_index=True, where=f"ties levels={levels} sorted")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("k", [1, 37, 2048])
+def test_special_rows(dtype, k):
+    N = 70000
+    ar = torch.arange(N, device=DEV, dtype=torch.float32)
+    rows = torch.stack([
+        torch.full((N,), 0.5, device=DEV),      # all equal
+        ar / 64,                                 # ascending (ties in bf16)
+        ar.flip(0) / 64,                         # descending
+        (ar % 1000) / 10,                        # saw-tooth
+    ]).to(dtype)
+    idx = run_case(rows, k, sorted_index=True, values=True, where="special rows").cpu().numpy()
+    assert idx[0].tolist() == list(range(k))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_signed_zero_infinity_and_subnormal(dtype):
+    N = 9000
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn((2, N), generator=g, device=DEV) * 1e-3
+    x[:, ::7] = 0.0
+    x[:, 3::7] = -0.0
+    x[0, 100] = float("inf")
+    x[0, 200] = float("-inf")
+    x[1, 5:50] = float("-inf")
+    x[1, 60:70] = float("inf")
+    x[1, 80] = 1e-40  # subnormal in float32 (flushed to a bf16 subnormal/zero after rounding)
+    x = x.to(dtype)
+    # about 3200 scores are positive, so k reaches into the zeros: -0.0 and
+    # +0.0 must tie and go by index
+    run_case(x, 4000, values=True, where="signed zeros")
+    run_case(x, 4000, sorted_index=True, values=True, where="signed zeros sorted")
+
+
+def test_negative_rows_and_wide_range():
+    g = torch.Generator(device=DEV).manual_seed(6)
+    x = -torch.rand((3, 65536), generator=g, device=DEV) * torch.logspace(-30, 30, 65536, device=DEV)
+    run_case(x, 777, values=True, where="negative wide range")
+
+
+def test_sampling_workload_full():
+    s = workloads.C3
+    x = workloads.sampling_rows(s.B, s.N, 3006, device=DEV)
+    run_case(x, s.k, values=True, where="sampling workload 128x129280 k=1024")
+
+
+def test_indexer_topk_workload_full():
+    s = workloads.C2
+    x = workloads.normal_rows(s.B, s.N, "bf16", 2006, device=DEV)
+    run_case(x, s.k, where="indexer-shaped workload 64x131072 bf16 k=512")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stress_levels_full(dtype):
+    s = workloads.C5_TOPK
+    x = workloads.stress_levels(s.B, s.N, 5008, device=DEV, dtype=dtype)
+    run_case(x, s.k, where=f"stress levels 64x262144 k=2048 {dtype}")
+    run_case(x, s.k, sorted_index=True, values=True, where=f"stress levels {dtype} sorted")
+
+
+def test_deterministic_and_workspace_contents_do_not_matter():
+    import indexer_top_gathered_amd as dsa
+    x = workloads.normal_rows(8, 100003, "f32", 99, device=DEV)
+    k = 1024
+    nb = dsa.dsa_topk_workspace_bytes(8, 100003, k, torch.float32)
+    ws1 = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    ws2 = torch.full((nb,), 0xFF, dtype=torch.uint8, device=DEV)
+    a, av = dsa.dsa_topk(x, k, return_values=True, ws=ws1)
+    b, bv = dsa.dsa_topk(x, k, return_values=True, ws=ws2)
+    c, cv = dsa.dsa_topk(x, k, return_values=True, ws=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(b, c)
+    assert torch.equal(av, bv)

@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse-attention decode step on one MI355X.
+
+A step is one pass of the whole hot path: indexer scoring, top-k, gather of
+the selected rows plus the window, and sparse multi-query attention, run by
+dsa_decode_step on the production decode shape (B=16, N=32768 compressed
+positions, 64 indexer heads of 128 channels, k=1024, a 128-row window, 128
+query heads, one K=V head of 512). Inputs are seeded synthetic tensors that
+are already resident in device memory; the timed loop rotates over enough
+input copies (> 1 GB) that each step reads its inputs from HBM rather than
+the 256 MB Infinity Cache.
+
+Printed: one JSON line. `value` is the step's effective bandwidth (its
+compulsory bytes - every input read once, the output written once - divided
+by the time per step), `us_per_step` the time per step, `roofline` the
+dominant kernel (indexer scoring) measured with HIP events on the stream it
+runs on, `topk` the top-k-only workload (bf16 64 x 131072, k=512), and
+`cpu_baseline` the CPU oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "top-k effective HBM GB/s; fused decode-step µs at B=16, N=32K, k=1024"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--copies", type=int, default=8, help="rotating input copies")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-topk", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also run one device copy of this many MiB (for counter calibration)")
+    return p.parse_args()
+
+
+def step_bytes(s) -> int:
+    """Compulsory bytes of one decode step: every input read once, the
+    output written once (intermediate scores and indices excluded)."""
+    b = s.B
+    return (b * s.H_I * s.D_I * 2 + b * s.N * s.D_I * 2 + b * s.H_I * 4      # indexer inputs
+            + b * s.H_q * s.D * 2                                            # q
+            + b * (s.k + s.W) * s.D * 2                                      # gathered rows + window
+            + b * s.H_q * s.D * 2)                                           # output
+
+
+def indexer_bytes(s) -> int:
+    """Algorithmic bytes of one indexer-score launch: k_idx, q_idx and w read
+    once, the float32 score rows written once."""
+    b = s.B
+    return b * s.N * s.D_I * 2 + b * s.H_I * s.D_I * 2 + b * s.H_I * 4 + b * s.N * 4
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch recorded by the rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "indexer_score_decode_step_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != source_digest(kernel_src):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(batch rows are independent, so N GPUs would each run this same kernel set "
+              "on B/N rows).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    import indexer_top_gathered_amd as dsa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = workloads.C4
+    R = max(1, args.copies)
+    copies = [workloads.step_inputs(s, 4000 + 10 * r, device=dev) for r in range(R)]
+    dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
+    ws = torch.empty(dsa.dsa_decode_step_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    out = torch.empty((s.B, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = copies[i % R]
+        dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"], c["kv_win"],
+                            s.k, s.scale, out=out, ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    us_step = ms_per_step * 1e3
+    sbytes = step_bytes(s)
+    value = sbytes / (us_step * 1e-6) / 1e9
+
+    # Dominant kernel: indexer scoring, same launch configuration as inside
+    # the step, timed alone on the same stream over the same rotation.
+    scores = torch.empty((s.B, s.N), dtype=torch.float32, device=dev)
+    for i in range(args.warmup):
+        c = copies[i % R]
+        dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"], scores=scores, stream=stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        c = copies[i % R]
+        dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"], scores=scores, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    is_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    is_bytes = indexer_bytes(s)
+    achieved = is_bytes / (is_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(os.path.join(ROOT, "indexer_top_gathered_amd", "csrc",
+                                                "indexer_score.hip"))
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": "indexer_score_kernel<4>",
+                "us_per_launch": round(is_us, 3), "bytes_per_launch": is_bytes}
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(us_step, 2), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "decode step B=16 N=32768 H_I=64 D_I=128 k=1024 W=128 "
+                               "H_q=128 D=512 (K=V)", "global_batch": s.B,
+                   "compulsory_bytes_per_step": sbytes, "rotating_input_copies": R,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    del scores
+
+    if not args.no_topk:
+        t = workloads.C2
+        rows = [workloads.normal_rows(t.B, t.N, "bf16", 2006 + r, device=dev) for r in range(R)]
+        tws = torch.empty(dsa.dsa_topk_workspace_bytes(t.B, t.N, t.k, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        oidx = torch.empty((t.B, t.k), dtype=torch.int32, device=dev)
+        for i in range(args.warmup):
+            dsa.dsa_topk(rows[i % R], t.k, out_idx=oidx, ws=tws, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            dsa.dsa_topk(rows[i % R], t.k, out_idx=oidx, ws=tws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        tk_us = e0.elapsed_time(e1) * 1e3 / args.steps
+        tbytes = t.B * t.N * 2 + t.B * t.k * 4
+        # torch.topk on the same rows, as the context ratio the pages report
+        for i in range(3):
+            torch.topk(rows[i % R], t.k, dim=1, sorted=False)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        n_ref = max(10, args.steps // 10)
+        for i in range(n_ref):
+            torch.topk(rows[i % R], t.k, dim=1, sorted=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ref_us = e0.elapsed_time(e1) * 1e3 / n_ref
+        gbps = tbytes / (tk_us * 1e-6) / 1e9
+        line["topk"] = {"workload": "bf16 scores 64 x 131072, k=512, indices only, unsorted",
+                        "us": round(tk_us, 2), "effective_GBps": round(gbps, 1),
+                        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                        "compulsory_bytes": tbytes, "torch_topk_us": round(ref_us, 2),
+                        "speedup_vs_torch_topk": round(ref_us / tk_us, 2)}
+        del rows
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(copies[0], s, sbytes)
+
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, s, sbytes):
+    """The CPU oracle (plain C, double precision) on the same workload: the
+    whole step (indexer, sort-based top-k, softmax attention) over all 16
+    batch rows, with one OpenMP thread per batch row at most."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+
+    h = {k: (workloads.bits16(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())
+         for k, v in inp.items()}
+    ncpu = len(os.sched_getaffinity(0))
+    threads = max(1, min(ncpu, s.B))
+    oracle.set_threads(threads)
+    t0 = time.perf_counter()
+    oracle.step(h["q_idx"], h["k_idx"], h["w"], h["q"], h["kv_cmp"], h["kv_win"], s.k, s.scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_step": round(dt, 3), "host_cpus": ncpu,
+            "sample": "one whole decode step, all 16 batch rows of the production shape"}
+
+
+if __name__ == "__main__":
+    main()

@@ -37,6 +37,71 @@ __device__ __forceinline__ uint32_t composite_pos(uint64_t c) {
   return 0xFFFFFFFFu - (uint32_t)c;
 }
 
+// ---------------------------------------------------------------- wave ops
+// Cross-lane primitives built on DPP row operations (VALU, a few cycles each)
+// and readlane, instead of LDS-routed shuffles. Rows are 16 lanes.
+namespace dpp {
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141, kRowMirror = 0x140;
+}  // namespace dpp
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_zero(uint32_t v) {  // lanes without a source read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_all(uint32_t v) {  // permutations: every lane has a source
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
+  x += dpp_zero<dpp::kRowShr1>(x);
+  x += dpp_zero<dpp::kRowShr2>(x);
+  x += dpp_zero<dpp::kRowShr4>(x);
+  x += dpp_zero<dpp::kRowShr8>(x);
+  x += dpp_zero<dpp::kRowBcast15, 0xA>(x);  // rows 1, 3 add the end of rows 0, 2
+  x += dpp_zero<dpp::kRowBcast31, 0xC>(x);  // rows 2, 3 add the end of row 1
+  return x;
+}
+
+// Reductions over the 64 lanes; the result is wave-uniform.
+struct OpAdd { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a + b; } };
+struct OpMin { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a < b ? a : b; } };
+struct OpMax { __device__ static uint32_t f(uint32_t a, uint32_t b) { return a > b ? a : b; } };
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
+  x = Op::f(x, dpp_all<dpp::kXor1>(x));
+  x = Op::f(x, dpp_all<dpp::kXor2>(x));
+  x = Op::f(x, dpp_all<dpp::kRowHalfMirror>(x));
+  x = Op::f(x, dpp_all<dpp::kRowMirror>(x));  // every lane holds its row's result
+  return Op::f(Op::f(lane_read(x, 0), lane_read(x, 16)), Op::f(lane_read(x, 32), lane_read(x, 48)));
+}
+__device__ __forceinline__ uint64_t u64_of(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_all64(uint64_t v) {
+  return u64_of(dpp_all<CTRL>((uint32_t)v), dpp_all<CTRL>((uint32_t)(v >> 32)));
+}
+template <bool MIN>
+__device__ __forceinline__ uint64_t wave_reduce64(uint64_t x) {
+  auto f = [](uint64_t a, uint64_t b) { return MIN ? (a < b ? a : b) : (a > b ? a : b); };
+  x = f(x, dpp_all64<dpp::kXor1>(x));
+  x = f(x, dpp_all64<dpp::kXor2>(x));
+  x = f(x, dpp_all64<dpp::kRowHalfMirror>(x));
+  x = f(x, dpp_all64<dpp::kRowMirror>(x));
+  uint64_t r = u64_of(lane_read((uint32_t)x, 0), lane_read((uint32_t)(x >> 32), 0));
+#pragma unroll
+  for (int row = 1; row < 4; ++row)
+    r = f(r, u64_of(lane_read((uint32_t)x, 16 * row), lane_read((uint32_t)(x >> 32), 16 * row)));
+  return r;
+}
+
 // ---------------------------------------------------------------- MFMA
 // v_mfma_f32_16x16x32_bf16. Lane l = 16*g + m supplies A[m][8g..8g+7] and
 // B[8g..8g+7][m]; it receives D[4g+i][m] for i < 4.
@@ -64,6 +129,7 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
 struct TopkPlan {
   int segs;         // segments per row
   int seg_len;      // elements per segment (all but the last segment)
+  int vec;          // 16-byte vectors per thread per register block (1..16)
   size_t cand_off;  // byte offsets inside the workspace
   size_t cnt_off;
   size_t bytes;     // total workspace bytes

@@ -1,190 +1,295 @@
 // Top-k selection on gfx950 ("feat: Add DeepSeek-V4 CSA attention kernels",
 // step 3, and its chunked score/top-k pipeline in "The top-k on the GPSIMD
-// engine"; "DeepSelect" project page: a dynamic threshold that starts at
-// minus infinity, blocks visited in a random order that does not depend on
-// the data, and early rejection of everything below the threshold).
+// engine"; "DeepSelect" project page: a threshold that only rises, early
+// rejection of everything below it, and a worst-case guarantee that does not
+// depend on the order of the data).
 //
 // The answer is exact under the order (value desc, index asc): every score
-// is mapped to a 64-bit composite key (order-preserving value key in the
-// high word, complemented position in the low word), so the k largest
-// composites are the unique answer.
+// is mapped to a 64-bit composite (order-preserving value key in the high
+// word, complemented position in the low word), so the k largest composites
+// are the unique answer. The kernels never sort.
 //
-// Stage 1, one workgroup per (row, segment): stream the segment once in
-// sub-chunks of 4096 scores, visiting the sub-chunks in a Weyl-sequence
-// order (a golden-ratio stride coprime to the count). Each thread rejects
-// its 8 scores with one compare against the running threshold; survivors
-// are appended to an LDS candidate buffer in a fixed order (wave prefix
-// sums, waves in index order). When the buffer could overflow on the next
-// sub-chunk, an exact radix select finds the k-th largest composite, the
-// buffer is compacted to k entries and that composite becomes the new
-// threshold. Anything at or below it can never enter this segment's top-k.
-// The segment ends with its exact top-min(k, length) in the workspace.
+// Stage 1, one workgroup per (row, segment). The segment is read once from
+// HBM straight into registers, V 16-byte vectors per thread, all loads in
+// flight together, and turned into order keys in place (bf16 keys two per
+// 32-bit word). A threshold comes cheaply from "group maxima": group
+// (thread t, element e) holds element e of every vector of thread t, so its
+// members are spread evenly over the block. If at least k groups have a
+// maximum >= T then at least k scores are >= T, so T may reject everything
+// below it; one histogram round over the 512*E group maxima (E = 8 bf16 or
+// 4 float32 per vector) gives such a T. Random rows let a few percent
+// through and sorted rows about k, because the spread-out groups see the
+// whole range. Each vector is first tested by its maximum, so most are
+// dismissed with a handful of instructions; survivors go to an LDS buffer in
+// thread order (block prefix sum). A later block of a long segment is also
+// filtered by the exact k-th candidate so far. If a block's survivors would
+// overflow the buffer, that block is taken one vector at a time with exact
+// selects in between. At most 2k candidates leave the segment; more are
+// first cut to exactly k.
 //
-// Stage 2, one workgroup per row: load the segments' candidates into LDS,
-// radix-select the row's k-th composite, and write the k winners (indices,
-// optional value copies) either in buffer order or sorted by index.
+// Stage 2, one workgroup per row: load every segment's candidates at once,
+// compact them into LDS, select the row's k-th composite exactly, and write
+// the k winners (indices, optional value copies), in buffer order or sorted
+// by index.
+//
+// Exact selection is a radix select whose 10-bit digits split the current
+// [lo, hi] range of the candidates into 1024 equal buckets (a histogram
+// round picks the bucket holding the K-th largest), so each round narrows
+// the range 1024-fold whatever the value distribution, and ties are split by
+// position.
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kTkThreads = 512;
-constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kTkEpt = 8;                           // scores per thread per sub-chunk
-constexpr int kTkSub = kTkThreads * kTkEpt;         // 4096 scores per sub-chunk
-constexpr int kMergeThreads = 1024;
-constexpr int kMergeWaves = kMergeThreads / kWave;
-constexpr int kMaxK = 4096;
-constexpr int kSegCap = 8192;                       // LDS candidates per segment (>= kMaxK + kTkSub)
-constexpr int kMergeCap = 8192;                     // candidates per row in stage 2
+constexpr int kTkMaxVec = 8;       // vectors per thread per register block
+constexpr int kSegCap = 8192;      // LDS candidates in stage 1 (>= 4096 + 512*8)
+constexpr int kMergeThreads = 512;
+constexpr int kMergeCap = 16384;   // candidate slots per row in stage 2
+constexpr int kMaxWaves = 16;
+constexpr int kBins = 1024;        // buckets of an exact-select round
+constexpr int kBinBits = 10;
+constexpr int kGBins = 256;        // buckets of the group-maxima round
 
-// LDS-only barrier: wait for this wave's LDS traffic, then meet the others.
-// Pending global loads (prefetches) are left in flight.
+// Per-half unsigned maximum of two words holding two 16-bit keys each. Plain
+// 32-bit code: 16-bit vector element access was miscompiled (element 0 was
+// returned for every index), so it is avoided throughout.
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  const uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
+  const uint32_t hi = max(a >> 16, b >> 16);
+  return lo | (hi << 16);
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ uint32_t gcd_u32(uint32_t a, uint32_t b) {
-  while (b) {
-    uint32_t t = a % b;
-    a = b;
-    b = t;
-  }
-  return a;
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
-  return v;
-}
-
-// Shared scratch of the block-wide helpers below.
-struct SelectScratch {
-  uint32_t hist[256];
-  uint32_t wave_sum[kMergeWaves];
+struct Scratch {
+  alignas(16) uint32_t hist[2][kBins];
+  uint64_t wlo[kMaxWaves], whi[kMaxWaves];
+  uint32_t wsum[kMaxWaves], wmin[kMaxWaves], wmax[kMaxWaves];
   uint32_t digit, above, in_bucket;
 };
 
-// Exclusive block-wide scan of one count per thread, in thread order.
-// Returns the exclusive prefix; *total receives the sum. Two barriers.
+// Exclusive block-wide scan in thread order; *total gets the sum. Two barriers.
 template <int THREADS>
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, SelectScratch& sc) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  constexpr int WAVES = THREADS / kWave;
-  const uint32_t inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) sc.wave_sum[wave] = inc;
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, Scratch& sc) {
+  constexpr int W = THREADS / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const uint32_t inc = wave_scan_incl(v);
+  if (lane == kWave - 1) sc.wsum[wave] = inc;
   lds_barrier();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < WAVES; ++w2) {
-    const uint32_t ws = sc.wave_sum[w2];
-    before += (w2 < wave) ? ws : 0u;
-    all += ws;
+  for (int w = 0; w < W; ++w) {
+    const uint32_t s = sc.wsum[w];
+    before += (w < wave) ? s : 0u;
+    all += s;
   }
   lds_barrier();
   *total = all;
   return before + inc - v;
 }
 
-// Radix select over the LDS buffer buf[0..cnt): returns T such that exactly
-// K entries are >= T (entries are distinct). Digits of 8 bits from the top,
-// skipping bit ranges that cannot differ between candidates: only
-// `key_levels` bytes of the value key carry information (2 for bf16 scores,
-// whose low key half follows from the sign, 4 for float32), and of the
-// complemented position only the low `pos_bits` bits vary. Stops as soon as
-// the bucket holding the K-th entry is taken whole.
-template <int THREADS>
-__device__ uint64_t block_select_kth(const uint64_t* buf, int cnt, int K, int key_levels,
-                                     int pos_bits, SelectScratch& sc) {
+// Wave 0 finds the digit whose bucket holds the need-th largest entry of
+// hist[0..NB) and publishes it; ends with a barrier.
+template <int NB>
+__device__ void pick_digit(const uint32_t* hist, uint32_t need, Scratch& sc, uint32_t& digit,
+                           uint32_t& above, uint32_t& in_bucket) {
+  constexpr int PER = NB / kWave;
+  static_assert(PER % 4 == 0, "lanes read their bins as 16-byte vectors");
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  uint64_t prefix = 0, mask = 0;
-  uint32_t need = (uint32_t)K;
-  int shift = 56;
-  int level = 0;
-  for (;;) {
-    for (int i = tid; i < 256; i += THREADS) sc.hist[i] = 0;
-    lds_barrier();
-    for (int i = tid; i < cnt; i += THREADS) {
-      const uint64_t e = buf[i];
-      if ((e & mask) == prefix) atomicAdd(&sc.hist[(uint32_t)(e >> shift) & 255u], 1u);
+  if (tid < kWave) {
+    // Lane l owns the PER contiguous bins ending at NB-1-PER*l, read as
+    // 16-byte vectors (a scalar stride-PER pattern would hit one LDS bank
+    // many times over). c[j] is bin NB-1-PER*l-j: lane order is descending.
+    const int base = NB - PER * (tid + 1);
+    uint32_t c[PER], local = 0;
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(hist + base + 4 * q);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[PER - 1 - (4 * q + i)] = x[i];
     }
-    lds_barrier();
-    if (tid < kWave) {
-      // Lane l owns bins 255-4l .. 252-4l, so lane order is descending digits.
-      uint32_t c[4];
-      uint32_t local = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = sc.hist[255 - 4 * lane - j];
-        local += c[j];
-      }
-      const uint32_t inc = wave_inclusive_scan(local);
-      const uint64_t hit = __ballot(inc >= need);
-      const int first = __ffsll((long long)hit) - 1;
-      if (lane == first) {
-        uint32_t run = inc - local;
+    for (int j = 0; j < PER; ++j) local += c[j];
+    const uint32_t inc = wave_scan_incl(local);
+    const uint64_t hit = __ballot(inc >= need);
+    const int first = __ffsll((long long)hit) - 1;
+    if (tid == first) {
+      // The winning lane walks its own bins (registers, no LDS round trips).
+      uint32_t run = inc - local, d = 0, a = 0, b = 0;
+      bool found = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (run + c[j] >= need) {
-            sc.digit = 255u - 4u * lane - j;
-            sc.above = run;
-            sc.in_bucket = c[j];
-            break;
-          }
-          run += c[j];
+      for (int j = 0; j < PER; ++j) {
+        if (!found && run + c[j] >= need) {
+          found = true;
+          d = (uint32_t)(NB - 1 - PER * tid - j);
+          a = run;
+          b = c[j];
         }
+        run += c[j];
       }
-    }
-    lds_barrier();
-    const uint32_t digit = sc.digit, above = sc.above, in_bucket = sc.in_bucket;
-    need -= above;
-    prefix |= (uint64_t)digit << shift;
-    mask |= (uint64_t)0xFF << shift;
-    if (in_bucket == need) break;
-    // Next digit. Overlapping the last position digit with bits already
-    // fixed is harmless: those bits match the prefix for every counted entry.
-    ++level;
-    if (level < key_levels) {
-      shift = 56 - 8 * level;
-    } else if (level == key_levels) {
-      // Entering the position digits. The skipped bits are the same for
-      // every entry still in play, so the prefix must carry their actual
-      // values: for bf16 scores the low half of the value key is 0x0000 for
-      // a non-negative value and 0xFFFF for a negative one (the sign sits
-      // in the prefix's top bit); above the low pos_bits bits the
-      // complemented position is all ones.
-      if (key_levels == 2) {
-        const uint64_t low_key = (prefix >> 63) ? 0u : 0xFFFFu;
-        prefix |= low_key << 32;
-        mask |= (uint64_t)0xFFFF << 32;
-      }
-      const uint64_t high_ones = pos_bits >= 32 ? 0 : ((uint64_t)(0xFFFFFFFFu >> pos_bits) << pos_bits);
-      prefix |= high_ones;
-      mask |= high_ones;
-      shift = max(pos_bits - 8, 0);
-    } else {
-      if (shift == 0) break;  // unreachable for distinct entries
-      shift = max(shift - 8, 0);
+      sc.digit = d;
+      sc.above = a;
+      sc.in_bucket = b;
     }
   }
-  return prefix;
+  lds_barrier();
+  digit = sc.digit;
+  above = sc.above;
+  in_bucket = sc.in_bucket;
 }
 
-// Keep the entries >= thr, preserving their order; returns the new count.
-// Each thread moves a contiguous run of entries through registers.
-template <int THREADS, int MAXPER>
-__device__ int block_compact(uint64_t* buf, int cnt, uint64_t thr, SelectScratch& sc) {
+// Block-wide min and max of the entries of buf[0..cnt) inside [lo, hi];
+// every thread gets both. One barrier; the wlo/whi slots are reused only
+// after further barriers.
+template <int THREADS>
+__device__ void bucket_range(const uint64_t* buf, int cnt, uint64_t& lo, uint64_t& hi, Scratch& sc) {
+  constexpr int W = THREADS / kWave;
   const int tid = threadIdx.x;
-  const int per = (cnt + THREADS - 1) / THREADS;  // <= MAXPER by construction
-  const int lo = min(cnt, tid * per);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint64_t a = ~(uint64_t)0, z = 0;
+  for (int i = tid; i < cnt; i += THREADS) {
+    const uint64_t e = buf[i];
+    if (e >= lo && e <= hi) {
+      a = e < a ? e : a;
+      z = e > z ? e : z;
+    }
+  }
+  a = wave_reduce64<true>(a);
+  z = wave_reduce64<false>(z);
+  if (lane == 0) {
+    sc.wlo[wave] = a;
+    sc.whi[wave] = z;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    a = sc.wlo[w] < a ? sc.wlo[w] : a;
+    z = sc.whi[w] > z ? sc.whi[w] : z;
+  }
+  lo = a;
+  hi = z;
+}
+
+// Exact: the T for which exactly K of the distinct entries buf[0..cnt) are
+// >= T (1 <= K <= cnt). Each round splits the entries' actual [lo, hi] into
+// 1024 equal buckets, keeps the bucket holding the K-th largest, and then
+// shrinks [lo, hi] to the entries inside that bucket. Expects both hist
+// halves clear behind a barrier and leaves them clear.
+template <int THREADS>
+__device__ __noinline__ uint64_t select_exact(const uint64_t* buf, int cnt, int K, Scratch& sc) {
+  const int tid = threadIdx.x;
+  uint64_t lo = 0, hi = ~(uint64_t)0;
+  bucket_range<THREADS>(buf, cnt, lo, hi, sc);
+  uint32_t need = (uint32_t)K;
+  uint64_t result = lo;
+  for (int round = 0; round < 8; ++round) {  // 10-bit rounds: 7 narrow any 64-bit range
+    const uint64_t range = hi - lo;
+    if (range == 0) {
+      result = lo;
+      break;
+    }
+    const int hb = 63 - __clzll((long long)range);
+    const int shift = hb >= kBinBits ? hb - (kBinBits - 1) : 0;
+    uint32_t* cur = sc.hist[round & 1];
+    uint32_t* nxt = sc.hist[(round + 1) & 1];
+    for (int i = tid; i < cnt; i += THREADS) {
+      const uint64_t e = buf[i];
+      if (e >= lo && e <= hi) atomicAdd(&cur[(uint32_t)((e - lo) >> shift)], 1u);
+    }
+    for (int i = tid; i < kBins; i += THREADS) nxt[i] = 0;
+    lds_barrier();
+    uint32_t digit, above, in_bucket;
+    pick_digit<kBins>(cur, need, sc, digit, above, in_bucket);
+    for (int i = tid; i < kBins; i += THREADS) cur[i] = 0;  // ordered by the next barrier
+    need -= above;
+    const uint64_t blo = lo + ((uint64_t)digit << shift);
+    result = blo;
+    if (in_bucket == need) break;
+    const uint64_t bhi = blo + (((uint64_t)1 << shift) - 1);
+    lo = blo;
+    hi = bhi < hi ? bhi : hi;
+    bucket_range<THREADS>(buf, cnt, lo, hi, sc);
+  }
+  lds_barrier();
+  return result;
+}
+
+// The same exact select over entries held in registers: PER slots per
+// thread, 0 = empty (real composites are non-zero). No LDS reads per pass.
+template <int THREADS, int PER>
+__device__ void regs_range(const uint64_t (&v)[PER], uint64_t& lo, uint64_t& hi, Scratch& sc) {
+  constexpr int W = THREADS / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  uint64_t a = ~(uint64_t)0, z = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool in = v[j] && v[j] >= lo && v[j] <= hi;
+    a = (in && v[j] < a) ? v[j] : a;
+    z = (in && v[j] > z) ? v[j] : z;
+  }
+  a = wave_reduce64<true>(a);
+  z = wave_reduce64<false>(z);
+  if (lane == 0) {
+    sc.wlo[wave] = a;
+    sc.whi[wave] = z;
+  }
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    a = sc.wlo[w] < a ? sc.wlo[w] : a;
+    z = sc.whi[w] > z ? sc.whi[w] : z;
+  }
+  lo = a;
+  hi = z;
+}
+
+template <int THREADS, int PER>
+__device__ uint64_t select_exact_regs(const uint64_t (&v)[PER], int K, Scratch& sc) {
+  const int tid = threadIdx.x;
+  uint64_t lo = 1, hi = ~(uint64_t)0;
+  regs_range<THREADS, PER>(v, lo, hi, sc);
+  uint32_t need = (uint32_t)K;
+  uint64_t result = lo;
+  for (int round = 0; round < 8; ++round) {
+    const uint64_t range = hi - lo;
+    if (range == 0) {
+      result = lo;
+      break;
+    }
+    const int hb = 63 - __clzll((long long)range);
+    const int shift = hb >= kBinBits ? hb - (kBinBits - 1) : 0;
+    uint32_t* cur = sc.hist[round & 1];
+    uint32_t* nxt = sc.hist[(round + 1) & 1];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (v[j] && v[j] >= lo && v[j] <= hi) atomicAdd(&cur[(uint32_t)((v[j] - lo) >> shift)], 1u);
+    for (int i = tid; i < kBins; i += THREADS) nxt[i] = 0;
+    lds_barrier();
+    uint32_t digit, above, in_bucket;
+    pick_digit<kBins>(cur, need, sc, digit, above, in_bucket);
+    for (int i = tid; i < kBins; i += THREADS) cur[i] = 0;  // ordered by the next barrier
+    need -= above;
+    const uint64_t blo = lo + ((uint64_t)digit << shift);
+    result = blo;
+    if (in_bucket == need) break;
+    const uint64_t bhi = blo + (((uint64_t)1 << shift) - 1);
+    lo = blo;
+    hi = bhi < hi ? bhi : hi;
+    regs_range<THREADS, PER>(v, lo, hi, sc);
+  }
+  lds_barrier();
+  return result;
+}
+
+// Keep the entries >= thr of buf[0..cnt), in order; returns the new count.
+template <int THREADS, int MAXPER>
+__device__ __noinline__ int block_compact(uint64_t* buf, int cnt, uint64_t thr, Scratch& sc) {
+  const int per = (cnt + THREADS - 1) / THREADS;
+  const int lo = min(cnt, (int)threadIdx.x * per);
   const int hi = min(cnt, lo + per);
   uint64_t v[MAXPER];
   uint32_t keep = 0;
@@ -195,7 +300,7 @@ __device__ int block_compact(uint64_t* buf, int cnt, uint64_t thr, SelectScratch
     keep += (i < hi && v[j] >= thr) ? 1u : 0u;
   }
   uint32_t total;
-  uint32_t pos = block_exclusive_scan<THREADS>(keep, &total, sc);  // also orders reads before writes
+  uint32_t pos = block_exclusive_scan<THREADS>(keep, &total, sc);  // orders reads before writes
 #pragma unroll
   for (int j = 0; j < MAXPER; ++j) {
     const int i = lo + j;
@@ -205,210 +310,367 @@ __device__ int block_compact(uint64_t* buf, int cnt, uint64_t thr, SelectScratch
   return (int)total;
 }
 
+// ---------------------------------------------------------------- keys
+// bf16: two 16-bit order keys per word, computed on the raw pair. A negative
+// half becomes its complement, a non-negative one gets its top bit set. The
+// pattern 0xFFFF (used for padding) maps to 0, below every real score. -0.0
+// maps to 0x7FFF, one below +0.0; canon16 merges the two.
+__device__ __forceinline__ uint32_t bf16_pair_keys(uint32_t w) {
+  const uint32_t neg = (w >> 15) & 0x00010001u;
+  return w ^ (neg * 0x7FFFu) ^ 0x80008000u;
+}
+__device__ __forceinline__ uint32_t canon16(uint32_t k16) { return k16 == 0x7FFFu ? 0x8000u : k16; }
+// The float32 order key of the bf16 value with (canonical) 16-bit key k16.
+__device__ __forceinline__ uint32_t key32_of_key16(uint32_t k16) {
+  return (k16 << 16) | (k16 < 0x8000u ? 0xFFFFu : 0u);
+}
+// float32 keys without the -0 merge (padding 0xFFFFFFFF maps to 0).
+__device__ __forceinline__ uint32_t f32_raw_key(uint32_t bits) {
+  return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t canon32(uint32_t k) { return k == 0x7FFFFFFFu ? 0x80000000u : k; }
+
 template <bool BF16>
-__device__ __forceinline__ uint32_t load_key(const void* row, int64_t j) {
+__device__ __forceinline__ uint32_t elem_key32(const u32x4& kv, int e) {
   if (BF16) {
-    const uint16_t h = reinterpret_cast<const uint16_t*>(row)[j];
-    return f32_key((uint32_t)h << 16);
-  } else {
-    return f32_key(reinterpret_cast<const uint32_t*>(row)[j]);
+    const uint32_t w = kv[e >> 1];
+    return key32_of_key16(canon16((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
   }
+  return canon32(kv[e]);
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t elem_rawkey(const u32x4& kv, int e) {
+  if (BF16) {
+    const uint32_t w = kv[e >> 1];
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+  return kv[e];
 }
 
-// Loads the 8 keys of one thread's slot. Positions at or past `end` get key 0,
-// whose composite (0 in the high word) is below every real score's.
+// One thread's vector at row position p0, as keys. Padding past `end` gets
+// key 0.
 template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ void load_keys(const void* row, int64_t j0, int64_t end, uint32_t key[kTkEpt]) {
-  if (ALIGNED && j0 + kTkEpt <= end) {
-    if (BF16) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const uint16_t*>(row) + j0));
+__device__ __forceinline__ u32x4 load_keys(const void* row, int64_t p0, int64_t end) {
+  constexpr int E = BF16 ? 8 : 4;
+  u32x4 r;
+  if (ALIGNED && p0 + E <= end) {
+    const u32x4* src = BF16 ? reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(row) + p0)
+                            : reinterpret_cast<const u32x4*>(reinterpret_cast<const uint32_t*>(row) + p0);
+    r = __builtin_nontemporal_load(src);
+  } else {
+    r = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[2 * e] = f32_key(v[e] << 16);
-        key[2 * e + 1] = f32_key(v[e] & 0xFFFF0000u);
-      }
-    } else {
-      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint32_t*>(row) + j0);
-      const u32x4 v0 = __builtin_nontemporal_load(p);
-      const u32x4 v1 = __builtin_nontemporal_load(p + 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        key[e] = f32_key(v0[e]);
-        key[4 + e] = f32_key(v1[e]);
+    for (int e = 0; e < E; ++e) {
+      if (p0 + e < end) {
+        if (BF16) {
+          const uint32_t h = reinterpret_cast<const uint16_t*>(row)[p0 + e];
+          r[e >> 1] = (e & 1) ? ((r[e >> 1] & 0xFFFFu) | (h << 16)) : ((r[e >> 1] & 0xFFFF0000u) | h);
+        } else {
+          r[e] = reinterpret_cast<const uint32_t*>(row)[p0 + e];
+        }
       }
     }
-  } else {
+  }
 #pragma unroll
-    for (int e = 0; e < kTkEpt; ++e) key[e] = (j0 + e < end) ? load_key<BF16>(row, j0 + e) : 0u;
+  for (int j = 0; j < 4; ++j) r[j] = BF16 ? bf16_pair_keys(r[j]) : f32_raw_key(r[j]);
+  return r;
+}
+
+// From below: a T with at least K of the G group maxima per thread (raw
+// keys, 0 = none) >= T, from two range-splitting histogram rounds; 1 when
+// fewer than K maxima exist.
+template <int G>
+__device__ uint32_t group_threshold(const uint32_t (&g)[G], int K, Scratch& sc) {
+  constexpr int W = kTkThreads / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0, n = 0;
+#pragma unroll
+  for (int e = 0; e < G; ++e) {
+    if (g[e]) {
+      lo = min(lo, g[e]);
+      hi = max(hi, g[e]);
+      ++n;
+    }
+  }
+  n = wave_reduce<OpAdd>(n);
+  lo = wave_reduce<OpMin>(lo);
+  hi = wave_reduce<OpMax>(hi);
+  if (lane == 0) {
+    sc.wsum[wave] = n;
+    sc.wmin[wave] = lo;
+    sc.wmax[wave] = hi;
+  }
+  lds_barrier();
+  n = 0;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    n += sc.wsum[w];
+    lo = min(lo, sc.wmin[w]);
+    hi = max(hi, sc.wmax[w]);
+  }
+  if ((int)n < K) return 1u;  // uniform
+  uint32_t need = (uint32_t)K;
+  for (int round = 0; round < 2; ++round) {
+    const uint32_t range = hi - lo;
+    if (range == 0) break;
+    const int hb = 31 - __clz(range);
+    const int shift = hb > 7 ? hb - 7 : 0;
+    uint32_t* h = sc.hist[round];
+#pragma unroll
+    for (int e = 0; e < G; ++e)
+      if (g[e] >= lo && g[e] <= hi) atomicAdd(&h[(g[e] - lo) >> shift], 1u);
+    lds_barrier();
+    uint32_t digit, above, in_bucket;
+    pick_digit<kGBins>(h, need, sc, digit, above, in_bucket);
+    for (int i = threadIdx.x; i < kGBins; i += kTkThreads) h[i] = 0;  // ordered by later barriers
+    need -= above;
+    const uint32_t blo = lo + (digit << shift);
+    if (in_bucket == need) return blo;
+    lo = blo;
+    const uint32_t bhi = blo + ((1u << shift) - 1u);
+    hi = bhi < hi ? bhi : hi;
+  }
+  return lo;
+}
+
+template <bool BF16, int V>
+__device__ __forceinline__ void write_admitted(uint64_t* cand, uint32_t at, const u32x4 (&kv)[V],
+                                               uint64_t adm, int64_t base) {
+  constexpr int E = BF16 ? 8 : 4;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    uint32_t m = (uint32_t)(adm >> (v * E)) & ((1u << E) - 1u);
+    const int64_t p0 = base + ((int64_t)v * kTkThreads + threadIdx.x) * E;
+    while (m) {
+      const int e = __ffs(m) - 1;
+      m &= m - 1;
+      uint32_t key;
+      if (BF16) {
+        const uint32_t w = kv[v][e >> 1];
+        key = key32_of_key16(canon16((e & 1) ? (w >> 16) : (w & 0xFFFFu)));
+      } else {
+        key = canon32(kv[v][e]);
+      }
+      cand[at++] = composite(key, (uint32_t)(p0 + e));
+    }
   }
 }
 
-struct SegShared {
-  SelectScratch sc;
-  uint32_t wave_cnt[kTkWaves];
-};
+// Admission bits of vector v: raw key >= t0 and, when have_thr, composite > thr.
+template <bool BF16>
+__device__ __forceinline__ uint32_t admit_vector(const u32x4& kv, uint32_t t0, bool have_thr,
+                                                 uint64_t thr, int64_t p0) {
+  constexpr int E = BF16 ? 8 : 4;
+  uint32_t vmax;
+  if (BF16) {
+    const uint32_t m = max_u16x2(max_u16x2(kv[0], kv[1]), max_u16x2(kv[2], kv[3]));
+    vmax = max(m & 0xFFFFu, m >> 16);
+  } else {
+    vmax = max(max(kv[0], kv[1]), max(kv[2], kv[3]));
+  }
+  uint32_t bits = 0;
+  if (vmax >= t0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      bool ok = elem_rawkey<BF16>(kv, e) >= t0;
+      if (have_thr && ok) ok = composite(elem_key32<BF16>(kv, e), (uint32_t)(p0 + e)) > thr;
+      bits |= ok ? (1u << e) : 0u;
+    }
+  }
+  return bits;
+}
 
-template <bool BF16, bool ALIGNED>
+template <bool BF16, bool ALIGNED, int V>
 __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
-    const void* __restrict__ scores, int N, int k, int seg_len, int segs, int pos_bits,
+    const void* __restrict__ scores, int N, int k, int seg_len, int segs,
     uint64_t* __restrict__ cand_out, uint32_t* __restrict__ cnt_out) {
+  constexpr int E = BF16 ? 8 : 4;
+  static_assert(V * E <= 64, "the admission mask holds 64 bits");
   extern __shared__ uint64_t cand[];  // kSegCap entries
-  __shared__ SegShared sh;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  __shared__ Scratch sc;
   const int b = blockIdx.y;
   const int sidx = blockIdx.x;
   const size_t esz = BF16 ? 2 : 4;
   const void* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;
   const int64_t seg_start = (int64_t)sidx * seg_len;
   const int64_t seg_end = min((int64_t)N, seg_start + seg_len);
-  const int L = (int)(seg_end - seg_start);
-  const int nsub = (L + kTkSub - 1) / kTkSub;
-  constexpr int key_levels = BF16 ? 2 : 4;
+  constexpr int64_t kBlock = (int64_t)kTkThreads * V * E;
 
-  // Visiting order: p(it) = (c0 + a*it) mod nsub with gcd(a, nsub) = 1 and a
-  // near nsub/phi, so consecutive visits land far apart for any input.
-  uint32_t a = (uint32_t)(nsub * 0.6180339887f);
-  if (a < 1) a = 1;
-  while (gcd_u32(a, (uint32_t)nsub) != 1u) ++a;
-  const uint32_t c0 = (uint32_t)(((uint64_t)b * 2654435761u + (uint64_t)sidx * 40503u) % (uint64_t)nsub);
-
-  uint64_t thr = 0;  // admit composites > thr
+  for (int i = threadIdx.x; i < kBins; i += kTkThreads) {
+    sc.hist[0][i] = 0;
+    sc.hist[1][i] = 0;
+  }
   int cnt = 0;
   bool have_thr = false;
+  uint64_t thr = 0;  // once set: admit only composites > thr
 
-  uint32_t nxt[kTkEpt];
-  {
-    const int64_t j0 = seg_start + (int64_t)(c0 % nsub) * kTkSub + tid * kTkEpt;
-    load_keys<BF16, ALIGNED>(row, j0, seg_end, nxt);
-  }
-  for (int it = 0; it < nsub; ++it) {
-    const uint32_t p = (uint32_t)((c0 + (uint64_t)a * it) % (uint64_t)nsub);
-    const int64_t j0 = seg_start + (int64_t)p * kTkSub + tid * kTkEpt;
-    uint32_t key[kTkEpt];
+  for (int64_t base = seg_start; base < seg_end; base += kBlock) {
+    u32x4 kv[V];
 #pragma unroll
-    for (int e = 0; e < kTkEpt; ++e) key[e] = nxt[e];
-    if (it + 1 < nsub) {
-      const uint32_t pn = (uint32_t)((c0 + (uint64_t)a * (it + 1)) % (uint64_t)nsub);
-      load_keys<BF16, ALIGNED>(row, seg_start + (int64_t)pn * kTkSub + tid * kTkEpt, seg_end, nxt);
-    }
-    // Filter: one compare of the largest key against the threshold's key
-    // rejects the whole slot in the common case.
-    uint32_t kmax = key[0];
+    for (int v = 0; v < V; ++v)
+      kv[v] = load_keys<BF16, ALIGNED>(row, base + ((int64_t)v * kTkThreads + threadIdx.x) * E, seg_end);
+    // Group maxima (raw keys): element e of every vector of this thread.
+    uint32_t g[E];
+    if (BF16) {
+      uint32_t m[4];
 #pragma unroll
-    for (int e = 1; e < kTkEpt; ++e) kmax = max(kmax, key[e]);
-    const uint32_t thr_key = (uint32_t)(thr >> 32);
-    uint32_t pass_mask = 0;
-    if (kmax >= thr_key) {
+      for (int j = 0; j < 4; ++j) m[j] = kv[0][j];
 #pragma unroll
-      for (int e = 0; e < kTkEpt; ++e) {
-        const uint64_t c = composite(key[e], (uint32_t)(j0 + e));
-        pass_mask |= (key[e] != 0u && c > thr) ? (1u << e) : 0u;
+      for (int v = 1; v < V; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], kv[v][j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g[2 * j] = m[j] & 0xFFFFu;
+        g[2 * j + 1] = m[j] >> 16;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        g[e] = kv[0][e];
+#pragma unroll
+        for (int v = 1; v < V; ++v) g[e] = max(g[e], kv[v][e]);
       }
     }
-    const uint32_t npass = __popc(pass_mask);
-    uint32_t excl = 0;
-    if (__ballot(npass != 0) != 0) {
-      const uint32_t inc = wave_inclusive_scan(npass);
-      excl = inc - npass;
-      if (lane == kWave - 1) sh.wave_cnt[wave] = inc;
-    } else if (lane == 0) {
-      sh.wave_cnt[wave] = 0;
-    }
-    lds_barrier();
-    uint32_t base = (uint32_t)cnt, total = 0;
+    // About 2k groups: fewer, larger groups cost fewer histogram atomics and
+    // still leave a threshold near the k-th largest score. Fold the E maxima
+    // per thread in halves (a zero slot means "no group") while half of them
+    // still give 2k groups.
+    const int gpt = (2 * k + kTkThreads - 1) / kTkThreads;  // wanted groups per thread
 #pragma unroll
-    for (int w2 = 0; w2 < kTkWaves; ++w2) {
-      const uint32_t wc = sh.wave_cnt[w2];
-      base += (w2 < wave) ? wc : 0u;
-      total += wc;
-    }
-    if (pass_mask) {
-      uint32_t at = base + excl;
+    for (int half = E / 2; half >= 1; half /= 2) {
+      if (gpt <= half) {  // uniform
 #pragma unroll
-      for (int e = 0; e < kTkEpt; ++e)
-        if (pass_mask & (1u << e)) cand[at++] = composite(key[e], (uint32_t)(j0 + e));
+        for (int j = 0; j < half; ++j) {
+          g[j] = max(g[j], g[j + half]);
+          g[j + half] = 0;
+        }
+      }
     }
-    cnt += (int)total;
-    lds_barrier();
-    // Select when the next sub-chunk might not fit, and once early (at 2k
-    // candidates) so that a useful threshold exists from then on.
-    if (cnt > k && (cnt > kSegCap - kTkSub || (!have_thr && cnt >= 2 * k))) {
-      const uint64_t t = block_select_kth<kTkThreads>(cand, cnt, k, key_levels, pos_bits, sh.sc);
-      cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sh.sc);
-      thr = t ? t - 1 : 0;  // t > 0 whenever more than k candidates exist
+    uint32_t t0 = group_threshold<E>(g, k, sc);
+    // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
+    if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
+    // Admission: raw key >= t0 and, once an exact threshold exists, composite > thr.
+    uint64_t adm = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      adm |= (uint64_t)admit_vector<BF16>(kv[v], t0, have_thr, thr,
+                                          base + ((int64_t)v * kTkThreads + threadIdx.x) * E)
+             << (v * E);
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan<kTkThreads>((uint32_t)__popcll(adm), &total, sc);
+    if (base == seg_start && base + kBlock >= seg_end && (int)total <= 2 * k) {
+      // The whole segment in one block and its survivors fit the output
+      // slots: write them straight to the workspace.
+      write_admitted<BF16, V>(cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k), excl, kv, adm, base);
+      if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = total;
+      return;
+    }
+    if (cnt + (int)total <= kSegCap) {
+      write_admitted<BF16, V>(cand, (uint32_t)cnt + excl, kv, adm, base);
+      cnt += (int)total;
+      lds_barrier();
+    } else {
+      // Too many survivors: one vector at a time (each adds at most 512*E
+      // entries), with an exact select whenever the next might not fit;
+      // each vector is filtered against the thresholds current at its turn.
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        if (cnt + kTkThreads * E > kSegCap && cnt > k) {
+          const uint64_t t = select_exact<kTkThreads>(cand, cnt, k, sc);
+          cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sc);
+          thr = t - 1;  // t > 0: real composites have a non-zero high word
+          have_thr = true;
+        }
+        const int64_t p0 = base + ((int64_t)v * kTkThreads + threadIdx.x) * E;
+        const uint64_t vbits = (uint64_t)admit_vector<BF16>(kv[v], t0, have_thr, thr, p0) << (v * E);
+        uint32_t vt;
+        const uint32_t vx = block_exclusive_scan<kTkThreads>((uint32_t)__popcll(vbits), &vt, sc);
+        write_admitted<BF16, V>(cand, (uint32_t)cnt + vx, kv, vbits, base);
+        cnt += (int)vt;
+        lds_barrier();
+      }
+    }
+    // Before another block: cut to the exact top k so that block is also
+    // filtered by the k-th composite.
+    if (base + kBlock < seg_end && cnt > k) {
+      const uint64_t t = select_exact<kTkThreads>(cand, cnt, k, sc);
+      cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sc);
+      thr = t - 1;
       have_thr = true;
     }
   }
-  if (cnt > k) {
-    const uint64_t t = block_select_kth<kTkThreads>(cand, cnt, k, key_levels, pos_bits, sh.sc);
-    cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sh.sc);
+  // At most 2k candidates leave the segment.
+  if (cnt > 2 * k) {
+    const uint64_t t = select_exact<kTkThreads>(cand, cnt, k, sc);
+    cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sc);
   }
-  cnt = min(cnt, k);  // never more than the k slots this segment owns
-  uint64_t* out = cand_out + ((size_t)b * segs + sidx) * (size_t)k;
-  for (int i = tid; i < cnt; i += kTkThreads) out[i] = cand[i];
-  if (tid == 0) cnt_out[(size_t)b * segs + sidx] = (uint32_t)cnt;
+  cnt = min(cnt, 2 * k);
+  uint64_t* out = cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k);
+  for (int i = threadIdx.x; i < cnt; i += kTkThreads) out[i] = cand[i];
+  if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = (uint32_t)cnt;
 }
 
-struct MergeShared {
-  SelectScratch sc;
-  uint32_t seg_off[65];
-};
-
-template <bool BF16>
+template <bool BF16, int kPer>  // kPer: candidate slots per thread (segs * 2k <= 512 * kPer)
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
-    const void* __restrict__ scores, int N, int k, int segs, int pos_bits,
+    const void* __restrict__ scores, int N, int k, int segs,
     const uint64_t* __restrict__ cand_in, const uint32_t* __restrict__ cnt_in,
     int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index) {
-  extern __shared__ uint64_t buf[];  // kMergeCap entries
-  __shared__ MergeShared sh;
+  extern __shared__ uint32_t pos_lds[];  // k positions (sorted path)
+  __shared__ Scratch sc;
+  __shared__ uint32_t seg_cnt[64];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  if (tid == 0) {
-    uint32_t off = 0;
-    for (int s2 = 0; s2 < segs; ++s2) {
-      sh.seg_off[s2] = off;
-      off += min((uint32_t)k, cnt_in[(size_t)b * segs + s2]);
-    }
-    sh.seg_off[segs] = off;
+  const int slots = 2 * k;  // per segment
+  if (tid < segs) seg_cnt[tid] = min((uint32_t)slots, cnt_in[(size_t)b * segs + tid]);
+  for (int i = tid; i < kBins; i += kMergeThreads) {
+    sc.hist[0][i] = 0;
+    sc.hist[1][i] = 0;
   }
   lds_barrier();
-  const int total = (int)sh.seg_off[segs];
-  for (int s2 = 0; s2 < segs; ++s2) {
-    const int o = (int)sh.seg_off[s2];
-    const int c = (int)sh.seg_off[s2 + 1] - o;
-    const uint64_t* src = cand_in + ((size_t)b * segs + s2) * (size_t)k;
-    for (int i = tid; i < c; i += kMergeThreads) buf[o + i] = src[i];
-  }
-  lds_barrier();
-  uint64_t thr = 0;
-  if (total > k) thr = block_select_kth<kMergeThreads>(buf, total, k, BF16 ? 2 : 4, pos_bits, sh.sc);
-
-  // Winners in buffer order: thread t owns a contiguous run of entries.
-  constexpr int kPer = kMergeCap / kMergeThreads;
-  const int per = (total + kMergeThreads - 1) / kMergeThreads;
-  const int lo = min(total, tid * per);
-  const int hi = min(total, lo + per);
-  uint32_t keep = 0;
+  // Every slot of the row at once: slot q = tid + j*512 is entry q % slots
+  // of segment q / slots, valid below that segment's count.
+  const uint64_t* src = cand_in + (size_t)b * segs * slots;
+  // All loads are issued unconditionally (clamped into the row's slots, which
+  // lie inside the workspace) so they overlap; validity is applied after.
   uint64_t v[kPer];
+  uint32_t nvalid = 0;
+  const int nslots = segs * slots;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = src[min(tid + j * kMergeThreads, nslots - 1)];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int i = lo + j;
-    v[j] = (i < hi) ? buf[i] : 0;
-    keep += (i < hi && v[j] >= thr) ? 1u : 0u;
+    const int q = tid + j * kMergeThreads;
+    const int s = q / slots;
+    const bool ok = q < nslots && (uint32_t)(q - s * slots) < seg_cnt[min(s, segs - 1)];
+    v[j] = ok ? v[j] : 0;
+    nvalid += ok ? 1u : 0u;
   }
+  uint32_t total = wave_reduce<OpAdd>(nvalid);
+  {
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    if (lane == 0) sc.wsum[wave] = total;
+    lds_barrier();
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kMergeThreads / kWave; ++w) total += sc.wsum[w];
+    lds_barrier();  // wsum is reused below
+  }
+  uint64_t thr = 0;
+  if ((int)total > k) thr = select_exact_regs<kMergeThreads, kPer>(v, k, sc);
+  // Winners in (thread, slot) order.
+  uint32_t keep = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) keep += (v[j] && v[j] >= thr) ? 1u : 0u;
   uint32_t nkeep;
-  uint32_t pos = block_exclusive_scan<kMergeThreads>(keep, &nkeep, sh.sc);
+  uint32_t pos = block_exclusive_scan<kMergeThreads>(keep, &nkeep, sc);
   int32_t* oi = out_idx + (size_t)b * k;
   const size_t esz = BF16 ? 2 : 4;
   const char* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;
   if (!sorted_index) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int i = lo + j;
-      if (i < hi && v[j] >= thr && pos < (uint32_t)k) {
+      if (v[j] && v[j] >= thr && pos < (uint32_t)k) {
         const uint32_t p = min(composite_pos(v[j]), (uint32_t)(N - 1));
         oi[pos] = (int32_t)p;
         if (out_val) {
@@ -420,18 +682,13 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     }
     return;
   }
-  // Sorted by index: place the winners' positions in LDS (reusing the front
-  // of the buffer as 32-bit slots after everyone has read it), pad to a power
-  // of two and run a bitonic sort.
-  lds_barrier();
-  uint32_t* pos_lds = reinterpret_cast<uint32_t*>(buf);
+  // Sorted by index: the winners' positions go to LDS, padded to a power of
+  // two, then a bitonic sort.
   int P = 1;
   while (P < k) P <<= 1;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = lo + j;
-    if (i < hi && v[j] >= thr && pos < (uint32_t)k) pos_lds[pos++] = min(composite_pos(v[j]), (uint32_t)(N - 1));
-  }
+  for (int j = 0; j < kPer; ++j)
+    if (v[j] && v[j] >= thr && pos < (uint32_t)k) pos_lds[pos++] = min(composite_pos(v[j]), (uint32_t)(N - 1));
   for (int i = k + tid; i < P; i += kMergeThreads) pos_lds[i] = 0xFFFFFFFFu;
   lds_barrier();
   for (int size = 2; size <= P; size <<= 1) {
@@ -461,37 +718,63 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+template <typename K>
+hipError_t allow_lds(K kernel, size_t bytes) {
+  // These workgroups use more than 64 KB of LDS (gfx950 has 160 KB per CU).
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <bool BF16, bool AL, int V>
+hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p,
+                      uint64_t* cand, uint32_t* cnt, hipStream_t st) {
+  const size_t lds = (size_t)kSegCap * sizeof(uint64_t);
+  hipError_t e = allow_lds(topk_segment_kernel<BF16, AL, V>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((topk_segment_kernel<BF16, AL, V>), dim3(p.segs, B), dim3(kTkThreads), lds,
+                     st, scores, N, k, p.seg_len, p.segs, cand, cnt);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool AL>
+hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan& p,
+                        uint64_t* cand, uint32_t* cnt, hipStream_t st) {
+  switch (p.vec) {
+    case 1: return launch_seg<BF16, AL, 1>(scores, B, N, k, p, cand, cnt, st);
+    case 2: return launch_seg<BF16, AL, 2>(scores, B, N, k, p, cand, cnt, st);
+    case 4: return launch_seg<BF16, AL, 4>(scores, B, N, k, p, cand, cnt, st);
+    default: return launch_seg<BF16, AL, 8>(scores, B, N, k, p, cand, cnt, st);
+  }
+}
+
 }  // namespace
 
 TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
-  (void)dt;
   TopkPlan p{};
-  // Aim for about two workgroups per CU over the whole call, but keep each
-  // row's candidates (segs * k) within the merge buffer.
-  long long want = (512 + B - 1) / B;
-  const long long max_by_len = (N + kTkSub - 1) / kTkSub;
-  const long long max_by_merge = kMergeCap / k;
-  long long segs = want;
+  const int E = dt == DSA_BF16 ? 8 : 4;
+  const long long chunk = (long long)kTkThreads * E;  // one vector per thread
+  // About one workgroup per CU over the call; each row's candidates
+  // (segs * 2k) must fit the merge buffer.
+  long long segs = (256 + B - 1) / B;
+  const long long max_by_len = (N + 16383) / 16384;  // at least 16K scores per segment
+  const long long max_by_merge = kMergeCap / (2LL * k);
   if (segs > max_by_len) segs = max_by_len;
   if (segs > max_by_merge) segs = max_by_merge;
   if (segs > 64) segs = 64;
   if (segs < 1) segs = 1;
   long long seg_len = (N + segs - 1) / segs;
-  seg_len = (seg_len + kTkSub - 1) / kTkSub * kTkSub;
+  seg_len = (seg_len + chunk - 1) / chunk * chunk;
   segs = (N + seg_len - 1) / seg_len;
+  const long long vec = seg_len / chunk;  // vectors per thread over the segment
+  int v = 1;
+  while (v < vec && v < kTkMaxVec) v <<= 1;
+  p.vec = v;
   p.segs = (int)segs;
   p.seg_len = (int)seg_len;
   p.cand_off = 0;
-  p.cnt_off = align_up((size_t)B * p.segs * (size_t)k * sizeof(uint64_t), 256);
+  p.cnt_off = align_up((size_t)B * p.segs * (size_t)(2 * k) * sizeof(uint64_t), 256);
   p.bytes = align_up(p.cnt_off + (size_t)B * p.segs * sizeof(uint32_t), 256);
   return p;
-}
-
-template <typename K>
-hipError_t allow_lds(K kernel, size_t bytes) {
-  // Workgroups here use more than 64 KB of LDS (gfx950 has 160 KB per CU).
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
@@ -500,38 +783,34 @@ hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
   uint64_t* cand = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + plan.cand_off);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + plan.cnt_off);
   const bool bf16 = dt == DSA_BF16;
-  const int vec = bf16 ? 8 : 4;
-  const bool aligned = (N % vec) == 0 && (reinterpret_cast<uintptr_t>(scores) % 16) == 0;
-  int pos_bits = 1;
-  while (pos_bits < 32 && ((uint32_t)(N - 1) >> pos_bits) != 0) ++pos_bits;
-  const size_t seg_lds = (size_t)kSegCap * sizeof(uint64_t);
-  const size_t merge_lds = (size_t)kMergeCap * sizeof(uint64_t);
-  dim3 g1(plan.segs, B);
-  hipError_t e = hipSuccess;
-#define DSA_SEG(BF, AL)                                                                        \
-  do {                                                                                         \
-    e = allow_lds(topk_segment_kernel<BF, AL>, seg_lds);                                       \
-    if (e != hipSuccess) return e;                                                             \
-    hipLaunchKernelGGL((topk_segment_kernel<BF, AL>), g1, dim3(kTkThreads), seg_lds, st, scores, \
-                       N, k, plan.seg_len, plan.segs, pos_bits, cand, cnt);                    \
+  const int E = bf16 ? 8 : 4;
+  const bool aligned = (N % E) == 0 && (reinterpret_cast<uintptr_t>(scores) % 16) == 0;
+  hipError_t e;
+  if (bf16) e = aligned ? launch_seg_v<true, true>(scores, B, N, k, plan, cand, cnt, st)
+                        : launch_seg_v<true, false>(scores, B, N, k, plan, cand, cnt, st);
+  else e = aligned ? launch_seg_v<false, true>(scores, B, N, k, plan, cand, cnt, st)
+                   : launch_seg_v<false, false>(scores, B, N, k, plan, cand, cnt, st);
+  if (e != hipSuccess) return e;
+  int P = 1;
+  while (P < k) P <<= 1;
+  const size_t merge_lds = (size_t)P * sizeof(uint32_t);
+  const int slots = plan.segs * 2 * k;
+  const int per = slots <= 512 * 4 ? 4 : slots <= 512 * 8 ? 8 : slots <= 512 * 16 ? 16 : 32;
+#define DSA_MERGE(BF, PER)                                                                      \
+  do {                                                                                          \
+    e = allow_lds(topk_merge_kernel<BF, PER>, merge_lds);                                       \
+    if (e != hipSuccess) return e;                                                              \
+    hipLaunchKernelGGL((topk_merge_kernel<BF, PER>), dim3(B), dim3(kMergeThreads), merge_lds, st, \
+                       scores, N, k, plan.segs, cand, cnt, out_idx, out_val, sorted_index);     \
   } while (0)
   if (bf16) {
-    if (aligned) DSA_SEG(true, true); else DSA_SEG(true, false);
+    if (per == 4) DSA_MERGE(true, 4); else if (per == 8) DSA_MERGE(true, 8);
+    else if (per == 16) DSA_MERGE(true, 16); else DSA_MERGE(true, 32);
   } else {
-    if (aligned) DSA_SEG(false, true); else DSA_SEG(false, false);
+    if (per == 4) DSA_MERGE(false, 4); else if (per == 8) DSA_MERGE(false, 8);
+    else if (per == 16) DSA_MERGE(false, 16); else DSA_MERGE(false, 32);
   }
-#undef DSA_SEG
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (bf16) {
-    e = allow_lds(topk_merge_kernel<true>, merge_lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((topk_merge_kernel<true>), dim3(B), dim3(kMergeThreads), merge_lds, st, scores, N, k, plan.segs, pos_bits, cand, cnt, out_idx, out_val, sorted_index);
-  } else {
-    e = allow_lds(topk_merge_kernel<false>, merge_lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((topk_merge_kernel<false>), dim3(B), dim3(kMergeThreads), merge_lds, st, scores, N, k, plan.segs, pos_bits, cand, cnt, out_idx, out_val, sorted_index);
-  }
+#undef DSA_MERGE
   return hipGetLastError();
 }
 

@@ -27,10 +27,23 @@
 namespace dsa {
 namespace {
 
-constexpr int kTile = 32;  // rows per LDS tile
+constexpr int kTile = 32;          // rows per LDS tile
+constexpr int kMaxSplitTiles = 64; // rows per split <= 2048
+constexpr float kRescale = 8.0f;   // lazy-rescale margin (natural log units)
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_byte + 16*l (M0 holds the wave-uniform LDS byte address). It
+// is issued from inline assembly so that the compiler, which cannot tell
+// these LDS writes apart from later LDS reads, does not wait for every
+// outstanding copy before each read; the kernel waits with explicit vmcnt
+// values instead. No register is written asynchronously.
+__device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_byte) : "memory", "m0");
 }
 
 template <int D, int WAVES>
@@ -38,18 +51,32 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int N, int k, int W, int Hq, float scale, int rows_per_split, int splits) {
+    int N, int k, int W, int Hq, float scale, int rows_per_split, int splits, int npairs,
+    int hgroups) {
   constexpr int THREADS = WAVES * kWave;
   constexpr int HW = WAVES * 16;
   constexpr int KSTEPS = D / 32;
   constexpr int DT = D / 16;
   constexpr int ROW_WORDS = D / 2 + 4;  // 16 bytes of padding per row
   constexpr int CHUNKS = D / 8;         // 16-byte chunks per row
-  __shared__ uint32_t R[kTile * ROW_WORDS];
+  constexpr int CH = kTile * CHUNKS / THREADS;  // staged chunks per thread per tile
+  static_assert(CH * THREADS == kTile * CHUNKS, "tile must split evenly over the threads");
+  extern __shared__ uint32_t lds[];
+  constexpr int kStagesDev = (D == 512 && WAVES >= 2) ? 4 : 2;
+  uint32_t* Rbuf = lds;                                     // kStagesDev tiles
+  int32_t* srow = reinterpret_cast<int32_t*>(lds + kStagesDev * kTile * ROW_WORDS);  // rows of this split
 
-  const int split = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+  // Workgroup -> (batch, split, head group). Workgroups are dispatched to
+  // the 8 XCDs round robin, so the head groups of one (batch, split) pair
+  // get ids 8 apart: they land on one XCD and share the gathered rows in
+  // its L2.
+  const int L = blockIdx.x;
+  const int per8 = 8 * hgroups;
+  const int pair = (L / per8) * 8 + (L % 8);
+  const int hg = (L % per8) / 8;
+  if (pair >= npairs) return;  // padding workgroup (uniform)
+  const int b = pair / splits;
+  const int split = pair % splits;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -60,11 +87,29 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
   const int r0 = split * rows_per_split;
   const int r1 = min(rows, r0 + rows_per_split);
 
+  // The split's source rows: >= 0 a compressed row, < 0 window row -(v+1).
+  const int32_t* irow = idx + (size_t)b * k;
+  for (int r = r0 + tid; r < r1; r += THREADS) {
+    int v;
+    if (r < k) {
+      v = irow[r];
+      v = v < 0 ? 0 : (v >= N ? N - 1 : v);  // out-of-range indices are clamped
+    } else {
+      v = -(r - k) - 1;
+    }
+    srow[r - r0] = v;
+  }
+
   // Query fragments (B operand of S^T): head h, dims 32*kk + 8g .. +8.
   bf16x8 qf[KSTEPS];
   const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g * 8);
+  // Settle the query loads here: otherwise the compiler places their waits
+  // inside the tile loop, where they would also wait for the row copies in
+  // flight.
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" : "+v"(qf[kk]));
 
   f32x4 o[DT];
 #pragma unroll
@@ -72,31 +117,82 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
   float mrun = -INFINITY;  // running max of the scaled logits of head h
   float lrun = 0.0f;       // this lane's share of the running sum
 
-  const int32_t* irow = idx + (size_t)b * k;
   const uint16_t* kvb = kv + (size_t)b * N * D;
   const uint16_t* winb = win ? win + (size_t)b * W * D : nullptr;
+  lds_barrier();  // srow visible
 
-  for (int t0 = r0; t0 < r1; t0 += kTile) {
-    lds_barrier();  // the previous tile's reads are done
-    for (int c = tid; c < kTile * CHUNKS; c += THREADS) {
-      const int rr = c / CHUNKS;
-      const int ch = c % CHUNKS;
+  // Two ways to stage rows into the LDS tiles. For D = 512 a row is 1 KB,
+  // exactly one wave-wide 16-byte-per-lane load, so each wave DMAs its rows
+  // straight into LDS (global_load_lds) and kStages tiles are in flight; the
+  // waits are explicit vmcnt values. Rows past r1 repeat the last valid row
+  // (finite data; their weights are zero). For D = 128 four rows share one
+  // wave load, which the padded row layout cannot take, so rows go through
+  // registers with one tile of prefetch.
+  constexpr bool kDma = (D == 512 && WAVES >= 2);
+  constexpr int kStages = kDma ? 4 : 2;
+  const int ntiles = (r1 - r0 + kTile - 1) / kTile;
+  u32x4 stage[kDma ? 1 : CH];
+  auto fetch = [&](int t0) {  // register path: rows of tile t0 (zeros past r1)
+#pragma unroll
+    for (int c = 0; c < (kDma ? 1 : CH); ++c) {
+      const int ci = tid + c * THREADS;
+      const int rr = ci / CHUNKS;
+      const int ch = ci % CHUNKS;
       const int r = t0 + rr;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      stage[c] = u32x4{0u, 0u, 0u, 0u};
       if (r < r1) {
-        const uint16_t* src;
-        if (r < k) {
-          int j = irow[r];
-          j = j < 0 ? 0 : (j >= N ? N - 1 : j);
-          src = kvb + (size_t)j * D;
-        } else {
-          src = winb + (size_t)(r - k) * D;
-        }
-        v = *reinterpret_cast<const u32x4*>(src + ch * 8);
+        const int v = srow[r - r0];
+        const uint16_t* src = v >= 0 ? kvb + (size_t)v * D : winb + (size_t)(-v - 1) * D;
+        stage[c] = *reinterpret_cast<const u32x4*>(src + ch * 8);
       }
-      *reinterpret_cast<u32x4*>(&R[rr * ROW_WORDS + ch * 4]) = v;
     }
-    lds_barrier();
+  };
+  constexpr int kRowsPerWave = kTile / WAVES;
+  auto dma = [&](int tile, int slot) {  // DMA path: this wave's rows of a tile
+    uint32_t* dst = Rbuf + slot * kTile * ROW_WORDS;
+    const int t0 = r0 + tile * kTile;
+    int vr[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) vr[i] = srow[min(t0 + wave * kRowsPerWave + i, r1 - 1) - r0];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int rr = wave * kRowsPerWave + i;
+      const int v = __builtin_amdgcn_readfirstlane(vr[i]);
+      const uint16_t* src = (v >= 0 ? kvb + (size_t)v * D : winb + (size_t)(-v - 1) * D) + lane * 8;
+      const uint32_t lds_byte = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)(dst + rr * ROW_WORDS);
+      dma_row16(src, __builtin_amdgcn_readfirstlane(lds_byte));
+    }
+  };
+  if (kDma) {
+    for (int j = 0; j < kStages - 1 && j < ntiles; ++j) dma(j, j);
+  } else {
+    fetch(r0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = r0 + t * kTile;
+    uint32_t* R = Rbuf + (t % kStages) * kTile * ROW_WORDS;
+    if (kDma) {
+      // Tile t has landed once at most (later tiles issued) * rows-per-wave
+      // of this wave's DMA loads are still outstanding.
+      const int later = min(kStages - 2, ntiles - 1 - t);
+      if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRowsPerWave) : "memory");
+      else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRowsPerWave) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      // The slot of tile t+kStages-1 was last read by tile t-1, which every
+      // wave has finished at the barrier above.
+      if (t + kStages - 1 < ntiles) dma(t + kStages - 1, (t + kStages - 1) % kStages);
+    } else {
+      // This buffer was last read two tiles ago; the barrier of the previous
+      // iteration has seen every wave finish that tile.
+#pragma unroll
+      for (int c = 0; c < (kDma ? 1 : CH); ++c) {
+        const int ci = tid + c * THREADS;
+        *reinterpret_cast<u32x4*>(&R[(ci / CHUNKS) * ROW_WORDS + (ci % CHUNKS) * 4]) = stage[c];
+      }
+      lds_barrier();
+      if (t0 + kTile < r1) fetch(t0 + kTile);  // in flight while this tile is computed
+    }
 
     // S^T for rows 0..15 and 16..31 of the tile.
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -119,28 +215,36 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
-    const float alpha = __expf(mrun - mnew);
-    mrun = mnew;
+    // Lazy rescaling: the weights are taken relative to a reference mrun that
+    // only moves when a tile's maximum exceeds it by more than kRescale, so
+    // the weights stay below e^kRescale and the accumulators are rescaled
+    // (for the whole wave at once) on few tiles only. The first tile always
+    // sets the reference (mrun starts at -inf).
+    if (__ballot(mx > mrun + kRescale) != 0) {
+      const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
+      const float alpha = __expf(mrun - mnew);
+      mrun = mnew;
+      lrun *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt][0] *= alpha;
+        o[dt][1] *= alpha;
+        o[dt][2] *= alpha;
+        o[dt][3] *= alpha;
+      }
+    }
     u32x4 pw;
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t b0 = f32_to_bf16_bits(__expf(z[2 * i] - mnew));
-      const uint32_t b1 = f32_to_bf16_bits(__expf(z[2 * i + 1] - mnew));
+      const uint32_t b0 = f32_to_bf16_bits(__expf(z[2 * i] - mrun));
+      const uint32_t b1 = f32_to_bf16_bits(__expf(z[2 * i + 1] - mrun));
       // the sum uses the rounded weights the MFMA sees
       psum += bf16_bits_to_f32((uint16_t)b0) + bf16_bits_to_f32((uint16_t)b1);
       pw[i] = b0 | (b1 << 16);
     }
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-    lrun = lrun * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      o[dt][0] *= alpha;
-      o[dt][1] *= alpha;
-      o[dt][2] *= alpha;
-      o[dt][3] *= alpha;
-    }
+    lrun += psum;
 
     // O^T += R^T P^T. Within each 16-lane group, lane j points at row
     // (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4) .. +4; the
@@ -220,13 +324,24 @@ __global__ __launch_bounds__(D / 4) void attend_combine_kernel(
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 template <int D, int WAVES>
-void launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                     const uint16_t* win, uint16_t* out, float* po, float2* pml,
-                     const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
-  dim3 grid(p.splits, d.q_heads / (16 * WAVES), d.batch);
-  hipLaunchKernelGGL((sparse_attend_kernel<D, WAVES>), grid, dim3(WAVES * kWave), 0, st, q, kv,
-                     idx, win, out, po, pml, d.n, d.topk, d.window, d.q_heads, d.scale,
-                     p.rows_per_split, p.splits);
+hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                           const uint16_t* win, uint16_t* out, float* po, float2* pml,
+                           const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
+  constexpr int ROW_WORDS = D / 2 + 4;
+  constexpr int kStagesHost = (D == 512 && WAVES >= 2) ? 4 : 2;
+  const size_t lds = (size_t)kStagesHost * kTile * ROW_WORDS * sizeof(uint32_t) +
+                     (size_t)p.rows_per_split * sizeof(int32_t);
+  auto kern = sparse_attend_kernel<D, WAVES>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int hgroups = d.q_heads / (16 * WAVES);
+  const int npairs = d.batch * p.splits;
+  const int grid = (npairs + 7) / 8 * 8 * hgroups;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
+                     pml, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split, p.splits,
+                     npairs, hgroups);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -241,7 +356,8 @@ AttendPlan plan_attend(const dsa_dims_t& d) {
   long long want = (256 + (long long)d.batch * hgroups - 1) / ((long long)d.batch * hgroups);
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
-  const int tiles_per_split = (tiles + (int)want - 1) / (int)want;
+  int tiles_per_split = (tiles + (int)want - 1) / (int)want;
+  if (tiles_per_split > kMaxSplitTiles) tiles_per_split = kMaxSplitTiles;  // bounds the row list in LDS
   p.rows_per_split = tiles_per_split * kTile;
   p.splits = (rows + p.rows_per_split - 1) / p.rows_per_split;
   if (p.splits > 1) {
@@ -261,16 +377,16 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
   float* po = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
   float2* pml = p.splits > 1 ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const int waves = p.heads_per_wg / 16;
+  hipError_t e;
   if (d.head_dim == 512) {
-    if (waves == 4) launch_attend_t<512, 4>(q, kv, idx, win, out, po, pml, d, p, st);
-    else if (waves == 2) launch_attend_t<512, 2>(q, kv, idx, win, out, po, pml, d, p, st);
-    else launch_attend_t<512, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    if (waves == 4) e = launch_attend_t<512, 4>(q, kv, idx, win, out, po, pml, d, p, st);
+    else if (waves == 2) e = launch_attend_t<512, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    else e = launch_attend_t<512, 1>(q, kv, idx, win, out, po, pml, d, p, st);
   } else {
-    if (waves == 4) launch_attend_t<128, 4>(q, kv, idx, win, out, po, pml, d, p, st);
-    else if (waves == 2) launch_attend_t<128, 2>(q, kv, idx, win, out, po, pml, d, p, st);
-    else launch_attend_t<128, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    if (waves == 4) e = launch_attend_t<128, 4>(q, kv, idx, win, out, po, pml, d, p, st);
+    else if (waves == 2) e = launch_attend_t<128, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    else e = launch_attend_t<128, 1>(q, kv, idx, win, out, po, pml, d, p, st);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int Hq = d.q_heads;
   if (d.head_dim == 512)

@@ -65,21 +65,20 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
   const int start = blockIdx.x * keys_per_wg;
   const int end = min(N, start + keys_per_wg);
 
-  for (int key0 = start + wave * kIsKeysPerStep; key0 < end; key0 += kIsKeysPerRound) {
-    bf16x8 kb[kIsTiles][4];
+  // Key fragments of one wave step: lane 16g+m holds key (key0 + 16t + m),
+  // channels 32*kk + 8g .. +8. Keys past N are clamped to N-1 (their columns
+  // are computed and never stored), so every load is unconditional.
+  auto load_keys = [&](bf16x8 (&kb)[kIsTiles][4], int key0) {
 #pragma unroll
     for (int t = 0; t < kIsTiles; ++t) {
-      const int key = key0 + t * 16 + m;
+      const int key = min(key0 + t * 16 + m, N - 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (key < N) {
-          kb[t][kk] = __builtin_nontemporal_load(
-              reinterpret_cast<const bf16x8*>(krow + (size_t)key * kDI + kk * 32 + g * 8));
-        } else {
-          kb[t][kk] = bf16x8{};
-        }
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        kb[t][kk] = __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x8*>(krow + (size_t)key * kDI + kk * 32 + g * 8));
     }
+  };
+  auto score_step = [&](const bf16x8 (&kb)[kIsTiles][4], int key0) {
     f32x4 acc[kIsTiles][MT];
 #pragma unroll
     for (int t = 0; t < kIsTiles; ++t)
@@ -113,6 +112,32 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
     if (g < 2) {
       const int key = key0 + g * 16 + m;
       if (key < N) srow[key] = mine;
+    }
+  };
+
+  // Two key buffers in turn: the loads of the next step are in flight while
+  // this step is computed. Each load sits on a path where the compiler can
+  // see exactly which loads are outstanding, so a step waits only for its
+  // own buffer.
+  bf16x8 ka[kIsTiles][4], kb[kIsTiles][4];
+  int key0 = start + wave * kIsKeysPerStep;
+  if (key0 < end) {
+    load_keys(ka, key0);
+    while (true) {
+      if (key0 + kIsKeysPerRound >= end) {
+        score_step(ka, key0);
+        break;
+      }
+      load_keys(kb, key0 + kIsKeysPerRound);
+      score_step(ka, key0);
+      key0 += kIsKeysPerRound;
+      if (key0 + kIsKeysPerRound >= end) {
+        score_step(kb, key0);
+        break;
+      }
+      load_keys(ka, key0 + kIsKeysPerRound);
+      score_step(kb, key0);
+      key0 += kIsKeysPerRound;
     }
   }
 }

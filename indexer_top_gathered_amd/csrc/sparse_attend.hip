@@ -46,25 +46,30 @@ __device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
                :: "v"(g), "s"(lds_byte) : "memory", "m0");
 }
 
-template <int D, int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
+template <int D, int HG, int DSPLIT>
+__global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
     int N, int k, int W, int Hq, float scale, int rows_per_split, int splits, int npairs,
     int hgroups) {
+  constexpr int WAVES = HG * DSPLIT;
   constexpr int THREADS = WAVES * kWave;
-  constexpr int HW = WAVES * 16;
-  constexpr int KSTEPS = D / 32;
-  constexpr int DT = D / 16;
+  constexpr int HW = HG * 16;           // query heads per workgroup
+  constexpr int DW = D / DSPLIT;        // dims of q and O owned by one wave
+  constexpr int KS = DW / 32;           // S^T k-steps per wave
+  constexpr int DTW = DW / 16;          // 16-dim output tiles per wave
   constexpr int ROW_WORDS = D / 2 + 4;  // 16 bytes of padding per row
   constexpr int CHUNKS = D / 8;         // 16-byte chunks per row
   constexpr int CH = kTile * CHUNKS / THREADS;  // staged chunks per thread per tile
   static_assert(CH * THREADS == kTile * CHUNKS, "tile must split evenly over the threads");
+  constexpr bool kDma = (D == 512 && WAVES >= 2);
+  constexpr int kStages = kDma ? 4 : 2;
+  constexpr int XWORDS = DSPLIT > 1 ? WAVES * kWave * 8 : 0;  // S^T exchange, 8 floats per lane
   extern __shared__ uint32_t lds[];
-  constexpr int kStagesDev = (D == 512 && WAVES >= 2) ? 4 : 2;
-  uint32_t* Rbuf = lds;                                     // kStagesDev tiles
-  int32_t* srow = reinterpret_cast<int32_t*>(lds + kStagesDev * kTile * ROW_WORDS);  // rows of this split
+  uint32_t* Rbuf = lds;  // kStages tiles
+  f32x4* xbuf = reinterpret_cast<f32x4*>(lds + kStages * kTile * ROW_WORDS);
+  int32_t* srow = reinterpret_cast<int32_t*>(lds + kStages * kTile * ROW_WORDS + XWORDS);
 
   // Workgroup -> (batch, split, head group). Workgroups are dispatched to
   // the 8 XCDs round robin, so the head groups of one (batch, split) pair
@@ -82,10 +87,22 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
   const int wave = tid / kWave;
   const int m = lane & 15;
   const int g = lane >> 4;
-  const int h = hg * HW + wave * 16 + m;  // the head this lane owns
+  // Wave (hq, dh): 16 heads, and the dh-th 1/DSPLIT of the dims for the
+  // query fragments and the output accumulators.
+  const int hq = wave % HG;
+  const int dh = wave / HG;
+  const int h = hg * HW + hq * 16 + m;  // the head this lane owns
+  const int dbase = dh * DW;
   const int rows = k + W;
   const int r0 = split * rows_per_split;
   const int r1 = min(rows, r0 + rows_per_split);
+
+  // Query fragments (B operand of S^T): head h, dims dbase + 32*kk + 8g .. +8.
+  // Issued first so that their latency overlaps the index loads below.
+  bf16x8 qf[KS];
+  const uint16_t* qrow = q + ((size_t)b * Hq + h) * D + dbase;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g * 8);
 
   // The split's source rows: >= 0 a compressed row, < 0 window row -(v+1).
   const int32_t* irow = idx + (size_t)b * k;
@@ -99,21 +116,15 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
     }
     srow[r - r0] = v;
   }
-
-  // Query fragments (B operand of S^T): head h, dims 32*kk + 8g .. +8.
-  bf16x8 qf[KSTEPS];
-  const uint16_t* qrow = q + ((size_t)b * Hq + h) * D;
-#pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g * 8);
   // Settle the query loads here: otherwise the compiler places their waits
   // inside the tile loop, where they would also wait for the row copies in
   // flight.
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" : "+v"(qf[kk]));
+  for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
 
-  f32x4 o[DT];
+  f32x4 o[DTW];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < DTW; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY;  // running max of the scaled logits of head h
   float lrun = 0.0f;       // this lane's share of the running sum
 
@@ -128,8 +139,6 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
   // (finite data; their weights are zero). For D = 128 four rows share one
   // wave load, which the padded row layout cannot take, so rows go through
   // registers with one tile of prefetch.
-  constexpr bool kDma = (D == 512 && WAVES >= 2);
-  constexpr int kStages = kDma ? 4 : 2;
   const int ntiles = (r1 - r0 + kTile - 1) / kTile;
   u32x4 stage[kDma ? 1 : CH];
   auto fetch = [&](int t0) {  // register path: rows of tile t0 (zeros past r1)
@@ -194,14 +203,28 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
       if (t0 + kTile < r1) fetch(t0 + kTile);  // in flight while this tile is computed
     }
 
-    // S^T for rows 0..15 and 16..31 of the tile.
+    // S^T for rows 0..15 and 16..31 of the tile, over this wave's dims.
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&R[m * ROW_WORDS + kk * 16 + g * 4]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&R[(16 + m) * ROW_WORDS + kk * 16 + g * 4]);
+    for (int kk = 0; kk < KS; ++kk) {
+      const int w0 = (dbase >> 1) + kk * 16 + g * 4;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&R[m * ROW_WORDS + w0]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&R[(16 + m) * ROW_WORDS + w0]);
       s0 = mfma16x16x32(a0, qf[kk], s0);
       s1 = mfma16x16x32(a1, qf[kk], s1);
+    }
+    if (DSPLIT > 1) {
+      // The two waves of a head group each hold half of the dot products;
+      // each adds the other's half. Both form the same sums (addition is
+      // commutative), so they run identical softmax states. The previous
+      // tile's reads of this buffer finished before the barrier at the top
+      // of this tile.
+      xbuf[(wave * 2 + 0) * kWave + lane] = s0;
+      xbuf[(wave * 2 + 1) * kWave + lane] = s1;
+      lds_barrier();
+      const int partner = (DSPLIT - 1 - dh) * HG + hq;
+      s0 += xbuf[(partner * 2 + 0) * kWave + lane];
+      s1 += xbuf[(partner * 2 + 1) * kWave + lane];
     }
     // Lane (m, g): s0[i] is row 4g+i, s1[i] is row 16+4g+i, head m.
     float z[8];
@@ -226,7 +249,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
       mrun = mnew;
       lrun *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+      for (int dt = 0; dt < DTW; ++dt) {
         o[dt][0] *= alpha;
         o[dt][1] *= alpha;
         o[dt][2] *= alpha;
@@ -237,23 +260,22 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t b0 = f32_to_bf16_bits(__expf(z[2 * i] - mrun));
-      const uint32_t b1 = f32_to_bf16_bits(__expf(z[2 * i + 1] - mrun));
+      const uint32_t pk = pack_bf16x2(__expf(z[2 * i] - mrun), __expf(z[2 * i + 1] - mrun));
       // the sum uses the rounded weights the MFMA sees
-      psum += bf16_bits_to_f32((uint16_t)b0) + bf16_bits_to_f32((uint16_t)b1);
-      pw[i] = b0 | (b1 << 16);
+      psum += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xFFFF0000u);
+      pw[i] = pk;
     }
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
     lrun += psum;
 
-    // O^T += R^T P^T. Within each 16-lane group, lane j points at row
-    // (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4) .. +4; the
-    // transposing read hands lane j the 4 rows at dim 16*dt + j.
+    // O^T += R^T P^T over this wave's dims. Within each 16-lane group, lane
+    // j points at row (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4)
+    // .. +4; the transposing read hands lane j the 4 rows at dim 16*dt + j.
     const int ra = 4 * g + (m >> 2);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DTW; ++dt) {
       typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-      const int col = dt * 8 + 2 * (m & 3);
+      const int col = (dbase >> 1) + dt * 8 + 2 * (m & 3);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4*)(&R[ra * ROW_WORDS + col]));
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -268,74 +290,94 @@ __global__ __launch_bounds__(WAVES * kWave) void sparse_attend_kernel(
   // Full sum over the four lane groups that share head m.
   float l = lrun + __shfl_xor(lrun, 16);
   l += __shfl_xor(l, 32);
-  // Lane (m, g) holds O[h][16*dt + 4g + i].
+  // Lane (m, g) holds O[h][dbase + 16*dt + 4g + i].
   if (splits == 1) {
     const float inv = 1.0f / l;
-    uint16_t* orow = out + ((size_t)b * Hq + h) * D;
+    uint16_t* orow = out + ((size_t)b * Hq + h) * D + dbase;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t lo = (uint32_t)f32_to_bf16_bits(o[dt][0] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(o[dt][1] * inv) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16_bits(o[dt][2] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(o[dt][3] * inv) << 16);
+    for (int dt = 0; dt < DTW; ++dt) {
+      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+      const uint32_t hi = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
       *reinterpret_cast<uint2*>(orow + dt * 16 + g * 4) = make_uint2(lo, hi);
     }
   } else {
     const size_t slot = ((size_t)b * splits + split) * Hq + h;
-    float* po = part_o + slot * D;
+    float* po = part_o + slot * D + dbase;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DTW; ++dt)
       *reinterpret_cast<float4*>(po + dt * 16 + g * 4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (g == 0) part_ml[slot] = make_float2(mrun, l);
+    if (dh == 0 && g == 0) part_ml[slot] = make_float2(mrun, l);
   }
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (batch, head),
-// each thread owns 4 dims.
+// each thread owns 4 dims. Splits are taken 8 at a time with every load of
+// a chunk issued before any is used (indices past the last split are
+// clamped and weighted zero), so a chunk costs one memory latency.
 template <int D>
 __global__ __launch_bounds__(D / 4) void attend_combine_kernel(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     uint16_t* __restrict__ out, int Hq, int splits) {
+  constexpr int SC = 8;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int h = bh % Hq;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((size_t)b * splits + s) * Hq + h].x);
-  float L = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const int d = threadIdx.x * 4;
-  for (int s = 0; s < splits; ++s) {
-    const size_t slot = ((size_t)b * splits + s) * Hq + h;
-    const float2 ml = part_ml[slot];
-    const float f = __expf(ml.x - M);
-    L += ml.y * f;
-    const float4 v = *reinterpret_cast<const float4*>(part_o + slot * D + d);
-    acc.x += v.x * f;
-    acc.y += v.y * f;
-    acc.z += v.z * f;
-    acc.w += v.w * f;
+  const size_t base = (size_t)b * splits * Hq + h;  // slot of split 0
+  float M = -INFINITY, L = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < splits; s0 += SC) {
+    float2 ml[SC];
+    float4 v[SC];
+#pragma unroll
+    for (int j = 0; j < SC; ++j) {
+      const size_t slot = base + (size_t)min(s0 + j, splits - 1) * Hq;
+      ml[j] = part_ml[slot];
+      v[j] = *reinterpret_cast<const float4*>(part_o + slot * D + d);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int j = 0; j < SC; ++j) Mc = fmaxf(Mc, ml[j].x);
+    const float r = __expf(M - Mc);  // 0 on the first chunk (M = -inf)
+    L *= r;
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+#pragma unroll
+    for (int j = 0; j < SC; ++j) {
+      const float f = (s0 + j < splits) ? __expf(ml[j].x - Mc) : 0.0f;
+      L += ml[j].y * f;
+      acc.x += v[j].x * f;
+      acc.y += v[j].y * f;
+      acc.z += v[j].z * f;
+      acc.w += v[j].w * f;
+    }
+    M = Mc;
   }
   const float inv = 1.0f / L;
-  const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc.x * inv) | ((uint32_t)f32_to_bf16_bits(acc.y * inv) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc.z * inv) | ((uint32_t)f32_to_bf16_bits(acc.w * inv) << 16);
+  const uint32_t lo = pack_bf16x2(acc.x * inv, acc.y * inv);
+  const uint32_t hi = pack_bf16x2(acc.z * inv, acc.w * inv);
   *reinterpret_cast<uint2*>(out + ((size_t)b * Hq + h) * D + d) = make_uint2(lo, hi);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-template <int D, int WAVES>
+template <int D, int HG, int DSPLIT>
 hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                            const uint16_t* win, uint16_t* out, float* po, float2* pml,
                            const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
+  constexpr int WAVES = HG * DSPLIT;
   constexpr int ROW_WORDS = D / 2 + 4;
   constexpr int kStagesHost = (D == 512 && WAVES >= 2) ? 4 : 2;
-  const size_t lds = (size_t)kStagesHost * kTile * ROW_WORDS * sizeof(uint32_t) +
+  constexpr int XWORDS = DSPLIT > 1 ? WAVES * kWave * 8 : 0;
+  const size_t lds = ((size_t)kStagesHost * kTile * ROW_WORDS + XWORDS) * sizeof(uint32_t) +
                      (size_t)p.rows_per_split * sizeof(int32_t);
-  auto kern = sparse_attend_kernel<D, WAVES>;
+  auto kern = sparse_attend_kernel<D, HG, DSPLIT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int hgroups = d.q_heads / (16 * WAVES);
+  const int hgroups = d.q_heads / (16 * HG);
   const int npairs = d.batch * p.splits;
   const int grid = (npairs + 7) / 8 * 8 * hgroups;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
@@ -376,16 +418,16 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
                          const AttendPlan& p, void* ws, hipStream_t st) {
   float* po = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
   float2* pml = p.splits > 1 ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
-  const int waves = p.heads_per_wg / 16;
+  const int hgw = p.heads_per_wg / 16;  // 16-head groups per workgroup
   hipError_t e;
   if (d.head_dim == 512) {
-    if (waves == 4) e = launch_attend_t<512, 4>(q, kv, idx, win, out, po, pml, d, p, st);
-    else if (waves == 2) e = launch_attend_t<512, 2>(q, kv, idx, win, out, po, pml, d, p, st);
-    else e = launch_attend_t<512, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    if (hgw == 4) e = launch_attend_t<512, 4, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    else if (hgw == 2) e = launch_attend_t<512, 2, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    else e = launch_attend_t<512, 1, 2>(q, kv, idx, win, out, po, pml, d, p, st);
   } else {
-    if (waves == 4) e = launch_attend_t<128, 4>(q, kv, idx, win, out, po, pml, d, p, st);
-    else if (waves == 2) e = launch_attend_t<128, 2>(q, kv, idx, win, out, po, pml, d, p, st);
-    else e = launch_attend_t<128, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    if (hgw == 4) e = launch_attend_t<128, 4, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    else if (hgw == 2) e = launch_attend_t<128, 2, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    else e = launch_attend_t<128, 1, 1>(q, kv, idx, win, out, po, pml, d, p, st);
   }
   if (e != hipSuccess || p.splits == 1) return e;
   const int Hq = d.q_heads;

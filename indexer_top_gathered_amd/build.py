@@ -16,6 +16,8 @@ HIPCC_FLAGS = [
     # Keep the compiler from forming packed-fp32 instructions.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden", "-Wno-unused-command-line-argument",
+    # The LDS copies write M0 from inline asm; the clobber is deliberate.
+    "-Wno-inline-asm",
 ]
 
 

@@ -128,6 +128,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// Two floats -> two fp16 in one word (lo = a), round to nearest even; one
+// v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+__device__ __forceinline__ float2 unpack_f16x2(uint32_t w) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+  return make_float2(v.x, v.y);
+}
+
+// ---------------------------------------------------------------- LDS DMA
+// Byte address of an LDS location (the M0 value of an LDS DMA).
+__device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_byte + 16*l (M0 holds the wave-uniform LDS byte address). It
+// is issued from inline assembly so that the compiler, which cannot tell
+// these LDS writes apart from later LDS reads, does not wait for every
+// outstanding copy before each read; the kernel waits with explicit vmcnt
+// values instead. No register is written asynchronously.
+// The kernels here use M0 for nothing else; the clobber documents the write
+// (the compiler reserves M0 and warns about the clobber; the build silences
+// that warning).
+__device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds_byte) : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. Arguments are already checked.
 
@@ -151,8 +185,9 @@ struct AttendPlan {
   int splits;        // row splits per (batch, head group)
   int rows_per_split;
   int heads_per_wg;  // 16 * waves per workgroup
-  size_t part_o_off; // float [B, splits, Hq, D]
-  size_t part_ml_off; // float2 [B, splits, Hq] (running max, running sum)
+  size_t part_o_off; // fp16 [B, splits, Hq, D]: O / scale of its dim half
+  size_t part_ml_off; // float4 [B, splits, Hq]: (running max, running sum, scale of dims
+                      // [0, D/2), scale of dims [D/2, D))
   size_t bytes;
 };
 AttendPlan plan_attend(const dsa_dims_t& d);

@@ -147,13 +147,16 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
 hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const float* w,
                                 float* s, int B, int N, int H, hipStream_t st) {
   // Each wave keeps its query fragments (up to 16 KB per batch row) in
-  // registers; give it at least 8 steps of keys so those reloads from L2 stay
-  // small next to the key stream, and keep a few thousand workgroups.
-  int rounds = 8;
+  // registers for its whole sweep. Aim for one round of about 256 workgroups
+  // (one per CU measured fastest), each sweeping at least 8 and at most 32
+  // rounds of 128 keys so the query loads stay small next to the key stream.
   const long long per_row_rounds = (N + kIsKeysPerRound - 1) / kIsKeysPerRound;
-  if (rounds > per_row_rounds) rounds = (int)per_row_rounds;
+  long long rounds = ((long long)B * per_row_rounds + 255) / 256;
+  if (rounds < 8) rounds = 8;
+  if (rounds > 32) rounds = 32;
+  if (rounds > per_row_rounds) rounds = per_row_rounds;
   if (rounds < 1) rounds = 1;
-  const int keys_per_wg = rounds * kIsKeysPerRound;
+  const int keys_per_wg = (int)rounds * kIsKeysPerRound;
   dim3 grid((N + keys_per_wg - 1) / keys_per_wg, B);
   dim3 block(kIsThreads);
   const int mt = (H + 15) / 16;

@@ -7,9 +7,11 @@
 //   R_b = kv_cmp[b, idx[b, :]] ++ kv_win[b, :]          (k + W rows of D)
 //   out[b,h,:] = softmax_r(scale * q[b,h,:] . R_b[r,:]) @ R_b
 //
-// Each workgroup takes one batch row, a group of 16*WAVES query heads (16
-// per wave) and a contiguous split of the rows. Rows are staged 32 at a time
-// into LDS (row-major, padded), and each staged row is used twice:
+// Each workgroup takes one batch row, a group of 16*HG query heads and a
+// contiguous split of the rows; each 16-head group is served by DSPLIT waves
+// that own 1/DSPLIT of the head dims each (they add up their halves of the
+// logits through LDS). Rows are copied 32 at a time from HBM straight into
+// LDS (row-major, padded), and each staged row is used twice:
 //   S^T = R Q^T  : MFMA A operand = 16 rows x 32 dims read straight from
 //                  LDS (ds_read_b128), B operand = the wave's query
 //                  fragments, kept in registers;
@@ -19,9 +21,12 @@
 //                  the right lanes (lane 16g+m: rows 4g..4g+3 of head m).
 // A lane therefore owns one head throughout, so the running max, the
 // rescale factor and the running sum need no cross-lane traffic except two
-// reductions per tile. The online softmax runs in float32. A single split
-// writes bf16 output directly; several splits write (max, sum, unnormalised
-// O) partials that a combine kernel merges with the log-sum-exp rule.
+// reductions per tile. The tiles are software-pipelined: the logits of tile
+// t+1 are computed while tile t is finished. The online softmax runs in
+// float32. A single split writes bf16 output directly; several splits write
+// partials (max, sum, and the unnormalised O in fp16 with one float32 scale
+// per head and dim half) that a combine kernel merges with the log-sum-exp
+// rule.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -30,28 +35,18 @@ namespace {
 constexpr int kTile = 32;          // rows per LDS tile
 constexpr int kMaxSplitTiles = 64; // rows per split <= 2048
 constexpr float kRescale = 8.0f;   // lazy-rescale margin (natural log units)
+constexpr int kStages = 3;         // LDS tiles
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at lds_byte + 16*l (M0 holds the wave-uniform LDS byte address). It
-// is issued from inline assembly so that the compiler, which cannot tell
-// these LDS writes apart from later LDS reads, does not wait for every
-// outstanding copy before each read; the kernel waits with explicit vmcnt
-// values instead. No register is written asynchronously.
-__device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_byte) : "memory", "m0");
 }
 
 template <int D, int HG, int DSPLIT>
 __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
-    uint16_t* __restrict__ out, float* __restrict__ part_o, float2* __restrict__ part_ml,
-    int N, int k, int W, int Hq, float scale, int rows_per_split, int splits, int npairs,
+    uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
+    int N, int k, int W, int Hq, float scale, int rows_per_split, int splits, int nitems,
     int hgroups) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int THREADS = WAVES * kWave;
@@ -60,26 +55,25 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   constexpr int KS = DW / 32;           // S^T k-steps per wave
   constexpr int DTW = DW / 16;          // 16-dim output tiles per wave
   constexpr int ROW_WORDS = D / 2 + 4;  // 16 bytes of padding per row
-  constexpr int CHUNKS = D / 8;         // 16-byte chunks per row
-  constexpr int CH = kTile * CHUNKS / THREADS;  // staged chunks per thread per tile
-  static_assert(CH * THREADS == kTile * CHUNKS, "tile must split evenly over the threads");
-  constexpr bool kDma = (D == 512 && WAVES >= 2);
-  constexpr int kStages = kDma ? 4 : 2;
-  constexpr int XWORDS = DSPLIT > 1 ? WAVES * kWave * 8 : 0;  // S^T exchange, 8 floats per lane
+  constexpr int ROW_LANES = D / 8;      // lanes that copy one row (16 bytes each)
+  constexpr int kRowsPerWave = kTile / WAVES;
+  constexpr int XWORDS = DSPLIT > 1 ? 2 * WAVES * kWave * 8 : 0;  // S^T exchange, by tile parity
   extern __shared__ uint32_t lds[];
   uint32_t* Rbuf = lds;  // kStages tiles
   f32x4* xbuf = reinterpret_cast<f32x4*>(lds + kStages * kTile * ROW_WORDS);
   int32_t* srow = reinterpret_cast<int32_t*>(lds + kStages * kTile * ROW_WORDS + XWORDS);
 
-  // Workgroup -> (batch, split, head group). Workgroups are dispatched to
-  // the 8 XCDs round robin, so the head groups of one (batch, split) pair
-  // get ids 8 apart: they land on one XCD and share the gathered rows in
-  // its L2.
+  // Workgroup -> work item (batch, split, head group), batch-major.
+  // Workgroups are dispatched to the 8 XCDs round robin, so XCD x runs ids
+  // x, x+8, ...; those take the x-th contiguous eighth of the work items.
+  // Every workgroup of one batch row then sits on one XCD: its query, its
+  // gathered rows and its partials are fetched from HBM once and shared
+  // through that XCD's L2.
   const int L = blockIdx.x;
-  const int per8 = 8 * hgroups;
-  const int pair = (L / per8) * 8 + (L % 8);
-  const int hg = (L % per8) / 8;
-  if (pair >= npairs) return;  // padding workgroup (uniform)
+  const int item = (L % 8) * (int)(gridDim.x / 8) + L / 8;
+  if (item >= nitems) return;  // padding workgroup (uniform)
+  const int hg = item % hgroups;
+  const int pair = item / hgroups;
   const int b = pair / splits;
   const int split = pair % splits;
   const int tid = threadIdx.x;
@@ -132,33 +126,15 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   const uint16_t* winb = win ? win + (size_t)b * W * D : nullptr;
   lds_barrier();  // srow visible
 
-  // Two ways to stage rows into the LDS tiles. For D = 512 a row is 1 KB,
-  // exactly one wave-wide 16-byte-per-lane load, so each wave DMAs its rows
-  // straight into LDS (global_load_lds) and kStages tiles are in flight; the
-  // waits are explicit vmcnt values. Rows past r1 repeat the last valid row
-  // (finite data; their weights are zero). For D = 128 four rows share one
-  // wave load, which the padded row layout cannot take, so rows go through
-  // registers with one tile of prefetch.
+  // Rows are copied from HBM straight into the LDS tiles (global_load_lds):
+  // one instruction per row, ROW_LANES lanes of 16 bytes each (at D = 128
+  // the other lanes are masked off, so rows keep their padding). Each wave
+  // copies kRowsPerWave rows of a tile; the waits are explicit vmcnt values
+  // over this wave's own copies, and a barrier publishes the tile. Rows past
+  // r1 repeat the last valid row (finite data; their weights are zero).
   const int ntiles = (r1 - r0 + kTile - 1) / kTile;
-  u32x4 stage[kDma ? 1 : CH];
-  auto fetch = [&](int t0) {  // register path: rows of tile t0 (zeros past r1)
-#pragma unroll
-    for (int c = 0; c < (kDma ? 1 : CH); ++c) {
-      const int ci = tid + c * THREADS;
-      const int rr = ci / CHUNKS;
-      const int ch = ci % CHUNKS;
-      const int r = t0 + rr;
-      stage[c] = u32x4{0u, 0u, 0u, 0u};
-      if (r < r1) {
-        const int v = srow[r - r0];
-        const uint16_t* src = v >= 0 ? kvb + (size_t)v * D : winb + (size_t)(-v - 1) * D;
-        stage[c] = *reinterpret_cast<const u32x4*>(src + ch * 8);
-      }
-    }
-  };
-  constexpr int kRowsPerWave = kTile / WAVES;
-  auto dma = [&](int tile, int slot) {  // DMA path: this wave's rows of a tile
-    uint32_t* dst = Rbuf + slot * kTile * ROW_WORDS;
+  auto dma = [&](int tile) {
+    uint32_t* dst = Rbuf + (tile % kStages) * kTile * ROW_WORDS;
     const int t0 = r0 + tile * kTile;
     int vr[kRowsPerWave];
 #pragma unroll
@@ -167,44 +143,18 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int rr = wave * kRowsPerWave + i;
       const int v = __builtin_amdgcn_readfirstlane(vr[i]);
-      const uint16_t* src = (v >= 0 ? kvb + (size_t)v * D : winb + (size_t)(-v - 1) * D) + lane * 8;
-      const uint32_t lds_byte = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)(dst + rr * ROW_WORDS);
-      dma_row16(src, __builtin_amdgcn_readfirstlane(lds_byte));
+      const uint16_t* src = (v >= 0 ? kvb + (size_t)v * D : winb + (size_t)(-v - 1) * D) + (lane % ROW_LANES) * 8;
+      const uint32_t at = __builtin_amdgcn_readfirstlane(lds_byte_addr(dst + rr * ROW_WORDS));
+      if (ROW_LANES == kWave || lane < ROW_LANES) dma_row16(src, at);
     }
   };
-  if (kDma) {
-    for (int j = 0; j < kStages - 1 && j < ntiles; ++j) dma(j, j);
-  } else {
-    fetch(r0);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = r0 + t * kTile;
-    uint32_t* R = Rbuf + (t % kStages) * kTile * ROW_WORDS;
-    if (kDma) {
-      // Tile t has landed once at most (later tiles issued) * rows-per-wave
-      // of this wave's DMA loads are still outstanding.
-      const int later = min(kStages - 2, ntiles - 1 - t);
-      if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kRowsPerWave) : "memory");
-      else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRowsPerWave) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();
-      // The slot of tile t+kStages-1 was last read by tile t-1, which every
-      // wave has finished at the barrier above.
-      if (t + kStages - 1 < ntiles) dma(t + kStages - 1, (t + kStages - 1) % kStages);
-    } else {
-      // This buffer was last read two tiles ago; the barrier of the previous
-      // iteration has seen every wave finish that tile.
-#pragma unroll
-      for (int c = 0; c < (kDma ? 1 : CH); ++c) {
-        const int ci = tid + c * THREADS;
-        *reinterpret_cast<u32x4*>(&R[(ci / CHUNKS) * ROW_WORDS + (ci % CHUNKS) * 4]) = stage[c];
-      }
-      lds_barrier();
-      if (t0 + kTile < r1) fetch(t0 + kTile);  // in flight while this tile is computed
-    }
 
-    // S^T for rows 0..15 and 16..31 of the tile, over this wave's dims.
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Partial S^T (this wave's dims) of a tile: rows 0..15 and 16..31.
+  // Lane (m, g): s0[i] is row 4g+i, s1[i] is row 16+4g+i, head m.
+  auto partial_s = [&](int tile, f32x4& s0, f32x4& s1) {
+    const uint32_t* R = Rbuf + (tile % kStages) * kTile * ROW_WORDS;
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int w0 = (dbase >> 1) + kk * 16 + g * 4;
@@ -213,26 +163,60 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       s0 = mfma16x16x32(a0, qf[kk], s0);
       s1 = mfma16x16x32(a1, qf[kk], s1);
     }
+  };
+
+  // Software pipeline over tiles: iteration t computes the (partial) logits
+  // of tile t+1 while it finishes tile t (exchange, softmax, PV), so the
+  // matrix work of one overlaps the vector work of the other. kStages = 3
+  // LDS tiles: t (PV), t+1 (S^T) and t+2 in flight.
+  static_assert(kStages == 3, "the waits below assume three tiles");
+  dma(0);
+  if (ntiles > 1) dma(1);
+  // Tile 0 has landed once at most tile 1's copies are outstanding.
+  if (ntiles > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRowsPerWave) : "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();  // tile 0 visible
+  f32x4 s0, s1;   // partial logits of the tile about to be finished
+  partial_s(0, s0, s1);
+  if (DSPLIT > 1) {
+    xbuf[(0 * WAVES + wave) * 2 * kWave + lane] = s0;
+    xbuf[(0 * WAVES + wave) * 2 * kWave + kWave + lane] = s1;
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = r0 + t * kTile;
+    // Tile t+1 has landed once no copy issued after it is outstanding (tile
+    // t+2 is issued below). The barrier also publishes the partial logits of
+    // tile t and tells that every wave finished tile t-1, whose slot then
+    // takes tile t+2.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (t + 2 < ntiles) dma(t + 2);
     if (DSPLIT > 1) {
       // The two waves of a head group each hold half of the dot products;
       // each adds the other's half. Both form the same sums (addition is
-      // commutative), so they run identical softmax states. The previous
-      // tile's reads of this buffer finished before the barrier at the top
-      // of this tile.
-      xbuf[(wave * 2 + 0) * kWave + lane] = s0;
-      xbuf[(wave * 2 + 1) * kWave + lane] = s1;
-      lds_barrier();
+      // commutative), so they run identical softmax states.
       const int partner = (DSPLIT - 1 - dh) * HG + hq;
-      s0 += xbuf[(partner * 2 + 0) * kWave + lane];
-      s1 += xbuf[(partner * 2 + 1) * kWave + lane];
+      const f32x4* xb = xbuf + ((t & 1) * WAVES + partner) * 2 * kWave;
+      s0 += xb[lane];
+      s1 += xb[kWave + lane];
     }
-    // Lane (m, g): s0[i] is row 4g+i, s1[i] is row 16+4g+i, head m.
+    const f32x4 c0 = s0, c1 = s1;  // logits of tile t
+    if (t + 1 < ntiles) {
+      partial_s(t + 1, s0, s1);
+      if (DSPLIT > 1) {
+        f32x4* xw = xbuf + (((t + 1) & 1) * WAVES + wave) * 2 * kWave;
+        xw[lane] = s0;
+        xw[kWave + lane] = s1;
+      }
+    }
+
     float z[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = (t0 + 4 * g + i < r1) ? s0[i] * scale : -INFINITY;
-      z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? s1[i] * scale : -INFINITY;
+      z[i] = (t0 + 4 * g + i < r1) ? c0[i] * scale : -INFINITY;
+      z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? c1[i] * scale : -INFINITY;
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
@@ -271,6 +255,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     // O^T += R^T P^T over this wave's dims. Within each 16-lane group, lane
     // j points at row (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4)
     // .. +4; the transposing read hands lane j the 4 rows at dim 16*dt + j.
+    const uint32_t* R = Rbuf + (t % kStages) * kTile * ROW_WORDS;
     const int ra = 4 * g + (m >> 2);
 #pragma unroll
     for (int dt = 0; dt < DTW; ++dt) {
@@ -301,12 +286,35 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       *reinterpret_cast<uint2*>(orow + dt * 16 + g * 4) = make_uint2(lo, hi);
     }
   } else {
-    const size_t slot = ((size_t)b * splits + split) * Hq + h;
-    float* po = part_o + slot * D + dbase;
+    // Partials in fp16, scaled by the largest magnitude of this wave's
+    // share of O[h] (so every value lies in [-1, 1] and keeps 11 significant
+    // bits); the scale goes with the running max and sum.
+    float amax = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < DTW; ++dt)
-      *reinterpret_cast<float4*>(po + dt * 16 + g * 4) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (dh == 0 && g == 0) part_ml[slot] = make_float2(mrun, l);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[dt][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float sc = amax > 0.0f ? amax : 1.0f;
+    const float inv = 1.0f / sc;
+    const size_t slot = ((size_t)b * splits + split) * Hq + h;
+    uint16_t* po = part_o + slot * D + dbase;
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) {
+      const uint32_t lo = pack_f16x2(o[dt][0] * inv, o[dt][1] * inv);
+      const uint32_t hi = pack_f16x2(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(po + dt * 16 + g * 4) = make_uint2(lo, hi);
+    }
+    if (g == 0) {
+      float* ml = part_ml + slot * 4;
+      if (dh == 0) {
+        ml[0] = mrun;
+        ml[1] = l;
+      }
+      ml[2 + dh] = sc;
+      if (DSPLIT == 1) ml[3] = sc;
+    }
   }
 }
 
@@ -316,24 +324,29 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
 // clamped and weighted zero), so a chunk costs one memory latency.
 template <int D>
 __global__ __launch_bounds__(D / 4) void attend_combine_kernel(
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-    uint16_t* __restrict__ out, int Hq, int splits) {
+    const uint16_t* __restrict__ part_o, const float4* __restrict__ part_ml,
+    uint16_t* __restrict__ out, int Hq, int splits, int nitems) {
   constexpr int SC = 8;
-  const int bh = blockIdx.x;
+  // The same XCD placement as the attention kernel: batch row b is merged on
+  // the XCD whose L2 holds its partials.
+  const int wg = blockIdx.x;
+  const int bh = (wg % 8) * (int)(gridDim.x / 8) + wg / 8;
+  if (bh >= nitems) return;  // padding workgroup (uniform)
   const int b = bh / Hq;
   const int h = bh % Hq;
   const int d = threadIdx.x * 4;
+  const bool upper = d >= D / 2;  // which scale covers these dims
   const size_t base = (size_t)b * splits * Hq + h;  // slot of split 0
   float M = -INFINITY, L = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < splits; s0 += SC) {
-    float2 ml[SC];
-    float4 v[SC];
+    float4 ml[SC];
+    uint2 v[SC];
 #pragma unroll
     for (int j = 0; j < SC; ++j) {
       const size_t slot = base + (size_t)min(s0 + j, splits - 1) * Hq;
       ml[j] = part_ml[slot];
-      v[j] = *reinterpret_cast<const float4*>(part_o + slot * D + d);
+      v[j] = *reinterpret_cast<const uint2*>(part_o + slot * D + d);
     }
     float Mc = M;
 #pragma unroll
@@ -348,10 +361,12 @@ __global__ __launch_bounds__(D / 4) void attend_combine_kernel(
     for (int j = 0; j < SC; ++j) {
       const float f = (s0 + j < splits) ? __expf(ml[j].x - Mc) : 0.0f;
       L += ml[j].y * f;
-      acc.x += v[j].x * f;
-      acc.y += v[j].y * f;
-      acc.z += v[j].z * f;
-      acc.w += v[j].w * f;
+      const float fs = f * (upper ? ml[j].w : ml[j].z);
+      const float2 a = unpack_f16x2(v[j].x), c = unpack_f16x2(v[j].y);
+      acc.x += a.x * fs;
+      acc.y += a.y * fs;
+      acc.z += c.x * fs;
+      acc.w += c.y * fs;
     }
     M = Mc;
   }
@@ -365,24 +380,23 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 template <int D, int HG, int DSPLIT>
 hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                           const uint16_t* win, uint16_t* out, float* po, float2* pml,
+                           const uint16_t* win, uint16_t* out, uint16_t* po, float* pml,
                            const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int ROW_WORDS = D / 2 + 4;
-  constexpr int kStagesHost = (D == 512 && WAVES >= 2) ? 4 : 2;
-  constexpr int XWORDS = DSPLIT > 1 ? WAVES * kWave * 8 : 0;
-  const size_t lds = ((size_t)kStagesHost * kTile * ROW_WORDS + XWORDS) * sizeof(uint32_t) +
+  constexpr int XWORDS = DSPLIT > 1 ? 2 * WAVES * kWave * 8 : 0;
+  const size_t lds = ((size_t)kStages * kTile * ROW_WORDS + XWORDS) * sizeof(uint32_t) +
                      (size_t)p.rows_per_split * sizeof(int32_t);
   auto kern = sparse_attend_kernel<D, HG, DSPLIT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int hgroups = d.q_heads / (16 * HG);
-  const int npairs = d.batch * p.splits;
-  const int grid = (npairs + 7) / 8 * 8 * hgroups;
+  const int nitems = d.batch * p.splits * hgroups;
+  const int grid = (nitems + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
                      pml, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split, p.splits,
-                     npairs, hgroups);
+                     nitems, hgroups);
   return hipGetLastError();
 }
 
@@ -404,8 +418,8 @@ AttendPlan plan_attend(const dsa_dims_t& d) {
   p.splits = (rows + p.rows_per_split - 1) / p.rows_per_split;
   if (p.splits > 1) {
     p.part_o_off = 0;
-    p.part_ml_off = align_up((size_t)d.batch * p.splits * d.q_heads * d.head_dim * sizeof(float), 256);
-    p.bytes = align_up(p.part_ml_off + (size_t)d.batch * p.splits * d.q_heads * sizeof(float2), 256);
+    p.part_ml_off = align_up((size_t)d.batch * p.splits * d.q_heads * d.head_dim * sizeof(uint16_t), 256);
+    p.bytes = align_up(p.part_ml_off + (size_t)d.batch * p.splits * d.q_heads * 4 * sizeof(float), 256);
   } else {
     p.part_o_off = p.part_ml_off = 0;
     p.bytes = 0;
@@ -416,8 +430,8 @@ AttendPlan plan_attend(const dsa_dims_t& d) {
 hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                          const uint16_t* win, uint16_t* out, const dsa_dims_t& d,
                          const AttendPlan& p, void* ws, hipStream_t st) {
-  float* po = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
-  float2* pml = p.splits > 1 ? reinterpret_cast<float2*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
+  uint16_t* po = p.splits > 1 ? reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
+  float* pml = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const int hgw = p.heads_per_wg / 16;  // 16-head groups per workgroup
   hipError_t e;
   if (d.head_dim == 512) {
@@ -431,10 +445,14 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
   }
   if (e != hipSuccess || p.splits == 1) return e;
   const int Hq = d.q_heads;
+  const int nitems = d.batch * Hq;
+  const int grid = (nitems + 7) / 8 * 8;
   if (d.head_dim == 512)
-    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(d.batch * Hq), dim3(128), 0, st, po, pml, out, Hq, p.splits);
+    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(grid), dim3(128), 0, st, po,
+                       reinterpret_cast<const float4*>(pml), out, Hq, p.splits, nitems);
   else
-    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(d.batch * Hq), dim3(32), 0, st, po, pml, out, Hq, p.splits);
+    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(grid), dim3(32), 0, st, po,
+                       reinterpret_cast<const float4*>(pml), out, Hq, p.splits, nitems);
   return hipGetLastError();
 }
 

@@ -96,7 +96,8 @@ DSA_EXPORT dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, 
  *            bit-identical copies of the input.
  * Requires 1 <= k <= N and k <= 4096. ws/ws_bytes: workspace of at least
  * dsa_topk_workspace_bytes(B, N, k, dtype) bytes; its contents on entry do
- * not matter.
+ * not matter. That size is 0 for rows one workgroup takes whole (then ws may
+ * be NULL), else it holds the per-segment candidates.
  */
 DSA_EXPORT size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype);
 DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k,

@@ -135,7 +135,7 @@ size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
 dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k,
                       int32_t* out_idx, void* out_val, int sorted_index, void* ws,
                       size_t ws_bytes, void* stream) {
-  if (!scores || !out_idx || !ws) return DSA_ERROR_INVALID_VALUE;
+  if (!scores || !out_idx) return DSA_ERROR_INVALID_VALUE;
   if (!aligned16(scores) || !aligned16(ws) || (reinterpret_cast<uintptr_t>(out_idx) & 3u))
     return DSA_ERROR_INVALID_VALUE;
   if (out_val && (reinterpret_cast<uintptr_t>(out_val) & (dtype == DSA_BF16 ? 1u : 3u)))
@@ -144,6 +144,7 @@ dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k
   dsa_status_t s = check_topk_shape(B, N, k, dtype);
   if (s != DSA_SUCCESS) return s;
   const TopkPlan plan = plan_topk(B, N, k, dtype);
+  if (plan.bytes > 0 && !ws) return DSA_ERROR_INVALID_VALUE;
   if (ws_bytes < plan.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();
   if (s != DSA_SUCCESS) return s;

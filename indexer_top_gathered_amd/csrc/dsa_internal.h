@@ -169,6 +169,7 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
                                 float* s, int B, int N, int H, hipStream_t st);
 
 struct TopkPlan {
+  bool fused;       // one workgroup per row does everything (no second kernel)
   int segs;         // segments per row
   int seg_len;      // elements per segment (all but the last segment)
   int vec;          // 16-byte vectors per thread per register block (1..16)

@@ -42,23 +42,34 @@
 namespace dsa {
 namespace {
 
-constexpr int kTkThreads = 512;
+constexpr int kTkThreads = 512;    // stage-1 workgroups of a segmented row
+constexpr int kRowThreads = 512;   // one workgroup for a whole row
+// Rows of at most this many vectors per thread are taken whole by one
+// workgroup; for longer rows the per-thread work of one workgroup outweighs
+// the second kernel of the segmented path (measured on the 16 x 32768
+// float32 decode-step rows: 16.9 us whole vs 15.7 us segmented).
+constexpr int kRowFusedVec = 4;
 constexpr int kTkMaxVec = 8;       // vectors per thread per register block
-constexpr int kSegCap = 8192;      // LDS candidates in stage 1 (>= 4096 + 512*8)
+// LDS candidates of a stage-1 workgroup: k (<= 4096) plus one vector of
+// every thread (THREADS * 8 bf16).
+template <int THREADS>
+constexpr int seg_cap() { return 4096 + THREADS * 8; }
 constexpr int kMergeThreads = 512;
 constexpr int kMergeCap = 16384;   // candidate slots per row in stage 2
 constexpr int kMaxWaves = 16;
 constexpr int kBins = 1024;        // buckets of an exact-select round
 constexpr int kBinBits = 10;
-constexpr int kGBins = 256;        // buckets of the group-maxima round
+constexpr int kHBins = 2048;       // buckets of a one-round histogram (11 bits)
+constexpr int kHBinBits = 11;
 
-// Per-half unsigned maximum of two words holding two 16-bit keys each. Plain
-// 32-bit code: 16-bit vector element access was miscompiled (element 0 was
-// returned for every index), so it is avoided throughout.
+// Per-half unsigned maximum of two words holding two 16-bit keys each: one
+// v_pk_max_u16. (Written as assembly: 16-bit vector element access was
+// miscompiled, element 0 being returned for every index, so 16-bit vector
+// types are avoided throughout.)
 __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
-  const uint32_t lo = max(a & 0xFFFFu, b & 0xFFFFu);
-  const uint32_t hi = max(a >> 16, b >> 16);
-  return lo | (hi << 16);
+  uint32_t r;
+  asm("v_pk_max_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 __device__ __forceinline__ void lds_barrier() {
@@ -66,13 +77,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 struct Scratch {
-  alignas(16) uint32_t hist[2][kBins];
+  alignas(16) uint32_t hist[2][kHBins];
   uint64_t wlo[kMaxWaves], whi[kMaxWaves];
-  uint32_t wsum[kMaxWaves], wmin[kMaxWaves], wmax[kMaxWaves];
+  uint32_t wsum[kMaxWaves];                                 // block scans
+  uint32_t wcnt[kMaxWaves], wmin[kMaxWaves], wmax[kMaxWaves];  // count/min/max reductions
   uint32_t digit, above, in_bucket;
+  uint32_t n_app;  // entries appended to an LDS list
+  uint64_t pick;   // a composite published to the block
 };
 
-// Exclusive block-wide scan in thread order; *total gets the sum. Two barriers.
+// Exclusive block-wide scan in thread order; *total gets the sum. One
+// barrier: every caller passes another barrier before wsum is written again.
 template <int THREADS>
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, Scratch& sc) {
   constexpr int W = THREADS / kWave;
@@ -87,53 +102,43 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, Scratch& s
     before += (w < wave) ? s : 0u;
     all += s;
   }
-  lds_barrier();
   *total = all;
   return before + inc - v;
 }
 
 // Wave 0 finds the digit whose bucket holds the need-th largest entry of
-// hist[0..NB) and publishes it; ends with a barrier.
+// hist[0..NB) and publishes it; ends with a barrier. Two wave scans: one
+// over per-lane sums of PER bins, then one over the PER bins of the lane
+// that holds the answer (one bin per lane).
 template <int NB>
 __device__ void pick_digit(const uint32_t* hist, uint32_t need, Scratch& sc, uint32_t& digit,
                            uint32_t& above, uint32_t& in_bucket) {
   constexpr int PER = NB / kWave;
-  static_assert(PER % 4 == 0, "lanes read their bins as 16-byte vectors");
+  static_assert(PER % 4 == 0 && PER <= kWave, "lanes read their bins as 16-byte vectors");
   const int tid = threadIdx.x;
   if (tid < kWave) {
-    // Lane l owns the PER contiguous bins ending at NB-1-PER*l, read as
-    // 16-byte vectors (a scalar stride-PER pattern would hit one LDS bank
-    // many times over). c[j] is bin NB-1-PER*l-j: lane order is descending.
+    // Lane l owns the PER contiguous bins ending at NB-1-PER*l (read as
+    // 16-byte vectors; a scalar stride-PER pattern would hit one LDS bank
+    // many times over), so lane order is descending bin order.
     const int base = NB - PER * (tid + 1);
-    uint32_t c[PER], local = 0;
+    uint32_t local = 0;
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(hist + base + 4 * q);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c[PER - 1 - (4 * q + i)] = x[i];
+      local += x[0] + x[1] + x[2] + x[3];
     }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) local += c[j];
     const uint32_t inc = wave_scan_incl(local);
-    const uint64_t hit = __ballot(inc >= need);
-    const int first = __ffsll((long long)hit) - 1;
-    if (tid == first) {
-      // The winning lane walks its own bins (registers, no LDS round trips).
-      uint32_t run = inc - local, d = 0, a = 0, b = 0;
-      bool found = false;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if (!found && run + c[j] >= need) {
-          found = true;
-          d = (uint32_t)(NB - 1 - PER * tid - j);
-          a = run;
-          b = c[j];
-        }
-        run += c[j];
-      }
-      sc.digit = d;
-      sc.above = a;
-      sc.in_bucket = b;
+    const int first = __ffsll((long long)__ballot(inc >= need)) - 1;  // uniform
+    const uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(inc - local), first);
+    // Lane j takes bin NB-1-PER*first-j, again in descending order.
+    const int top = NB - 1 - PER * first;
+    const uint32_t cj = tid < PER ? hist[top - tid] : 0u;
+    const uint32_t incj = wave_scan_incl(cj);
+    const int j = __ffsll((long long)__ballot(tid < PER && run + incj >= need)) - 1;
+    if (tid == j) {
+      sc.digit = (uint32_t)(top - j);
+      sc.above = run + incj - cj;
+      sc.in_bucket = cj;
     }
   }
   lds_barrier();
@@ -180,7 +185,7 @@ __device__ void bucket_range(const uint64_t* buf, int cnt, uint64_t& lo, uint64_
 // shrinks [lo, hi] to the entries inside that bucket. Expects both hist
 // halves clear behind a barrier and leaves them clear.
 template <int THREADS>
-__device__ __noinline__ uint64_t select_exact(const uint64_t* buf, int cnt, int K, Scratch& sc) {
+__device__ __forceinline__ uint64_t select_exact(const uint64_t* buf, int cnt, int K, Scratch& sc) {
   const int tid = threadIdx.x;
   uint64_t lo = 0, hi = ~(uint64_t)0;
   bucket_range<THREADS>(buf, cnt, lo, hi, sc);
@@ -377,11 +382,13 @@ __device__ __forceinline__ u32x4 load_keys(const void* row, int64_t p0, int64_t 
 }
 
 // From below: a T with at least K of the G group maxima per thread (raw
-// keys, 0 = none) >= T, from two range-splitting histogram rounds; 1 when
-// fewer than K maxima exist.
-template <int G>
+// keys, 0 = none) >= T: the lower edge of the bucket that holds the K-th
+// largest maximum, in one histogram round whose 2048 buckets split the
+// maxima's actual [lo, hi]; 1 when fewer than K maxima exist. Leaves
+// hist[0] clear.
+template <int THREADS, int G>
 __device__ uint32_t group_threshold(const uint32_t (&g)[G], int K, Scratch& sc) {
-  constexpr int W = kTkThreads / kWave;
+  constexpr int W = THREADS / kWave;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   uint32_t lo = 0xFFFFFFFFu, hi = 0, n = 0;
 #pragma unroll
@@ -395,8 +402,10 @@ __device__ uint32_t group_threshold(const uint32_t (&g)[G], int K, Scratch& sc) 
   n = wave_reduce<OpAdd>(n);
   lo = wave_reduce<OpMin>(lo);
   hi = wave_reduce<OpMax>(hi);
+  // wcnt/wmin/wmax are written again only behind later barriers (block
+  // scans use wsum), so no second barrier is needed.
   if (lane == 0) {
-    sc.wsum[wave] = n;
+    sc.wcnt[wave] = n;
     sc.wmin[wave] = lo;
     sc.wmax[wave] = hi;
   }
@@ -404,43 +413,34 @@ __device__ uint32_t group_threshold(const uint32_t (&g)[G], int K, Scratch& sc) 
   n = 0;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
-    n += sc.wsum[w];
+    n += sc.wcnt[w];
     lo = min(lo, sc.wmin[w]);
     hi = max(hi, sc.wmax[w]);
   }
   if ((int)n < K) return 1u;  // uniform
-  uint32_t need = (uint32_t)K;
-  for (int round = 0; round < 2; ++round) {
-    const uint32_t range = hi - lo;
-    if (range == 0) break;
-    const int hb = 31 - __clz(range);
-    const int shift = hb > 7 ? hb - 7 : 0;
-    uint32_t* h = sc.hist[round];
+  const uint32_t range = hi - lo;
+  if (range == 0) return lo;
+  const int hb = 31 - __clz(range);
+  const int shift = hb >= kHBinBits ? hb - (kHBinBits - 1) : 0;
+  uint32_t* h = sc.hist[0];
 #pragma unroll
-    for (int e = 0; e < G; ++e)
-      if (g[e] >= lo && g[e] <= hi) atomicAdd(&h[(g[e] - lo) >> shift], 1u);
-    lds_barrier();
-    uint32_t digit, above, in_bucket;
-    pick_digit<kGBins>(h, need, sc, digit, above, in_bucket);
-    for (int i = threadIdx.x; i < kGBins; i += kTkThreads) h[i] = 0;  // ordered by later barriers
-    need -= above;
-    const uint32_t blo = lo + (digit << shift);
-    if (in_bucket == need) return blo;
-    lo = blo;
-    const uint32_t bhi = blo + ((1u << shift) - 1u);
-    hi = bhi < hi ? bhi : hi;
-  }
-  return lo;
+  for (int e = 0; e < G; ++e)
+    if (g[e] >= lo) atomicAdd(&h[(g[e] - lo) >> shift], 1u);
+  lds_barrier();
+  uint32_t digit, above, in_bucket;
+  pick_digit<kHBins>(h, (uint32_t)K, sc, digit, above, in_bucket);
+  for (int i = threadIdx.x; i < kHBins; i += THREADS) h[i] = 0;  // ordered by later barriers
+  return lo + (digit << shift);
 }
 
-template <bool BF16, int V>
+template <bool BF16, int V, int THREADS>
 __device__ __forceinline__ void write_admitted(uint64_t* cand, uint32_t at, const u32x4 (&kv)[V],
                                                uint64_t adm, int64_t base) {
   constexpr int E = BF16 ? 8 : 4;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     uint32_t m = (uint32_t)(adm >> (v * E)) & ((1u << E) - 1u);
-    const int64_t p0 = base + ((int64_t)v * kTkThreads + threadIdx.x) * E;
+    const int64_t p0 = base + ((int64_t)v * THREADS + threadIdx.x) * E;
     while (m) {
       const int e = __ffs(m) - 1;
       m &= m - 1;
@@ -480,13 +480,83 @@ __device__ __forceinline__ uint32_t admit_vector(const u32x4& kv, uint32_t t0, b
   return bits;
 }
 
-template <bool BF16, bool ALIGNED, int V>
-__global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
+// The K-th largest of the distinct composites buf[0..cnt) (K < cnt), as a
+// threshold: exactly K entries are >= it. One histogram round over the
+// value keys (2048 buckets over their actual range) finds its bucket; a
+// bucket that is not taken whole is gathered into a list and ranked entry
+// against entry; a bucket of more than THREADS entries (heavy ties) takes
+// the general select. Expects both histograms clear and leaves them dirty.
+template <int THREADS>
+__device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int K, Scratch& sc) {
+  constexpr int W = THREADS / kWave;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int i = tid; i < cnt; i += THREADS) {
+    const uint32_t key = (uint32_t)(buf[i] >> 32);
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  lo = wave_reduce<OpMin>(lo);
+  hi = wave_reduce<OpMax>(hi);
+  if (lane == 0) {
+    sc.wmin[wave] = lo;
+    sc.wmax[wave] = hi;
+  }
+  if (tid == 0) sc.n_app = 0;
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    lo = min(lo, sc.wmin[w]);
+    hi = max(hi, sc.wmax[w]);
+  }
+  const uint32_t range = hi - lo;
+  const int shift = range == 0 ? 0 : max(0, 31 - __clz(range) - (kHBinBits - 1));
+  uint32_t* h = sc.hist[0];
+  for (int i = tid; i < cnt; i += THREADS) atomicAdd(&h[((uint32_t)(buf[i] >> 32) - lo) >> shift], 1u);
+  lds_barrier();
+  uint32_t digit, above, in_bucket;
+  pick_digit<kHBins>(h, (uint32_t)K, sc, digit, above, in_bucket);
+  const uint32_t need = (uint32_t)K - above;
+  const uint32_t blo = lo + (digit << shift);
+  if (in_bucket == need) return (uint64_t)blo << 32;  // the whole bucket is in (uniform)
+  if (in_bucket <= (uint32_t)THREADS && in_bucket <= (uint32_t)(kHBins / 2)) {
+    uint64_t* list = reinterpret_cast<uint64_t*>(sc.hist[1]);  // kHBins / 2 entries
+    for (int i = tid; i < cnt; i += THREADS) {
+      const uint64_t x = buf[i];
+      if ((((uint32_t)(x >> 32) - lo) >> shift) == digit) list[atomicAdd(&sc.n_app, 1u)] = x;
+    }
+    lds_barrier();
+    if (tid < (int)in_bucket) {
+      const uint64_t x = list[tid];
+      uint32_t r = 0;
+      for (uint32_t i = 0; i < in_bucket; ++i) r += list[i] > x ? 1u : 0u;
+      if (r == need - 1) sc.pick = x;  // exactly one entry has this rank
+    }
+    lds_barrier();
+    return sc.pick;
+  }
+  for (int i = tid; i < kHBins; i += THREADS) h[i] = 0;  // ordered by the next barrier
+  return select_exact<THREADS>(buf, cnt, K, sc);
+}
+
+// FUSED (one segment covering the whole row): after stage 1 the workgroup
+// also selects the row's k winners from its LDS candidates and writes them,
+// so no stage 2 runs.
+template <bool BF16, int kPer, int THREADS>
+__device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t thr, const char* row,
+                                       int N, int k, int32_t* oi, void* out_val, size_t out_off,
+                                       int sorted_index, uint32_t* pos_lds, Scratch& sc);
+
+template <bool BF16, bool ALIGNED, int V, int THREADS, bool FUSED>
+__global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     const void* __restrict__ scores, int N, int k, int seg_len, int segs,
-    uint64_t* __restrict__ cand_out, uint32_t* __restrict__ cnt_out) {
+    uint64_t* __restrict__ cand_out, uint32_t* __restrict__ cnt_out,
+    int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index) {
   constexpr int E = BF16 ? 8 : 4;
+  constexpr int CAP = seg_cap<THREADS>();
   static_assert(V * E <= 64, "the admission mask holds 64 bits");
-  extern __shared__ uint64_t cand[];  // kSegCap entries
+  extern __shared__ uint64_t cand[];  // CAP entries
   __shared__ Scratch sc;
   const int b = blockIdx.y;
   const int sidx = blockIdx.x;
@@ -494,9 +564,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
   const void* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;
   const int64_t seg_start = (int64_t)sidx * seg_len;
   const int64_t seg_end = min((int64_t)N, seg_start + seg_len);
-  constexpr int64_t kBlock = (int64_t)kTkThreads * V * E;
+  constexpr int64_t kBlock = (int64_t)THREADS * V * E;
 
-  for (int i = threadIdx.x; i < kBins; i += kTkThreads) {
+  for (int i = threadIdx.x; i < kHBins; i += THREADS) {
     sc.hist[0][i] = 0;
     sc.hist[1][i] = 0;
   }
@@ -508,7 +578,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
     u32x4 kv[V];
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      kv[v] = load_keys<BF16, ALIGNED>(row, base + ((int64_t)v * kTkThreads + threadIdx.x) * E, seg_end);
+      kv[v] = load_keys<BF16, ALIGNED>(row, base + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
     // Group maxima (raw keys): element e of every vector of this thread.
     uint32_t g[E];
     if (BF16) {
@@ -536,7 +606,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
     // still leave a threshold near the k-th largest score. Fold the E maxima
     // per thread in halves (a zero slot means "no group") while half of them
     // still give 2k groups.
-    const int gpt = (2 * k + kTkThreads - 1) / kTkThreads;  // wanted groups per thread
+    const int gpt = (2 * k + THREADS - 1) / THREADS;  // wanted groups per thread
 #pragma unroll
     for (int half = E / 2; half >= 1; half /= 2) {
       if (gpt <= half) {  // uniform
@@ -547,7 +617,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
         }
       }
     }
-    uint32_t t0 = group_threshold<E>(g, k, sc);
+    uint32_t t0 = group_threshold<THREADS, E>(g, k, sc);
     // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
     if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
     // Admission: raw key >= t0 and, once an exact threshold exists, composite > thr.
@@ -555,38 +625,45 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
 #pragma unroll
     for (int v = 0; v < V; ++v)
       adm |= (uint64_t)admit_vector<BF16>(kv[v], t0, have_thr, thr,
-                                          base + ((int64_t)v * kTkThreads + threadIdx.x) * E)
+                                          base + ((int64_t)v * THREADS + threadIdx.x) * E)
              << (v * E);
     uint32_t total;
-    const uint32_t excl = block_exclusive_scan<kTkThreads>((uint32_t)__popcll(adm), &total, sc);
-    if (base == seg_start && base + kBlock >= seg_end && (int)total <= 2 * k) {
+    const uint32_t excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
+    if (!FUSED && base == seg_start && base + kBlock >= seg_end && (int)total <= 2 * k) {
       // The whole segment in one block and its survivors fit the output
       // slots: write them straight to the workspace.
-      write_admitted<BF16, V>(cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k), excl, kv, adm, base);
+      write_admitted<BF16, V, THREADS>(cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k), excl, kv,
+                                       adm, base);
       if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = total;
       return;
     }
-    if (cnt + (int)total <= kSegCap) {
-      write_admitted<BF16, V>(cand, (uint32_t)cnt + excl, kv, adm, base);
+    if (cnt + (int)total <= CAP) {
+      write_admitted<BF16, V, THREADS>(cand, (uint32_t)cnt + excl, kv, adm, base);
       cnt += (int)total;
       lds_barrier();
     } else {
-      // Too many survivors: one vector at a time (each adds at most 512*E
-      // entries), with an exact select whenever the next might not fit;
-      // each vector is filtered against the thresholds current at its turn.
+      // Too many survivors: one vector at a time (each adds at most
+      // THREADS*E entries), with an exact select whenever the next might not
+      // fit; each vector is filtered against the thresholds current at its
+      // turn.
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        if (cnt + kTkThreads * E > kSegCap && cnt > k) {
-          const uint64_t t = select_exact<kTkThreads>(cand, cnt, k, sc);
-          cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sc);
+        if (cnt + THREADS * E > CAP && cnt > k) {
+          const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
+          cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
+          for (int i = threadIdx.x; i < kHBins; i += THREADS) {
+            sc.hist[0][i] = 0;
+            sc.hist[1][i] = 0;
+          }
+          lds_barrier();
           thr = t - 1;  // t > 0: real composites have a non-zero high word
           have_thr = true;
         }
-        const int64_t p0 = base + ((int64_t)v * kTkThreads + threadIdx.x) * E;
+        const int64_t p0 = base + ((int64_t)v * THREADS + threadIdx.x) * E;
         const uint64_t vbits = (uint64_t)admit_vector<BF16>(kv[v], t0, have_thr, thr, p0) << (v * E);
         uint32_t vt;
-        const uint32_t vx = block_exclusive_scan<kTkThreads>((uint32_t)__popcll(vbits), &vt, sc);
-        write_admitted<BF16, V>(cand, (uint32_t)cnt + vx, kv, vbits, base);
+        const uint32_t vx = block_exclusive_scan<THREADS>((uint32_t)__popcll(vbits), &vt, sc);
+        write_admitted<BF16, V, THREADS>(cand, (uint32_t)cnt + vx, kv, vbits, base);
         cnt += (int)vt;
         lds_barrier();
       }
@@ -594,21 +671,104 @@ __global__ __launch_bounds__(kTkThreads) void topk_segment_kernel(
     // Before another block: cut to the exact top k so that block is also
     // filtered by the k-th composite.
     if (base + kBlock < seg_end && cnt > k) {
-      const uint64_t t = select_exact<kTkThreads>(cand, cnt, k, sc);
-      cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sc);
+      const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
+      cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
+      for (int i = threadIdx.x; i < kHBins; i += THREADS) {
+        sc.hist[0][i] = 0;
+        sc.hist[1][i] = 0;
+      }
+      lds_barrier();
       thr = t - 1;
       have_thr = true;
     }
   }
+  if (FUSED) {
+    // The row's candidates are all here: select the k winners and write them.
+    const uint64_t t = cnt > k ? select_k_lds<THREADS>(cand, cnt, k, sc) : (uint64_t)0;
+    write_winners_from_lds<BF16, CAP / THREADS, THREADS>(
+        cand, cnt, t, reinterpret_cast<const char*>(row), N, k, out_idx + (size_t)b * k, out_val,
+        (size_t)b * k, sorted_index, reinterpret_cast<uint32_t*>(cand + CAP), sc);
+    return;
+  }
   // At most 2k candidates leave the segment.
   if (cnt > 2 * k) {
-    const uint64_t t = select_exact<kTkThreads>(cand, cnt, k, sc);
-    cnt = block_compact<kTkThreads, kSegCap / kTkThreads>(cand, cnt, t, sc);
+    const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
+    cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
   }
   cnt = min(cnt, 2 * k);
   uint64_t* out = cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k);
-  for (int i = threadIdx.x; i < cnt; i += kTkThreads) out[i] = cand[i];
+  for (int i = threadIdx.x; i < cnt; i += THREADS) out[i] = cand[i];
   if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = (uint32_t)cnt;
+}
+
+// The winners (entries >= thr, exactly k of them, or all cnt <= k) of an
+// LDS candidate list: indices (and value copies) in list order, or sorted
+// by index through pos_lds (P = next power of two >= k entries).
+template <bool BF16, int kPer, int THREADS>
+__device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t thr, const char* row,
+                                       int N, int k, int32_t* oi, void* out_val, size_t out_off,
+                                       int sorted_index, uint32_t* pos_lds, Scratch& sc) {
+  const int tid = threadIdx.x;
+  // Thread t takes entries [t*per, t*per + per).
+  const int per = (cnt + THREADS - 1) / THREADS;
+  const int lo = min(cnt, tid * per);
+  const int hi = min(cnt, lo + per);
+  uint64_t v[kPer];
+  uint32_t keep = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = lo + j;
+    v[j] = (i < hi) ? cand[i] : 0;
+    keep += (i < hi && v[j] >= thr) ? 1u : 0u;
+  }
+  uint32_t nkeep;
+  uint32_t pos = block_exclusive_scan<THREADS>(keep, &nkeep, sc);
+  if (!sorted_index) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (lo + j < hi && v[j] >= thr && pos < (uint32_t)k) {
+        const uint32_t p = min(composite_pos(v[j]), (uint32_t)(N - 1));
+        oi[pos] = (int32_t)p;
+        if (out_val) {
+          if (BF16) reinterpret_cast<uint16_t*>(out_val)[out_off + pos] = reinterpret_cast<const uint16_t*>(row)[p];
+          else reinterpret_cast<uint32_t*>(out_val)[out_off + pos] = reinterpret_cast<const uint32_t*>(row)[p];
+        }
+        ++pos;
+      }
+    }
+    return;
+  }
+  int P = 1;
+  while (P < k) P <<= 1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (lo + j < hi && v[j] >= thr && pos < (uint32_t)k) pos_lds[pos++] = min(composite_pos(v[j]), (uint32_t)(N - 1));
+  for (int i = (int)min(nkeep, (uint32_t)k) + tid; i < P; i += THREADS) pos_lds[i] = 0xFFFFFFFFu;
+  lds_barrier();
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < P / 2; t += THREADS) {
+        const int i = 2 * t - (t & (stride - 1));
+        const int j = i + stride;
+        const bool up = ((i & size) == 0);
+        const uint32_t x = pos_lds[i], y = pos_lds[j];
+        if ((x > y) == up) {
+          pos_lds[i] = y;
+          pos_lds[j] = x;
+        }
+      }
+      lds_barrier();
+    }
+  }
+  const int nout = (int)min(nkeep, (uint32_t)k);
+  for (int i = tid; i < nout; i += THREADS) {
+    const uint32_t p = pos_lds[i];
+    oi[i] = (int32_t)p;
+    if (out_val) {
+      if (BF16) reinterpret_cast<uint16_t*>(out_val)[out_off + i] = reinterpret_cast<const uint16_t*>(row)[p];
+      else reinterpret_cast<uint32_t*>(out_val)[out_off + i] = reinterpret_cast<const uint32_t*>(row)[p];
+    }
+  }
 }
 
 template <bool BF16, int kPer>  // kPer: candidate slots per thread (segs * 2k <= 512 * kPer)
@@ -623,10 +783,11 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   const int b = blockIdx.x;
   const int slots = 2 * k;  // per segment
   if (tid < segs) seg_cnt[tid] = min((uint32_t)slots, cnt_in[(size_t)b * segs + tid]);
-  for (int i = tid; i < kBins; i += kMergeThreads) {
+  for (int i = tid; i < kHBins; i += kMergeThreads) {
     sc.hist[0][i] = 0;
     sc.hist[1][i] = 0;
   }
+  if (tid == 0) sc.n_app = 0;
   lds_barrier();
   // Every slot of the row at once: slot q = tid + j*512 is entry q % slots
   // of segment q / slots, valid below that segment's count.
@@ -646,18 +807,77 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     v[j] = ok ? v[j] : 0;
     nvalid += ok ? 1u : 0u;
   }
-  uint32_t total = wave_reduce<OpAdd>(nvalid);
+  // Count, smallest and largest value key of the valid entries.
+  uint32_t total, kmin, kmax;
   {
     const int lane = tid & (kWave - 1), wave = tid / kWave;
-    if (lane == 0) sc.wsum[wave] = total;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t key = (uint32_t)(v[j] >> 32);
+      lo = v[j] ? min(lo, key) : lo;
+      hi = v[j] ? max(hi, key) : hi;
+    }
+    const uint32_t n = wave_reduce<OpAdd>(nvalid);
+    lo = wave_reduce<OpMin>(lo);
+    hi = wave_reduce<OpMax>(hi);
+    if (lane == 0) {  // wcnt/wmin/wmax: not written again in this kernel
+      sc.wcnt[wave] = n;
+      sc.wmin[wave] = lo;
+      sc.wmax[wave] = hi;
+    }
     lds_barrier();
     total = 0;
+    kmin = 0xFFFFFFFFu;
+    kmax = 0;
 #pragma unroll
-    for (int w = 0; w < kMergeThreads / kWave; ++w) total += sc.wsum[w];
-    lds_barrier();  // wsum is reused below
+    for (int w = 0; w < kMergeThreads / kWave; ++w) {
+      total += sc.wcnt[w];
+      kmin = min(kmin, sc.wmin[w]);
+      kmax = max(kmax, sc.wmax[w]);
+    }
   }
+  // The k-th largest composite. One histogram round over the value keys
+  // (2048 buckets over [kmin, kmax]) finds its bucket; if that bucket is not
+  // taken whole, its few entries are gathered in LDS and ranked against one
+  // another (composites are distinct, so exactly one has rank need-1). A
+  // bucket of more than 512 entries (heavy ties) takes the general select.
   uint64_t thr = 0;
-  if ((int)total > k) thr = select_exact_regs<kMergeThreads, kPer>(v, k, sc);
+  if ((int)total > k) {
+    const uint32_t range = kmax - kmin;
+    const int shift = range == 0 ? 0 : max(0, 31 - __clz(range) - (kHBinBits - 1));
+    uint32_t* h = sc.hist[0];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (v[j]) atomicAdd(&h[((uint32_t)(v[j] >> 32) - kmin) >> shift], 1u);
+    lds_barrier();
+    uint32_t digit, above, in_bucket;
+    pick_digit<kHBins>(h, (uint32_t)k, sc, digit, above, in_bucket);
+    const uint32_t need = (uint32_t)k - above;
+    const uint32_t blo = kmin + (digit << shift);
+    if (in_bucket == need) {
+      thr = (uint64_t)blo << 32;  // the whole bucket is in
+    } else if (in_bucket <= (uint32_t)kMergeThreads) {
+      uint64_t* list = reinterpret_cast<uint64_t*>(sc.hist[1]);  // 1024 entries
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        if (v[j] && (((uint32_t)(v[j] >> 32) - kmin) >> shift) == digit)
+          list[atomicAdd(&sc.n_app, 1u)] = v[j];
+      }
+      lds_barrier();
+      if (tid < (int)in_bucket) {
+        const uint64_t x = list[tid];
+        uint32_t r = 0;
+        for (uint32_t i = 0; i < in_bucket; ++i) r += list[i] > x ? 1u : 0u;
+        if (r == need - 1) sc.pick = x;
+      }
+      lds_barrier();
+      thr = sc.pick;
+    } else {
+      for (int i = tid; i < kHBins; i += kMergeThreads) h[i] = 0;  // ordered by the next barrier
+      thr = select_exact_regs<kMergeThreads, kPer>(v, k, sc);
+    }
+  }
   // Winners in (thread, slot) order.
   uint32_t keep = 0;
 #pragma unroll
@@ -725,26 +945,42 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <bool BF16, bool AL, int V>
-hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p,
-                      uint64_t* cand, uint32_t* cnt, hipStream_t st) {
-  const size_t lds = (size_t)kSegCap * sizeof(uint64_t);
-  hipError_t e = allow_lds(topk_segment_kernel<BF16, AL, V>, lds);
+template <bool BF16, bool AL, int V, int THREADS, bool FUSED>
+hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
+                      uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
+                      hipStream_t st) {
+  int P = 1;
+  while (P < k) P <<= 1;
+  const size_t lds = (size_t)seg_cap<THREADS>() * sizeof(uint64_t) + (FUSED ? (size_t)P * sizeof(uint32_t) : 0);
+  auto kern = topk_segment_kernel<BF16, AL, V, THREADS, FUSED>;
+  hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_segment_kernel<BF16, AL, V>), dim3(p.segs, B), dim3(kTkThreads), lds,
-                     st, scores, N, k, p.seg_len, p.segs, cand, cnt);
+  hipLaunchKernelGGL(kern, dim3(p.segs, B), dim3(THREADS), lds, st, scores, N, k, p.seg_len, p.segs,
+                     cand, cnt, out_idx, out_val, sorted_index);
   return hipGetLastError();
 }
 
-template <bool BF16, bool AL>
-hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan& p,
-                        uint64_t* cand, uint32_t* cnt, hipStream_t st) {
+template <bool BF16, bool AL, int THREADS, bool FUSED>
+hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
+                        uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
+                        hipStream_t st) {
   switch (p.vec) {
-    case 1: return launch_seg<BF16, AL, 1>(scores, B, N, k, p, cand, cnt, st);
-    case 2: return launch_seg<BF16, AL, 2>(scores, B, N, k, p, cand, cnt, st);
-    case 4: return launch_seg<BF16, AL, 4>(scores, B, N, k, p, cand, cnt, st);
-    default: return launch_seg<BF16, AL, 8>(scores, B, N, k, p, cand, cnt, st);
+    case 1: return launch_seg<BF16, AL, 1, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
+    case 2: return launch_seg<BF16, AL, 2, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
+    case 4: return launch_seg<BF16, AL, 4, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
+    default: return launch_seg<BF16, AL, 8, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
   }
+}
+
+template <bool BF16, bool AL>
+hipError_t launch_stage1(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
+                         uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
+                         hipStream_t st) {
+  if (p.fused)
+    return launch_seg_v<BF16, AL, kRowThreads, true>(scores, B, N, k, p, cand, cnt, out_idx, out_val,
+                                                     sorted_index, st);
+  return launch_seg_v<BF16, AL, kTkThreads, false>(scores, B, N, k, p, cand, cnt, out_idx, out_val,
+                                                   sorted_index, st);
 }
 
 }  // namespace
@@ -752,6 +988,23 @@ hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan&
 TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
   TopkPlan p{};
   const int E = dt == DSA_BF16 ? 8 : 4;
+  // A row that one workgroup covers in one register block is taken whole
+  // by that workgroup (one kernel, no candidates in memory); longer rows are
+  // split into segments that a second kernel merges.
+  const int max_vec = kRowFusedVec;
+  if ((long long)N <= (long long)kRowThreads * max_vec * E) {
+    const long long chunk = (long long)kRowThreads * E;
+    long long vec = ((long long)N + chunk - 1) / chunk;
+    int v = 1;
+    while (v < vec && v < max_vec) v <<= 1;
+    p.fused = true;
+    p.vec = v;
+    p.segs = 1;
+    p.seg_len = N;
+    p.cand_off = p.cnt_off = 0;
+    p.bytes = 0;
+    return p;
+  }
   const long long chunk = (long long)kTkThreads * E;  // one vector per thread
   // About one workgroup per CU over the call; each row's candidates
   // (segs * 2k) must fit the merge buffer.
@@ -768,6 +1021,7 @@ TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
   const long long vec = seg_len / chunk;  // vectors per thread over the segment
   int v = 1;
   while (v < vec && v < kTkMaxVec) v <<= 1;
+  p.fused = false;
   p.vec = v;
   p.segs = (int)segs;
   p.seg_len = (int)seg_len;
@@ -786,11 +1040,11 @@ hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
   const int E = bf16 ? 8 : 4;
   const bool aligned = (N % E) == 0 && (reinterpret_cast<uintptr_t>(scores) % 16) == 0;
   hipError_t e;
-  if (bf16) e = aligned ? launch_seg_v<true, true>(scores, B, N, k, plan, cand, cnt, st)
-                        : launch_seg_v<true, false>(scores, B, N, k, plan, cand, cnt, st);
-  else e = aligned ? launch_seg_v<false, true>(scores, B, N, k, plan, cand, cnt, st)
-                   : launch_seg_v<false, false>(scores, B, N, k, plan, cand, cnt, st);
-  if (e != hipSuccess) return e;
+  if (bf16) e = aligned ? launch_stage1<true, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st)
+                        : launch_stage1<true, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st);
+  else e = aligned ? launch_stage1<false, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st)
+                   : launch_stage1<false, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st);
+  if (e != hipSuccess || plan.fused) return e;
   int P = 1;
   while (P < k) P <<= 1;
   const size_t merge_lds = (size_t)P * sizeof(uint32_t);

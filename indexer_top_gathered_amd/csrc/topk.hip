@@ -574,11 +574,26 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   bool have_thr = false;
   uint64_t thr = 0;  // once set: admit only composites > thr
 
-  for (int64_t base = seg_start; base < seg_end; base += kBlock) {
-    u32x4 kv[V];
+  // Register blocks of THREADS*V*E scores. The first block sets a threshold
+  // from its group maxima and is cut to its exact top k; later blocks are
+  // only filtered against that k-th composite (which every later winner must
+  // beat), and the next block's loads are in flight while one is filtered.
+  u32x4 kv[V], kn[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      kv[v] = load_keys<BF16, ALIGNED>(row, base + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+  for (int v = 0; v < V; ++v)
+    kv[v] = load_keys<BF16, ALIGNED>(row, seg_start + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+  for (int64_t base = seg_start; base < seg_end; base += kBlock) {
+    if (base + kBlock < seg_end) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        kn[v] = load_keys<BF16, ALIGNED>(row, base + kBlock + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+    }
+    uint32_t t0;
+    if (have_thr) {
+      // Raw-key bound of the k-th composite for the vector test.
+      const uint32_t key32 = (uint32_t)(thr >> 32);
+      t0 = BF16 ? (key32 >> 16) : key32;
+    } else {
     // Group maxima (raw keys): element e of every vector of this thread.
     uint32_t g[E];
     if (BF16) {
@@ -617,14 +632,17 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
         }
       }
     }
-    uint32_t t0 = group_threshold<THREADS, E>(g, k, sc);
+    t0 = group_threshold<THREADS, E>(g, k, sc);
+    }
     // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
     if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
-    // Admission: raw key >= t0 and, once an exact threshold exists, composite > thr.
+    // Admission: raw key >= t0. Once an exact threshold exists, t0 is its
+    // value key, so ties at that value are admitted too (harmless extra
+    // candidates; the position test is left to the overflow path below).
     uint64_t adm = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      adm |= (uint64_t)admit_vector<BF16>(kv[v], t0, have_thr, thr,
+      adm |= (uint64_t)admit_vector<BF16>(kv[v], t0, false, thr,
                                           base + ((int64_t)v * THREADS + threadIdx.x) * E)
              << (v * E);
     uint32_t total;
@@ -668,9 +686,9 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
         lds_barrier();
       }
     }
-    // Before another block: cut to the exact top k so that block is also
-    // filtered by the k-th composite.
-    if (base + kBlock < seg_end && cnt > k) {
+    // After the first block: cut to the exact top k so that later blocks
+    // are filtered by the k-th composite.
+    if (base + kBlock < seg_end && cnt > k && !have_thr) {
       const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
       cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
       for (int i = threadIdx.x; i < kHBins; i += THREADS) {
@@ -681,6 +699,8 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       thr = t - 1;
       have_thr = true;
     }
+#pragma unroll
+    for (int v = 0; v < V; ++v) kv[v] = kn[v];
   }
   if (FUSED) {
     // The row's candidates are all here: select the k winners and write them.

@@ -34,7 +34,10 @@ namespace {
 
 constexpr int kTile = 32;          // rows per LDS tile
 constexpr int kMaxSplitTiles = 64; // rows per split <= 2048
-constexpr float kRescale = 8.0f;   // lazy-rescale margin (natural log units)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy-rescale margin in base-2 units: weights stay below 2^11.5 (about e^8).
+constexpr float kRescale2 = 11.5f;
 constexpr int kStages = 3;         // LDS tiles
 
 __device__ __forceinline__ void lds_barrier() {
@@ -91,15 +94,52 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   const int r0 = split * rows_per_split;
   const int r1 = min(rows, r0 + rows_per_split);
 
+  const int ntiles = (r1 - r0 + kTile - 1) / kTile;
+  const int32_t* irow = idx + (size_t)b * k;
+  const uint16_t* kvb = kv + (size_t)b * N * D;
+  const uint16_t* winb = win ? win + (size_t)b * W * D : nullptr;
+
+  // The first two tiles' copies go out first, their row indices read with
+  // wave-uniform scalar loads (all issued before any is used), so they need
+  // neither the row list in LDS nor a barrier. A row is copied by one
+  // instruction, ROW_LANES lanes of 16 bytes each (at D = 128 the other
+  // lanes are masked off, so rows keep their padding).
+  {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int vr[2][kRowsPerWave];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile)
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int r = min(r0 + tile * kTile + wv * kRowsPerWave + i, r1 - 1);
+        vr[tile][i] = irow[min(r, k - 1)];
+      }
+    const uint32_t rbase = lds_byte_addr(Rbuf);  // tile slot j starts at rbase + j*kTile*ROW_WORDS*4
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      if (tile < ntiles) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+          const int rr = wv * kRowsPerWave + i;
+          const int r = min(r0 + tile * kTile + rr, r1 - 1);
+          const int v = vr[tile][i] < 0 ? 0 : (vr[tile][i] >= N ? N - 1 : vr[tile][i]);
+          const uint16_t* src = r < k ? kvb + (size_t)v * D : winb + (size_t)(r - k) * D;
+          const uint32_t at = __builtin_amdgcn_readfirstlane(
+              rbase + (uint32_t)((tile * kTile + rr) * ROW_WORDS * 4));
+          if (ROW_LANES == kWave || lane < ROW_LANES) dma_row16(src + (lane % ROW_LANES) * 8, at);
+        }
+      }
+    }
+  }
+
   // Query fragments (B operand of S^T): head h, dims dbase + 32*kk + 8g .. +8.
-  // Issued first so that their latency overlaps the index loads below.
   bf16x8 qf[KS];
   const uint16_t* qrow = q + ((size_t)b * Hq + h) * D + dbase;
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g * 8);
 
-  // The split's source rows: >= 0 a compressed row, < 0 window row -(v+1).
-  const int32_t* irow = idx + (size_t)b * k;
+  // The split's source rows for the later tiles: >= 0 a compressed row,
+  // < 0 window row -(v+1).
   for (int r = r0 + tid; r < r1; r += THREADS) {
     int v;
     if (r < k) {
@@ -119,20 +159,17 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   f32x4 o[DTW];
 #pragma unroll
   for (int dt = 0; dt < DTW; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // The softmax runs in base 2: logits are scaled by scale*log2(e), so every
+  // weight is one exp2. mrun is in those units.
+  const float scale2 = scale * kLog2e;
   float mrun = -INFINITY;  // running max of the scaled logits of head h
   float lrun = 0.0f;       // this lane's share of the running sum
 
-  const uint16_t* kvb = kv + (size_t)b * N * D;
-  const uint16_t* winb = win ? win + (size_t)b * W * D : nullptr;
-  lds_barrier();  // srow visible
-
-  // Rows are copied from HBM straight into the LDS tiles (global_load_lds):
-  // one instruction per row, ROW_LANES lanes of 16 bytes each (at D = 128
-  // the other lanes are masked off, so rows keep their padding). Each wave
-  // copies kRowsPerWave rows of a tile; the waits are explicit vmcnt values
-  // over this wave's own copies, and a barrier publishes the tile. Rows past
-  // r1 repeat the last valid row (finite data; their weights are zero).
-  const int ntiles = (r1 - r0 + kTile - 1) / kTile;
+  // Rows are copied from HBM straight into the LDS tiles (global_load_lds).
+  // Each wave copies kRowsPerWave rows of a tile; the waits are explicit
+  // vmcnt values over this wave's own copies, and a barrier publishes the
+  // tile. Rows past r1 repeat the last valid row (finite data; their weights
+  // are zero).
   auto dma = [&](int tile) {
     uint32_t* dst = Rbuf + (tile % kStages) * kTile * ROW_WORDS;
     const int t0 = r0 + tile * kTile;
@@ -169,13 +206,10 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   // of tile t+1 while it finishes tile t (exchange, softmax, PV), so the
   // matrix work of one overlaps the vector work of the other. kStages = 3
   // LDS tiles: t (PV), t+1 (S^T) and t+2 in flight.
-  static_assert(kStages == 3, "the waits below assume three tiles");
-  dma(0);
-  if (ntiles > 1) dma(1);
   // Tile 0 has landed once at most tile 1's copies are outstanding.
   if (ntiles > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRowsPerWave) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_barrier();  // tile 0 visible
+  lds_barrier();  // tile 0 and the row list visible
   f32x4 s0, s1;   // partial logits of the tile about to be finished
   partial_s(0, s0, s1);
   if (DSPLIT > 1) {
@@ -213,23 +247,31 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
 
     float z[8];
     float mx = -INFINITY;
+    if (t0 + kTile <= r1) {  // a full tile (uniform)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = (t0 + 4 * g + i < r1) ? c0[i] * scale : -INFINITY;
-      z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? c1[i] * scale : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        z[i] = c0[i] * scale2;
+        z[4 + i] = c1[i] * scale2;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = (t0 + 4 * g + i < r1) ? c0[i] * scale2 : -INFINITY;
+        z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? c1[i] * scale2 : -INFINITY;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescaling: the weights are taken relative to a reference mrun that
-    // only moves when a tile's maximum exceeds it by more than kRescale, so
-    // the weights stay below e^kRescale and the accumulators are rescaled
+    // only moves when a tile's maximum exceeds it by more than kRescale2, so
+    // the weights stay below 2^kRescale2 and the accumulators are rescaled
     // (for the whole wave at once) on few tiles only. The first tile always
     // sets the reference (mrun starts at -inf).
-    if (__ballot(mx > mrun + kRescale) != 0) {
+    if (__ballot(mx > mrun + kRescale2) != 0) {
       const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
-      const float alpha = __expf(mrun - mnew);
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
       mrun = mnew;
       lrun *= alpha;
 #pragma unroll
@@ -244,9 +286,13 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t pk = pack_bf16x2(__expf(z[2 * i] - mrun), __expf(z[2 * i + 1] - mrun));
-      // the sum uses the rounded weights the MFMA sees
-      psum += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xFFFF0000u);
+      const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(z[2 * i] - mrun),
+                                      __builtin_amdgcn_exp2f(z[2 * i + 1] - mrun));
+      // The sum uses the rounded weights the MFMA sees: a dot product of the
+      // packed pair with (1, 1).
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                             __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
       pw[i] = pk;
     }
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
@@ -309,7 +355,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     if (g == 0) {
       float* ml = part_ml + slot * 4;
       if (dh == 0) {
-        ml[0] = mrun;
+        ml[0] = mrun * kLn2;  // natural-log units for the combine
         ml[1] = l;
       }
       ml[2 + dh] = sc;

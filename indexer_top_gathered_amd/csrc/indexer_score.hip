@@ -7,23 +7,27 @@
 //
 // Per batch row this is a [H x 128] x [128 x N] product followed by a
 // weighted ReLU reduction over H, so it is streamed as MFMA tiles with the
-// heads as the M dimension and 16 keys as the N dimension. The key rows are
-// read straight from HBM into the B operand: lane 16g+m loads 16 contiguous
-// bytes of key m at channel 32*kk + 8g, so four lanes cover 64 contiguous
-// bytes of a row per instruction and every byte of k is read exactly once.
-// The query fragments and weights stay in registers for the whole sweep.
-// Each lane ends with four heads of one key; the head sum finishes with two
-// cross-lane steps. Summation order is fixed, so results are deterministic.
+// heads as the M dimension and 16 keys as the N dimension. An MFMA B operand
+// wants 16 different keys per 16 lanes (64 bytes of each per instruction);
+// loaded that way a key row costs twice the cache-line requests of a
+// contiguous read, which bounds the load rate. So keys are loaded in whole
+// 1 KB runs (4 keys per instruction, three steps in flight per wave), written
+// to a per-wave LDS area with each key's 16-byte chunks XOR-swizzled by the
+// key index, and read back in MFMA layout without bank conflicts. Every byte
+// of k is read from HBM exactly once. The query fragments and weights stay
+// in registers for the whole sweep. Each lane ends with four heads of one
+// key; the head sum finishes with two cross-lane steps. Summation order is
+// fixed, so results are deterministic.
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kIsWaves = 4;
+constexpr int kIsWaves = 8;
 constexpr int kIsThreads = kIsWaves * kWave;
 constexpr int kIsTiles = 2;                       // 16-key tiles per wave step
 constexpr int kIsKeysPerStep = 16 * kIsTiles;     // keys per wave per step
-constexpr int kIsKeysPerRound = kIsWaves * kIsKeysPerStep;  // 128 per workgroup round
+constexpr int kIsKeysPerRound = kIsWaves * kIsKeysPerStep;  // 256 per workgroup round
 constexpr int kDI = 128;
 
 template <int MT>  // MT = number of 16-head tiles (1..4)
@@ -65,20 +69,34 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
   const int start = blockIdx.x * keys_per_wg;
   const int end = min(N, start + keys_per_wg);
 
-  // Key fragments of one wave step: lane 16g+m holds key (key0 + 16t + m),
-  // channels 32*kk + 8g .. +8. Keys past N are clamped to N-1 (their columns
-  // are computed and never stored), so every load is unconditional.
-  auto load_keys = [&](bf16x8 (&kb)[kIsTiles][4], int key0) {
+  // Keys are loaded with whole 1 KB runs per instruction (4 keys x 256 B,
+  // lane l: key 4j + l/16, 16-byte chunk l%16), then written to this wave's
+  // LDS area with the chunk of key q at slot (chunk ^ q%16), so that the MFMA
+  // fragment reads (16 different keys, one chunk) hit 16 different slots.
+  __shared__ u32x4 stage_lds[kIsWaves][32 * 16];  // 8 KB per wave: 32 keys x 16 chunks
+  u32x4* st = stage_lds[wave];
+  auto load_step = [&](u32x4 (&r)[8], int key0) {
 #pragma unroll
-    for (int t = 0; t < kIsTiles; ++t) {
-      const int key = min(key0 + t * 16 + m, N - 1);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kb[t][kk] = __builtin_nontemporal_load(
-            reinterpret_cast<const bf16x8*>(krow + (size_t)key * kDI + kk * 32 + g * 8));
+    for (int j = 0; j < 8; ++j) {
+      const int key = min(key0 + 4 * j + (lane >> 4), N - 1);
+      r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (size_t)key * kDI) + (lane & 15));
     }
   };
-  auto score_step = [&](const bf16x8 (&kb)[kIsTiles][4], int key0) {
+  auto score_step = [&](const u32x4 (&r)[8], int key0) {
+    // stage: key q = 4j + lane/16, chunk c = lane%16 -> slot q*16 + (c ^ (q & 15))
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = 4 * j + (lane >> 4);
+      st[q * 16 + ((lane & 15) ^ (q & 15))] = r[j];
+    }
+    bf16x8 kb[kIsTiles][4];
+#pragma unroll
+    for (int t = 0; t < kIsTiles; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int q = 16 * t + m;
+        kb[t][kk] = __builtin_bit_cast(bf16x8, st[q * 16 + ((4 * kk + g) ^ m)]);
+      }
     f32x4 acc[kIsTiles][MT];
 #pragma unroll
     for (int t = 0; t < kIsTiles; ++t)
@@ -90,8 +108,6 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
       for (int t = 0; t < kIsTiles; ++t)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32(qa[mt][kk], kb[t][kk], acc[t][mt]);
-
-    // Weighted ReLU over this lane's heads, per key tile.
     float p[kIsTiles];
 #pragma unroll
     for (int t = 0; t < kIsTiles; ++t) {
@@ -102,9 +118,6 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
         for (int i = 0; i < 4; ++i) sum += wv[mt][i] * fmaxf(acc[t][mt][i], 0.0f);
       p[t] = sum;
     }
-    // Sum over the four lane groups. Lanes with even g keep tile 0, odd g
-    // keep tile 1: one exchange with g^1 hands over the other tile, one with
-    // g^2 completes the sum.
     float mine = (g & 1) ? p[1] : p[0];
     const float other = (g & 1) ? p[0] : p[1];
     mine += __shfl_xor(other, 16);
@@ -114,31 +127,22 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
       if (key < N) srow[key] = mine;
     }
   };
-
-  // Two key buffers in turn: the loads of the next step are in flight while
-  // this step is computed. Each load sits on a path where the compiler can
-  // see exactly which loads are outstanding, so a step waits only for its
-  // own buffer.
-  bf16x8 ka[kIsTiles][4], kb[kIsTiles][4];
+  // Three register buffers in turn: two steps of loads in flight while one
+  // step is staged and computed.
+  u32x4 ra[8], rb[8], rc[8];
   int key0 = start + wave * kIsKeysPerStep;
-  if (key0 < end) {
-    load_keys(ka, key0);
-    while (true) {
-      if (key0 + kIsKeysPerRound >= end) {
-        score_step(ka, key0);
-        break;
-      }
-      load_keys(kb, key0 + kIsKeysPerRound);
-      score_step(ka, key0);
-      key0 += kIsKeysPerRound;
-      if (key0 + kIsKeysPerRound >= end) {
-        score_step(kb, key0);
-        break;
-      }
-      load_keys(ka, key0 + kIsKeysPerRound);
-      score_step(kb, key0);
-      key0 += kIsKeysPerRound;
-    }
+  const int nsteps = key0 < end ? (end - key0 + kIsKeysPerRound - 1) / kIsKeysPerRound : 0;
+  if (nsteps > 0) load_step(ra, key0);
+  if (nsteps > 1) load_step(rb, key0 + kIsKeysPerRound);
+  for (int i = 0; i < nsteps; i += 3) {
+    if (i + 2 < nsteps) load_step(rc, key0 + (i + 2) * kIsKeysPerRound);
+    score_step(ra, key0 + i * kIsKeysPerRound);
+    if (i + 1 >= nsteps) break;
+    if (i + 3 < nsteps) load_step(ra, key0 + (i + 3) * kIsKeysPerRound);
+    score_step(rb, key0 + (i + 1) * kIsKeysPerRound);
+    if (i + 2 >= nsteps) break;
+    if (i + 4 < nsteps) load_step(rb, key0 + (i + 4) * kIsKeysPerRound);
+    score_step(rc, key0 + (i + 2) * kIsKeysPerRound);
   }
 }
 
@@ -149,7 +153,7 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
   // Each wave keeps its query fragments (up to 16 KB per batch row) in
   // registers for its whole sweep. Aim for one round of about 256 workgroups
   // (one per CU measured fastest), each sweeping at least 8 and at most 32
-  // rounds of 128 keys so the query loads stay small next to the key stream.
+  // rounds of 256 keys so the query loads stay small next to the key stream.
   const long long per_row_rounds = (N + kIsKeysPerRound - 1) / kIsKeysPerRound;
   long long rounds = ((long long)B * per_row_rounds + 255) / 256;
   if (rounds < 8) rounds = 8;

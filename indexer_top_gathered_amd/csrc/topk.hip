@@ -798,32 +798,34 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index) {
   extern __shared__ uint32_t pos_lds[];  // k positions (sorted path)
   __shared__ Scratch sc;
-  __shared__ uint32_t seg_cnt[64];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   const int slots = 2 * k;  // per segment
-  if (tid < segs) seg_cnt[tid] = min((uint32_t)slots, cnt_in[(size_t)b * segs + tid]);
+  // Every slot of the row at once: slot q = tid + j*512 is entry q % slots
+  // of segment q / slots, valid below that segment's count. All loads, the
+  // counts included, are issued unconditionally (clamped into the row's
+  // slots, which lie inside the workspace) so they overlap; validity is
+  // applied after.
+  const uint64_t* src = cand_in + (size_t)b * segs * slots;
+  const int nslots = segs * slots;
+  uint64_t v[kPer];
+  uint32_t c[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = min(tid + j * kMergeThreads, nslots - 1);
+    v[j] = src[q];
+    c[j] = cnt_in[(size_t)b * segs + q / slots];
+  }
   for (int i = tid; i < kHBins; i += kMergeThreads) {
     sc.hist[0][i] = 0;
     sc.hist[1][i] = 0;
   }
   if (tid == 0) sc.n_app = 0;
-  lds_barrier();
-  // Every slot of the row at once: slot q = tid + j*512 is entry q % slots
-  // of segment q / slots, valid below that segment's count.
-  const uint64_t* src = cand_in + (size_t)b * segs * slots;
-  // All loads are issued unconditionally (clamped into the row's slots, which
-  // lie inside the workspace) so they overlap; validity is applied after.
-  uint64_t v[kPer];
   uint32_t nvalid = 0;
-  const int nslots = segs * slots;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) v[j] = src[min(tid + j * kMergeThreads, nslots - 1)];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int q = tid + j * kMergeThreads;
-    const int s = q / slots;
-    const bool ok = q < nslots && (uint32_t)(q - s * slots) < seg_cnt[min(s, segs - 1)];
+    const bool ok = q < nslots && (uint32_t)(q % slots) < min((uint32_t)slots, c[j]);
     v[j] = ok ? v[j] : 0;
     nvalid += ok ? 1u : 0u;
   }

@@ -63,14 +63,18 @@ def indexer_bytes(s) -> int:
     return b * s.N * s.D_I * 2 + b * s.H_I * s.D_I * 2 + b * s.H_I * 4 + b * s.N * 4
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str):
+def traffic_from_profile(kernel_srcs):
     """HBM bytes per launch recorded by the rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    were taken on the current kernel sources (the kernel's file and the
+    internal header it includes); else None."""
     path = os.path.join(ROOT, "profiles", "indexer_score_decode_step_counters.md")
     if not os.path.exists(path):
         return None
@@ -79,7 +83,7 @@ def traffic_from_profile(kernel_src: str):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha256_16") != source_digest(kernel_src):
+    if vals.get("kernel_source_sha256_16") != source_digest(kernel_srcs):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -144,8 +148,9 @@ def main():
     is_us = e0.elapsed_time(e1) * 1e3 / args.steps
     is_bytes = indexer_bytes(s)
     achieved = is_bytes / (is_us * 1e-6) / 1e9
-    traffic = traffic_from_profile(os.path.join(ROOT, "indexer_top_gathered_amd", "csrc",
-                                                "indexer_score.hip"))
+    csrc = os.path.join(ROOT, "indexer_top_gathered_amd", "csrc")
+    traffic = traffic_from_profile([os.path.join(csrc, "indexer_score.hip"),
+                                    os.path.join(csrc, "dsa_internal.h")])
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "kernel": "indexer_score_kernel<4>",

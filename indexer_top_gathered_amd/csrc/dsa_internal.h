@@ -102,6 +102,21 @@ __device__ __forceinline__ uint64_t wave_reduce64(uint64_t x) {
   return r;
 }
 
+// The value of lane l ^ 16 (or l ^ 32) through v_permlane16_swap /
+// v_permlane32_swap: plain VALU instructions, where __shfl_xor would be a
+// ds_bpermute that waits in the LDS queue behind every outstanding LDS read.
+// With both operands x, the swap returns (x of the lower lane, x of the
+// upper lane) of each pair in every lane of the pair. Blocks are
+// one-dimensional, so the lane is threadIdx.x mod 64.
+__device__ __forceinline__ float lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // ---------------------------------------------------------------- MFMA
 // v_mfma_f32_16x16x32_bf16. Lane l = 16*g + m supplies A[m][8g..8g+7] and
 // B[8g..8g+7][m]; it receives D[4g+i][m] for i < 4.

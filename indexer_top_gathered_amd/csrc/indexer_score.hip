@@ -120,8 +120,8 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
     }
     float mine = (g & 1) ? p[1] : p[0];
     const float other = (g & 1) ? p[0] : p[1];
-    mine += __shfl_xor(other, 16);
-    mine += __shfl_xor(mine, 32);
+    mine += lane_xor16(other);
+    mine += lane_xor32(mine);
     if (g < 2) {
       const int key = key0 + g * 16 + m;
       if (key < N) srow[key] = mine;

@@ -383,62 +383,68 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials: one workgroup per (batch, head),
-// each thread owns 4 dims. Splits are taken 8 at a time with every load of
-// a chunk issued before any is used (indices past the last split are
-// clamped and weighted zero), so a chunk costs one memory latency.
+// Log-sum-exp merge of the split partials. A head's D dims are taken by D/8
+// threads, 8 dims (16 bytes of fp16) each, and a workgroup of 256 threads
+// takes 256/(D/8) heads of one batch row. Splits are taken 8 at a time with
+// every load of a chunk issued before any is used (indices past the last
+// split are clamped and weighted zero), so a chunk costs one memory latency.
 template <int D>
-__global__ __launch_bounds__(D / 4) void attend_combine_kernel(
+__global__ __launch_bounds__(256) void attend_combine_kernel(
     const uint16_t* __restrict__ part_o, const float4* __restrict__ part_ml,
     uint16_t* __restrict__ out, int Hq, int splits, int nitems) {
+  constexpr int TPH = D / 8;      // threads per head
+  constexpr int HPW = 256 / TPH;  // heads per workgroup (divides Hq, a multiple of 16)
   constexpr int SC = 8;
   // The same XCD placement as the attention kernel: batch row b is merged on
   // the XCD whose L2 holds its partials.
   const int wg = blockIdx.x;
-  const int bh = (wg % 8) * (int)(gridDim.x / 8) + wg / 8;
-  if (bh >= nitems) return;  // padding workgroup (uniform)
+  const int item = (wg % 8) * (int)(gridDim.x / 8) + wg / 8;
+  if (item >= nitems) return;  // padding workgroup (uniform)
+  const int bh = item * HPW + (int)threadIdx.x / TPH;
   const int b = bh / Hq;
   const int h = bh % Hq;
-  const int d = threadIdx.x * 4;
+  const int d = ((int)threadIdx.x % TPH) * 8;
   const bool upper = d >= D / 2;  // which scale covers these dims
   const size_t base = (size_t)b * splits * Hq + h;  // slot of split 0
   float M = -INFINITY, L = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
   for (int s0 = 0; s0 < splits; s0 += SC) {
     float4 ml[SC];
-    uint2 v[SC];
+    u32x4 v[SC];
 #pragma unroll
     for (int j = 0; j < SC; ++j) {
       const size_t slot = base + (size_t)min(s0 + j, splits - 1) * Hq;
       ml[j] = part_ml[slot];
-      v[j] = *reinterpret_cast<const uint2*>(part_o + slot * D + d);
+      v[j] = *reinterpret_cast<const u32x4*>(part_o + slot * D + d);
     }
     float Mc = M;
 #pragma unroll
     for (int j = 0; j < SC; ++j) Mc = fmaxf(Mc, ml[j].x);
     const float r = __expf(M - Mc);  // 0 on the first chunk (M = -inf)
     L *= r;
-    acc.x *= r;
-    acc.y *= r;
-    acc.z *= r;
-    acc.w *= r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= r;
 #pragma unroll
     for (int j = 0; j < SC; ++j) {
       const float f = (s0 + j < splits) ? __expf(ml[j].x - Mc) : 0.0f;
       L += ml[j].y * f;
       const float fs = f * (upper ? ml[j].w : ml[j].z);
-      const float2 a = unpack_f16x2(v[j].x), c = unpack_f16x2(v[j].y);
-      acc.x += a.x * fs;
-      acc.y += a.y * fs;
-      acc.z += c.x * fs;
-      acc.w += c.y * fs;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float2 a = unpack_f16x2(v[j][q]);
+        acc[2 * q] += a.x * fs;
+        acc[2 * q + 1] += a.y * fs;
+      }
     }
     M = Mc;
   }
   const float inv = 1.0f / L;
-  const uint32_t lo = pack_bf16x2(acc.x * inv, acc.y * inv);
-  const uint32_t hi = pack_bf16x2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(out + ((size_t)b * Hq + h) * D + d) = make_uint2(lo, hi);
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
+  *reinterpret_cast<u32x4*>(out + ((size_t)b * Hq + h) * D + d) = o;
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -510,13 +516,14 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
   }
   if (e != hipSuccess || p.splits == 1) return e;
   const int Hq = d.q_heads;
-  const int nitems = d.batch * Hq;
+  const int hpw = 256 / (d.head_dim / 8);  // heads per combine workgroup
+  const int nitems = d.batch * Hq / hpw;
   const int grid = (nitems + 7) / 8 * 8;
   if (d.head_dim == 512)
-    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(grid), dim3(128), 0, st, po,
+    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(grid), dim3(256), 0, st, po,
                        reinterpret_cast<const float4*>(pml), out, Hq, p.splits, nitems);
   else
-    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(grid), dim3(32), 0, st, po,
+    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(grid), dim3(256), 0, st, po,
                        reinterpret_cast<const float4*>(pml), out, Hq, p.splits, nitems);
   return hipGetLastError();
 }

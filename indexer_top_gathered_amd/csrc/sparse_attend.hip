@@ -85,16 +85,9 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   const int m = lane & 15;
   const int g = lane >> 4;
   // Wave (hq, dh): 16 heads, and the dh-th 1/DSPLIT of the dims for the
-  // query fragments and the output accumulators. The waves of a workgroup
-  // are spread over the 4 SIMDs round robin (wave w on SIMD w % 4), so with
-  // 8 waves SIMD s runs waves s and s+4: head groups hq and hq + HG/2.
-  const int hq = wave / DSPLIT;
-  const int dh = wave % DSPLIT;
-  // The two waves that share a SIMD take the phases of a tile in opposite
-  // orders (logits of the next tile first, or softmax and PV of this tile
-  // first), so that one's LDS reads overlap the other's vector and matrix
-  // work instead of both waiting on the same unit at once.
-  const bool late = WAVES >= 8 && hq >= HG / 2;
+  // query fragments and the output accumulators.
+  const int hq = wave % HG;
+  const int dh = wave / HG;
   const int h = hg * HW + hq * 16 + m;  // the head this lane owns
   const int dbase = dh * DW;
   const int rows = k + W;
@@ -237,103 +230,91 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       // The two waves of a head group each hold half of the dot products;
       // each adds the other's half. Both form the same sums (addition is
       // commutative), so they run identical softmax states.
-      const int partner = hq * DSPLIT + (DSPLIT - 1 - dh);
+      const int partner = (DSPLIT - 1 - dh) * HG + hq;
       const f32x4* xb = xbuf + ((t & 1) * WAVES + partner) * 2 * kWave;
       s0 += xb[lane];
       s1 += xb[kWave + lane];
     }
     const f32x4 c0 = s0, c1 = s1;  // logits of tile t
-    // Partial logits of tile t+1 (published by the next barrier).
-    auto next_logits = [&]() {
-      if (t + 1 < ntiles) {
-        partial_s(t + 1, s0, s1);
-        if (DSPLIT > 1) {
-          f32x4* xw = xbuf + (((t + 1) & 1) * WAVES + wave) * 2 * kWave;
-          xw[lane] = s0;
-          xw[kWave + lane] = s1;
-        }
+    if (t + 1 < ntiles) {
+      partial_s(t + 1, s0, s1);
+      if (DSPLIT > 1) {
+        f32x4* xw = xbuf + (((t + 1) & 1) * WAVES + wave) * 2 * kWave;
+        xw[lane] = s0;
+        xw[kWave + lane] = s1;
       }
-    };
-    // Softmax of tile t and O^T += R^T P^T.
-    auto finish = [&]() {
-      float z[8];
-      float mx = -INFINITY;
-      if (t0 + kTile <= r1) {  // a full tile (uniform)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          z[i] = c0[i] * scale2;
-          z[4 + i] = c1[i] * scale2;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          z[i] = (t0 + 4 * g + i < r1) ? c0[i] * scale2 : -INFINITY;
-          z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? c1[i] * scale2 : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
-      mx = fmaxf(mx, lane_xor16(mx));
-      mx = fmaxf(mx, lane_xor32(mx));
-      // Lazy rescaling: the weights are taken relative to a reference mrun that
-      // only moves when a tile's maximum exceeds it by more than kRescale2, so
-      // the weights stay below 2^kRescale2 and the accumulators are rescaled
-      // (for the whole wave at once) on few tiles only. The first tile always
-      // sets the reference (mrun starts at -inf).
-      if (__ballot(mx > mrun + kRescale2) != 0) {
-        const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
-        const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
-        mrun = mnew;
-        lrun *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) {
-          o[dt][0] *= alpha;
-          o[dt][1] *= alpha;
-          o[dt][2] *= alpha;
-          o[dt][3] *= alpha;
-        }
-      }
-      u32x4 pw;
-      float psum = 0.0f;
+    }
+
+    float z[8];
+    float mx = -INFINITY;
+    if (t0 + kTile <= r1) {  // a full tile (uniform)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(z[2 * i] - mrun),
-                                        __builtin_amdgcn_exp2f(z[2 * i + 1] - mrun));
-        // The sum uses the rounded weights the MFMA sees: a dot product of the
-        // packed pair with (1, 1).
-        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
-                                               __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
-        pw[i] = pk;
+        z[i] = c0[i] * scale2;
+        z[4 + i] = c1[i] * scale2;
       }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-      lrun += psum;
-
-      // O^T += R^T P^T over this wave's dims. Within each 16-lane group, lane
-      // j points at row (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4)
-      // .. +4; the transposing read hands lane j the 4 rows at dim 16*dt + j.
-      const uint32_t* R = Rbuf + (t % kStages) * kTile * ROW_WORDS;
-      const int ra = 4 * g + (m >> 2);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = (t0 + 4 * g + i < r1) ? c0[i] * scale2 : -INFINITY;
+        z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? c1[i] * scale2 : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
+    mx = fmaxf(mx, lane_xor16(mx));
+    mx = fmaxf(mx, lane_xor32(mx));
+    // Lazy rescaling: the weights are taken relative to a reference mrun that
+    // only moves when a tile's maximum exceeds it by more than kRescale2, so
+    // the weights stay below 2^kRescale2 and the accumulators are rescaled
+    // (for the whole wave at once) on few tiles only. The first tile always
+    // sets the reference (mrun starts at -inf).
+    if (__ballot(mx > mrun + kRescale2) != 0) {
+      const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      mrun = mnew;
+      lrun *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt) {
-        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-        const int col = (dbase >> 1) + dt * 8 + 2 * (m & 3);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(&R[ra * ROW_WORDS + col]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(&R[(16 + ra) * ROW_WORDS + col]));
-        // Concatenate as whole vectors (element-wise inserts of bit-cast
-        // halves were folded into copies of element 0 by the compiler).
-        const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, cat), pb, o[dt]);
+        o[dt][0] *= alpha;
+        o[dt][1] *= alpha;
+        o[dt][2] *= alpha;
+        o[dt][3] *= alpha;
       }
-    };
-    if (late) {
-      finish();
-      next_logits();
-    } else {
-      next_logits();
-      finish();
+    }
+    u32x4 pw;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pk = pack_bf16x2(__builtin_amdgcn_exp2f(z[2 * i] - mrun),
+                                      __builtin_amdgcn_exp2f(z[2 * i + 1] - mrun));
+      // The sum uses the rounded weights the MFMA sees: a dot product of the
+      // packed pair with (1, 1).
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                             __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+      pw[i] = pk;
+    }
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    lrun += psum;
+
+    // O^T += R^T P^T over this wave's dims. Within each 16-lane group, lane
+    // j points at row (4g + j/4) [then 16 + 4g + j/4], dims 16*dt + 4*(j%4)
+    // .. +4; the transposing read hands lane j the 4 rows at dim 16*dt + j.
+    const uint32_t* R = Rbuf + (t % kStages) * kTile * ROW_WORDS;
+    const int ra = 4 * g + (m >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) {
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const int col = (dbase >> 1) + dt * 8 + 2 * (m & 3);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(&R[ra * ROW_WORDS + col]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(&R[(16 + ra) * ROW_WORDS + col]));
+      // Concatenate as whole vectors (element-wise inserts of bit-cast
+      // halves were folded into copies of element 0 by the compiler).
+      const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, cat), pb, o[dt]);
     }
   }
 

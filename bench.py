@@ -16,6 +16,12 @@ by the time per step), `us_per_step` the time per step, `roofline` the
 dominant kernel (indexer scoring) measured with HIP events on the stream it
 runs on, `topk` the top-k-only workload (bf16 64 x 131072, k=512), and
 `cpu_baseline` the CPU oracle timed on this host.
+
+`--workload` times one of the other workloads instead (for profiling; one
+JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
+`topk-sampling` (float32 128 x 129280, k=1024, values), `topk-stress`
+(quantised rows, half sorted, 64 x 262144, k=2048, bf16 and float32) or
+`stress-step` (B=64, N=262144, k=2048, scores equal to the stress rows).
 """
 from __future__ import annotations
 
@@ -43,6 +49,8 @@ def parse():
     p.add_argument("--no-topk", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for counter calibration)")
+    p.add_argument("--workload", default="step",
+                   choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step"])
     return p.parse_args()
 
 
@@ -54,6 +62,105 @@ def step_bytes(s) -> int:
             + b * s.H_q * s.D * 2                                            # q
             + b * (s.k + s.W) * s.D * 2                                      # gathered rows + window
             + b * s.H_q * s.D * 2)                                           # output
+
+
+def step_roofline_us(s) -> float:
+    """Serial stages, each at the larger of its HBM time (compulsory bytes at
+    8 TB/s) and its MFMA time (bf16 flops at 2.5 PFLOP/s)."""
+    b = s.B
+    is_bytes = b * s.H_I * s.D_I * 2 + b * s.N * s.D_I * 2 + b * s.H_I * 4
+    is_flops = 2 * b * s.N * s.H_I * s.D_I
+    sa_bytes = step_bytes(s) - is_bytes
+    sa_flops = 4 * b * s.H_q * (s.k + s.W) * s.D
+    peak_flops = 2.5e15
+    return 1e6 * (max(is_bytes / (HBM_PEAK_GBPS * 1e9), is_flops / peak_flops)
+                  + max(sa_bytes / (HBM_PEAK_GBPS * 1e9), sa_flops / peak_flops))
+
+
+def time_calls(fn, n_warm, n_timed, stream):
+    """Mean µs per call of fn(i) over n_timed back-to-back calls on stream."""
+    import torch
+    for i in range(n_warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n_timed):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n_timed
+
+
+def other_workload(args):
+    """One JSON line for a workload other than the production step."""
+    import torch
+    import workloads
+    import indexer_top_gathered_amd as dsa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    line = {"workload": args.workload, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "data": "synthetic", "unit": "GB/s", "higher_is_better": True}
+    if args.workload in ("tiny-step", "stress-step"):
+        s = workloads.C1 if args.workload == "tiny-step" else workloads.C5
+        one = step_bytes(s)
+        # Enough copies to exceed 1 GB (the stress step's one copy is ~21 GB).
+        R = max(1, min(256, -(-(1 << 30) // one)))
+        if args.workload == "tiny-step":
+            copies = [workloads.step_inputs(s, 1000 + 10 * r, device=dev) for r in range(R)]
+        else:
+            copies = [workloads.stress_step_inputs(s, 5000 + 10 * r, device=dev) for r in range(R)]
+        dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
+        ws = torch.empty(dsa.dsa_decode_step_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        out = torch.empty((s.B, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+
+        def call(i):
+            c = copies[i % R]
+            dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"], c["kv_win"],
+                                s.k, s.scale, out=out, ws=ws, stream=stream)
+        us = time_calls(call, args.warmup, args.steps, stream)
+        roof = step_roofline_us(s)
+        line.update({"us_per_step": round(us, 2), "value": round(one / (us * 1e-6) / 1e9, 1),
+                     "compulsory_bytes": one, "roofline_us": round(roof, 3),
+                     "frac_of_roofline": round(roof / us, 4), "rotating_input_copies": R,
+                     "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
+                                "W": s.W, "H_q": s.H_q, "D": s.D}})
+        print(json.dumps(line), flush=True)
+        return
+    # Top-k workloads.
+    if args.workload == "topk-sampling":
+        t = workloads.C3
+        cases = [("f32", lambda r: workloads.sampling_rows(t.B, t.N, 3006 + r, device=dev))]
+    else:
+        t = workloads.C5_TOPK
+        cases = [(dt, (lambda r, dt=dt: workloads.stress_levels(t.B, t.N, 5008 + r, device=dev, dtype=dt)))
+                 for dt in ("bf16", "f32")]
+    results = []
+    for dt, make in cases:
+        esz = 2 if dt == "bf16" else 4
+        tbytes = t.B * t.N * esz + t.B * t.k * 4 + (t.B * t.k * esz if t.values else 0)
+        R = max(1, -(-(1 << 30) // (t.B * t.N * esz)))
+        rows = [make(r) for r in range(R)]
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        tws = torch.empty(dsa.dsa_topk_workspace_bytes(t.B, t.N, t.k, tdt), dtype=torch.uint8,
+                          device=dev)
+        oidx = torch.empty((t.B, t.k), dtype=torch.int32, device=dev)
+        oval = torch.empty((t.B, t.k), dtype=tdt, device=dev) if t.values else None
+
+        def call(i):
+            dsa.dsa_topk(rows[i % R], t.k, out_idx=oidx, out_val=oval, ws=tws, stream=stream)
+        us = time_calls(call, args.warmup, args.steps, stream)
+        gbps = tbytes / (us * 1e-6) / 1e9
+        results.append({"dtype": dt, "us": round(us, 2), "effective_GBps": round(gbps, 1),
+                        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                        "compulsory_bytes": tbytes, "rotating_input_copies": R})
+        del rows
+    line.update({"value": results[0]["effective_GBps"], "results": results,
+                 "config": {"B": t.B, "N": t.N, "k": t.k, "values": t.values}})
+    print(json.dumps(line), flush=True)
 
 
 def indexer_bytes(s) -> int:
@@ -98,6 +205,9 @@ def main():
               "(batch rows are independent, so N GPUs would each run this same kernel set "
               "on B/N rows).", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "step":
+        other_workload(args)
+        return
     import torch
     import workloads
     import indexer_top_gathered_amd as dsa

@@ -352,16 +352,22 @@ __device__ __forceinline__ uint32_t elem_rawkey(const u32x4& kv, int e) {
   return kv[e];
 }
 
-// One thread's vector at row position p0, as keys. Padding past `end` gets
-// key 0.
+// One thread's vector of raw scores at row position p0, wholly inside the
+// row and 16-byte aligned.
+template <bool BF16>
+__device__ __forceinline__ u32x4 load_raw_full(const void* row, int64_t p0) {
+  const u32x4* src = BF16 ? reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(row) + p0)
+                          : reinterpret_cast<const u32x4*>(reinterpret_cast<const uint32_t*>(row) + p0);
+  return __builtin_nontemporal_load(src);
+}
+// The same for any vector: positions past `end` get the padding pattern
+// (all ones), whose key is 0.
 template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ u32x4 load_keys(const void* row, int64_t p0, int64_t end) {
+__device__ __forceinline__ u32x4 load_raw(const void* row, int64_t p0, int64_t end) {
   constexpr int E = BF16 ? 8 : 4;
   u32x4 r;
   if (ALIGNED && p0 + E <= end) {
-    const u32x4* src = BF16 ? reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(row) + p0)
-                            : reinterpret_cast<const u32x4*>(reinterpret_cast<const uint32_t*>(row) + p0);
-    r = __builtin_nontemporal_load(src);
+    r = load_raw_full<BF16>(row, p0);
   } else {
     r = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
@@ -376,9 +382,13 @@ __device__ __forceinline__ u32x4 load_keys(const void* row, int64_t p0, int64_t 
       }
     }
   }
+  return r;
+}
+// Raw scores -> order keys, in place.
+template <bool BF16>
+__device__ __forceinline__ void to_keys(u32x4& r) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) r[j] = BF16 ? bf16_pair_keys(r[j]) : f32_raw_key(r[j]);
-  return r;
 }
 
 // From below: a T with at least K of the G group maxima per thread (raw
@@ -578,75 +588,112 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   // from its group maxima and is cut to its exact top k; later blocks are
   // only filtered against that k-th composite (which every later winner must
   // beat), and the next block's loads are in flight while one is filtered.
+  //
+  // A block wholly inside the segment (all but possibly the last) is read
+  // by straight-line 16-byte loads, so all of them are in flight before the
+  // first is used; scores become keys only when the block is taken up.
   u32x4 kv[V], kn[V];
+  if (ALIGNED && seg_start + kBlock <= seg_end) {  // uniform
 #pragma unroll
-  for (int v = 0; v < V; ++v)
-    kv[v] = load_keys<BF16, ALIGNED>(row, seg_start + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+    for (int v = 0; v < V; ++v) kv[v] = load_raw_full<BF16>(row, seg_start + ((int64_t)v * THREADS + threadIdx.x) * E);
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      kv[v] = load_raw<BF16, ALIGNED>(row, seg_start + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+  }
   for (int64_t base = seg_start; base < seg_end; base += kBlock) {
-    if (base + kBlock < seg_end) {
+    const int64_t nb = base + kBlock;
+    if (ALIGNED && nb + kBlock <= seg_end) {  // uniform
+#pragma unroll
+      for (int v = 0; v < V; ++v) kn[v] = load_raw_full<BF16>(row, nb + ((int64_t)v * THREADS + threadIdx.x) * E);
+    } else if (nb < seg_end) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        kn[v] = load_keys<BF16, ALIGNED>(row, base + kBlock + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+        kn[v] = load_raw<BF16, ALIGNED>(row, nb + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
     }
+#pragma unroll
+    for (int v = 0; v < V; ++v) to_keys<BF16>(kv[v]);
+    // A threshold from this block's group maxima (raw keys): at least k
+    // scores of the block, hence of the segment, are >= it. A group is
+    // element e of every vector of this thread.
+    auto block_threshold = [&]() __attribute__((always_inline)) -> uint32_t {
+      uint32_t g[E];
+      if (BF16) {
+        uint32_t m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = kv[0][j];
+#pragma unroll
+        for (int v = 1; v < V; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], kv[v][j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          g[2 * j] = m[j] & 0xFFFFu;
+          g[2 * j + 1] = m[j] >> 16;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          g[e] = kv[0][e];
+#pragma unroll
+          for (int v = 1; v < V; ++v) g[e] = max(g[e], kv[v][e]);
+        }
+      }
+      // About 2k groups: fewer, larger groups cost fewer histogram atomics
+      // and still leave a threshold near the k-th largest score. Fold the E
+      // maxima per thread in halves (a zero slot means "no group") while
+      // half of them still give 2k groups.
+      const int gpt = (2 * k + THREADS - 1) / THREADS;  // wanted groups per thread
+#pragma unroll
+      for (int half = E / 2; half >= 1; half /= 2) {
+        if (gpt <= half) {  // uniform
+#pragma unroll
+          for (int j = 0; j < half; ++j) {
+            g[j] = max(g[j], g[j + half]);
+            g[j + half] = 0;
+          }
+        }
+      }
+      uint32_t t = group_threshold<THREADS, E>(g, k, sc);
+      // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
+      if (t == (BF16 ? 0x8000u : 0x80000000u)) t -= 1;
+      return t;
+    };
+    auto admit_block = [&](uint32_t t) __attribute__((always_inline)) -> uint64_t {
+      uint64_t a = 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        a |= (uint64_t)admit_vector<BF16>(kv[v], t, false, thr,
+                                          base + ((int64_t)v * THREADS + threadIdx.x) * E)
+             << (v * E);
+      return a;
+    };
     uint32_t t0;
     if (have_thr) {
       // Raw-key bound of the k-th composite for the vector test.
       const uint32_t key32 = (uint32_t)(thr >> 32);
       t0 = BF16 ? (key32 >> 16) : key32;
+      if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
     } else {
-    // Group maxima (raw keys): element e of every vector of this thread.
-    uint32_t g[E];
-    if (BF16) {
-      uint32_t m[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m[j] = kv[0][j];
-#pragma unroll
-      for (int v = 1; v < V; ++v)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], kv[v][j]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        g[2 * j] = m[j] & 0xFFFFu;
-        g[2 * j + 1] = m[j] >> 16;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        g[e] = kv[0][e];
-#pragma unroll
-        for (int v = 1; v < V; ++v) g[e] = max(g[e], kv[v][e]);
-      }
+      t0 = block_threshold();
     }
-    // About 2k groups: fewer, larger groups cost fewer histogram atomics and
-    // still leave a threshold near the k-th largest score. Fold the E maxima
-    // per thread in halves (a zero slot means "no group") while half of them
-    // still give 2k groups.
-    const int gpt = (2 * k + THREADS - 1) / THREADS;  // wanted groups per thread
-#pragma unroll
-    for (int half = E / 2; half >= 1; half /= 2) {
-      if (gpt <= half) {  // uniform
-#pragma unroll
-        for (int j = 0; j < half; ++j) {
-          g[j] = max(g[j], g[j + half]);
-          g[j + half] = 0;
-        }
-      }
-    }
-    t0 = group_threshold<THREADS, E>(g, k, sc);
-    }
-    // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
-    if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
     // Admission: raw key >= t0. Once an exact threshold exists, t0 is its
     // value key, so ties at that value are admitted too (harmless extra
     // candidates; the position test is left to the overflow path below).
-    uint64_t adm = 0;
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      adm |= (uint64_t)admit_vector<BF16>(kv[v], t0, false, thr,
-                                          base + ((int64_t)v * THREADS + threadIdx.x) * E)
-             << (v * E);
+    uint64_t adm = admit_block(t0);
     uint32_t total;
-    const uint32_t excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
+    uint32_t excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
+    if (__builtin_expect(have_thr && cnt + (int)total > CAP, 0)) {
+      // A later block that beats the running threshold almost everywhere
+      // (a row rising along the segment): its own group maxima give a
+      // higher bound, and the segment's k-th largest is at least that.
+      const uint32_t t2 = block_threshold();
+      if (t2 > t0) {  // uniform
+        t0 = t2;
+        adm = admit_block(t0);
+        excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
+      }
+    }
     if (!FUSED && base == seg_start && base + kBlock >= seg_end && (int)total <= 2 * k) {
       // The whole segment in one block and its survivors fit the output
       // slots: write them straight to the workspace.

@@ -583,6 +583,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   int cnt = 0;
   bool have_thr = false;
   uint64_t thr = 0;  // once set: admit only composites > thr
+  uint32_t t_floor = 0;  // raw key that the segment's k-th largest is known to reach
 
   // Register blocks of THREADS*V*E scores. The first block sets a threshold
   // from its group maxima and is cut to its exact top k; later blocks are
@@ -674,6 +675,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       const uint32_t key32 = (uint32_t)(thr >> 32);
       t0 = BF16 ? (key32 >> 16) : key32;
       if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
+      t0 = max(t0, t_floor);
     } else {
       t0 = block_threshold();
     }
@@ -687,11 +689,16 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       // A later block that beats the running threshold almost everywhere
       // (a row rising along the segment): its own group maxima give a
       // higher bound, and the segment's k-th largest is at least that.
+      // Listed candidates below it can go, and later blocks are held to it.
       const uint32_t t2 = block_threshold();
       if (t2 > t0) {  // uniform
         t0 = t2;
+        t_floor = t2;
         adm = admit_block(t0);
         excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
+        lds_barrier();  // every thread has read the scan's totals
+        const uint32_t vk = BF16 ? key32_of_key16(canon16(t2)) : canon32(t2);
+        cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, (uint64_t)vk << 32, sc);
       }
     }
     if (!FUSED && base == seg_start && base + kBlock >= seg_end && (int)total <= 2 * k) {

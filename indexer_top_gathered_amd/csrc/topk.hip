@@ -179,15 +179,16 @@ __device__ void bucket_range(const uint64_t* buf, int cnt, uint64_t& lo, uint64_
   hi = z;
 }
 
-// Exact: the T for which exactly K of the distinct entries buf[0..cnt) are
-// >= T (1 <= K <= cnt). Each round splits the entries' actual [lo, hi] into
-// 1024 equal buckets, keeps the bucket holding the K-th largest, and then
-// shrinks [lo, hi] to the entries inside that bucket. Expects both hist
-// halves clear behind a barrier and leaves them clear.
+// Exact: the T for which exactly K of the distinct entries of buf[0..cnt)
+// inside [lo, hi] (all of them by default) are >= T (1 <= K <= their
+// number). Each round splits the entries' actual range into 1024 equal
+// buckets, keeps the bucket holding the K-th largest, and then shrinks the
+// range to the entries inside that bucket. Expects both hist halves clear
+// behind a barrier and leaves them clear.
 template <int THREADS>
-__device__ __forceinline__ uint64_t select_exact(const uint64_t* buf, int cnt, int K, Scratch& sc) {
+__device__ __forceinline__ uint64_t select_exact(const uint64_t* buf, int cnt, int K, Scratch& sc,
+                                                 uint64_t lo = 0, uint64_t hi = ~(uint64_t)0) {
   const int tid = threadIdx.x;
-  uint64_t lo = 0, hi = ~(uint64_t)0;
   bucket_range<THREADS>(buf, cnt, lo, hi, sc);
   uint32_t need = (uint32_t)K;
   uint64_t result = lo;
@@ -253,9 +254,9 @@ __device__ void regs_range(const uint64_t (&v)[PER], uint64_t& lo, uint64_t& hi,
 }
 
 template <int THREADS, int PER>
-__device__ uint64_t select_exact_regs(const uint64_t (&v)[PER], int K, Scratch& sc) {
+__device__ uint64_t select_exact_regs(const uint64_t (&v)[PER], int K, Scratch& sc,
+                                      uint64_t lo = 1, uint64_t hi = ~(uint64_t)0) {
   const int tid = threadIdx.x;
-  uint64_t lo = 1, hi = ~(uint64_t)0;
   regs_range<THREADS, PER>(v, lo, hi, sc);
   uint32_t need = (uint32_t)K;
   uint64_t result = lo;
@@ -546,8 +547,11 @@ __device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int 
     lds_barrier();
     return sc.pick;
   }
+  // A heavy bucket (many ties): the K-th largest is the need-th largest of
+  // the bucket's own entries, so the exact select starts from the bucket.
   for (int i = tid; i < kHBins; i += THREADS) h[i] = 0;  // ordered by the next barrier
-  return select_exact<THREADS>(buf, cnt, K, sc);
+  const uint64_t bhi = min((uint64_t)hi, (uint64_t)blo + (((uint64_t)1 << shift) - 1));
+  return select_exact<THREADS>(buf, cnt, (int)need, sc, (uint64_t)blo << 32, (bhi << 32) | 0xFFFFFFFFull);
 }
 
 // FUSED (one segment covering the whole row): after stage 1 the workgroup
@@ -950,8 +954,11 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       lds_barrier();
       thr = sc.pick;
     } else {
+      // Heavy bucket: start the exact select from its own entries.
       for (int i = tid; i < kHBins; i += kMergeThreads) h[i] = 0;  // ordered by the next barrier
-      thr = select_exact_regs<kMergeThreads, kPer>(v, k, sc);
+      const uint64_t bhi = min((uint64_t)kmax, (uint64_t)blo + (((uint64_t)1 << shift) - 1));
+      thr = select_exact_regs<kMergeThreads, kPer>(v, (int)need, sc, (uint64_t)blo << 32,
+                                                   (bhi << 32) | 0xFFFFFFFFull);
     }
   }
   // Winners in (thread, slot) order.

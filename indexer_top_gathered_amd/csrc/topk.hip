@@ -86,6 +86,21 @@ struct Scratch {
   uint64_t pick;   // a composite published to the block
 };
 
+// How many entries of list[0..n8) are above x; n8 is a multiple of 8 and
+// the list is zero-padded to it (real composites are non-zero). Every lane
+// reads the same 16-byte slots (broadcast reads), four at a time.
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t count_above(const uint64_t* list, uint32_t n8, uint64_t x) {
+  const u64x2* L = reinterpret_cast<const u64x2*>(list);
+  uint32_t r = 0;
+  for (uint32_t i = 0; i < n8 / 2; i += 4) {
+    const u64x2 a = L[i], b = L[i + 1], c = L[i + 2], d = L[i + 3];
+    r += (a.x > x ? 1u : 0u) + (a.y > x ? 1u : 0u) + (b.x > x ? 1u : 0u) + (b.y > x ? 1u : 0u) +
+         (c.x > x ? 1u : 0u) + (c.y > x ? 1u : 0u) + (d.x > x ? 1u : 0u) + (d.y > x ? 1u : 0u);
+  }
+  return r;
+}
+
 // Exclusive block-wide scan in thread order; *total gets the sum. One
 // barrier: every caller passes another barrier before wsum is written again.
 template <int THREADS>
@@ -496,9 +511,13 @@ __device__ __forceinline__ uint32_t admit_vector(const u32x4& kv, uint32_t t0, b
 // value keys (2048 buckets over their actual range) finds its bucket; a
 // bucket that is not taken whole is gathered into a list and ranked entry
 // against entry; a bucket of more than THREADS entries (heavy ties) takes
-// the general select. Expects both histograms clear and leaves them dirty.
+// the general select, except when all of its entries tie on one value: then
+// the K-th is the entry of that value with the need-th smallest position,
+// found through a bitmap of positions (entries lie in [pos0, pos0 + npos);
+// npos <= 65536). Expects both histograms clear and leaves them dirty.
 template <int THREADS>
-__device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int K, Scratch& sc) {
+__device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int K, Scratch& sc,
+                                              uint32_t pos0, uint32_t npos) {
   constexpr int W = THREADS / kWave;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
@@ -537,21 +556,64 @@ __device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int 
       const uint64_t x = buf[i];
       if ((((uint32_t)(x >> 32) - lo) >> shift) == digit) list[atomicAdd(&sc.n_app, 1u)] = x;
     }
+    const uint32_t n8 = (in_bucket + 7u) & ~7u;
+    if ((uint32_t)tid >= in_bucket && (uint32_t)tid < n8) list[tid] = 0;
     lds_barrier();
     if (tid < (int)in_bucket) {
       const uint64_t x = list[tid];
-      uint32_t r = 0;
-      for (uint32_t i = 0; i < in_bucket; ++i) r += list[i] > x ? 1u : 0u;
+      const uint32_t r = count_above(list, n8, x);
       if (r == need - 1) sc.pick = x;  // exactly one entry has this rank
     }
     lds_barrier();
     return sc.pick;
   }
   // A heavy bucket (many ties): the K-th largest is the need-th largest of
-  // the bucket's own entries, so the exact select starts from the bucket.
+  // the bucket's own entries.
   for (int i = tid; i < kHBins; i += THREADS) h[i] = 0;  // ordered by the next barrier
   const uint64_t bhi = min((uint64_t)hi, (uint64_t)blo + (((uint64_t)1 << shift) - 1));
-  return select_exact<THREADS>(buf, cnt, (int)need, sc, (uint64_t)blo << 32, (bhi << 32) | 0xFFFFFFFFull);
+  uint64_t clo = (uint64_t)blo << 32, chi = (bhi << 32) | 0xFFFFFFFFull;
+  bucket_range<THREADS>(buf, cnt, clo, chi, sc);
+  if ((uint32_t)(clo >> 32) == (uint32_t)(chi >> 32) && npos <= 32u * kHBins) {  // uniform
+    // One value: larger composites are smaller positions, so the answer is
+    // the tied entry with the need-th smallest position.
+    constexpr int WPT = kHBins / THREADS;  // bitmap words per thread
+    const uint32_t val = (uint32_t)(clo >> 32);
+    for (int i = tid; i < cnt; i += THREADS) {
+      const uint64_t x = buf[i];
+      if ((uint32_t)(x >> 32) == val) {
+        const uint32_t p = composite_pos(x) - pos0;
+        atomicOr(&h[p >> 5], 1u << (p & 31));
+      }
+    }
+    lds_barrier();
+    uint32_t w[WPT], c = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      w[j] = h[tid * WPT + j];
+      c += __popc(w[j]);
+    }
+    uint32_t before_total;
+    const uint32_t before = block_exclusive_scan<THREADS>(c, &before_total, sc);
+    if (before < need && need <= before + c) {
+      uint32_t r = need - before;  // 1-based rank inside this thread's words
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        const uint32_t pc = __popc(w[j]);
+        if (r > 0 && r <= pc) {
+          uint32_t m = w[j];
+          for (uint32_t q = 1; q < r; ++q) m &= m - 1;  // drop the r-1 lowest set bits
+          const uint32_t p = (uint32_t)(tid * WPT + j) * 32u + (uint32_t)(__ffs(m) - 1);
+          sc.pick = composite(val, pos0 + p);
+          r = 0;
+        } else if (r > 0) {
+          r -= pc;
+        }
+      }
+    }
+    lds_barrier();
+    return sc.pick;
+  }
+  return select_exact<THREADS>(buf, cnt, (int)need, sc, clo, chi);
 }
 
 // FUSED (one segment covering the whole row): after stage 1 the workgroup
@@ -725,7 +787,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         if (cnt + THREADS * E > CAP && cnt > k) {
-          const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
+          const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
           cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
           for (int i = threadIdx.x; i < kHBins; i += THREADS) {
             sc.hist[0][i] = 0;
@@ -747,7 +809,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     // After the first block: cut to the exact top k so that later blocks
     // are filtered by the k-th composite.
     if (base + kBlock < seg_end && cnt > k && !have_thr) {
-      const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
+      const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
       cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
       for (int i = threadIdx.x; i < kHBins; i += THREADS) {
         sc.hist[0][i] = 0;
@@ -762,7 +824,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   }
   if (FUSED) {
     // The row's candidates are all here: select the k winners and write them.
-    const uint64_t t = cnt > k ? select_k_lds<THREADS>(cand, cnt, k, sc) : (uint64_t)0;
+    const uint64_t t = cnt > k ? select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start)) : (uint64_t)0;
     write_winners_from_lds<BF16, CAP / THREADS, THREADS>(
         cand, cnt, t, reinterpret_cast<const char*>(row), N, k, out_idx + (size_t)b * k, out_val,
         (size_t)b * k, sorted_index, reinterpret_cast<uint32_t*>(cand + CAP), sc);
@@ -770,7 +832,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   }
   // At most 2k candidates leave the segment.
   if (cnt > 2 * k) {
-    const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc);
+    const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
     cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
   }
   cnt = min(cnt, 2 * k);
@@ -944,11 +1006,12 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
         if (v[j] && (((uint32_t)(v[j] >> 32) - kmin) >> shift) == digit)
           list[atomicAdd(&sc.n_app, 1u)] = v[j];
       }
+      const uint32_t n8 = (in_bucket + 7u) & ~7u;
+      if ((uint32_t)tid >= in_bucket && (uint32_t)tid < n8) list[tid] = 0;
       lds_barrier();
       if (tid < (int)in_bucket) {
         const uint64_t x = list[tid];
-        uint32_t r = 0;
-        for (uint32_t i = 0; i < in_bucket; ++i) r += list[i] > x ? 1u : 0u;
+        const uint32_t r = count_above(list, n8, x);
         if (r == need - 1) sc.pick = x;
       }
       lds_barrier();

@@ -152,11 +152,14 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
                                 float* s, int B, int N, int H, hipStream_t st) {
   // Each wave keeps its query fragments (up to 16 KB per batch row) in
   // registers for its whole sweep. Aim for one round of about 256 workgroups
-  // (one per CU measured fastest), each sweeping at least 8 and at most 32
-  // rounds of 256 keys so the query loads stay small next to the key stream.
+  // (one per CU measured fastest), each sweeping at most 32 rounds of 256
+  // keys; large calls take at least 8 rounds per workgroup so the query
+  // loads stay small next to the key stream, while small calls (fewer than
+  // 256 * 8 rounds in all) spread over as many workgroups as they can fill.
   const long long per_row_rounds = (N + kIsKeysPerRound - 1) / kIsKeysPerRound;
-  long long rounds = ((long long)B * per_row_rounds + 255) / 256;
-  if (rounds < 8) rounds = 8;
+  const long long total_rounds = (long long)B * per_row_rounds;
+  long long rounds = (total_rounds + 255) / 256;
+  if (rounds < 8 && total_rounds >= 256 * 8) rounds = 8;
   if (rounds > 32) rounds = 32;
   if (rounds > per_row_rounds) rounds = per_row_rounds;
   if (rounds < 1) rounds = 1;

@@ -70,6 +70,40 @@ def test_special_rows(dtype, k):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rising_and_falling_long_rows(dtype):
+    # Segments of several register blocks: a rising row beats the running
+    # bound in every later block (each block then takes its own threshold and
+    # the list is compacted); a falling row is settled by its first block.
+    N = 262144
+    ar = torch.arange(N, device=DEV, dtype=torch.float32)
+    rows = torch.stack([ar, ar.flip(0), (ar % 4096) + ar / N]).to(dtype)
+    run_case(rows, 2048, values=True, where="rising/falling long rows")
+    run_case(rows, 777, sorted_index=True, where="rising/falling long rows sorted")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_heavy_bucket_of_several_values(dtype):
+    # A few huge scores stretch the candidates' range, so one histogram
+    # bucket holds the whole cluster below them: more than 512 entries of
+    # several distinct values, with the k-th inside. Low background elsewhere.
+    N = 65536
+    g = torch.Generator(device=DEV).manual_seed(8)
+    x = -1.0e6 - torch.rand((2, N), generator=g, device=DEV)
+    pos = torch.randperm(N, generator=g, device=DEV)
+    huge, clus = pos[:10], pos[10:3010]
+    x[:, huge] = 1.0e30 * (1 + torch.arange(10, device=DEV, dtype=torch.float32))
+    if dtype == torch.float32:
+        base = torch.tensor(1.0, dtype=torch.float32, device=DEV).view(torch.int32)
+        vals = (base + torch.arange(3000, device=DEV, dtype=torch.int32) % 1000).view(torch.float32)
+    else:  # eight adjacent bf16 values above 1.0
+        vals = 1.0 + (torch.arange(3000, device=DEV, dtype=torch.float32) % 8) / 128
+    x[:, clus] = vals
+    x = x.to(dtype)
+    run_case(x, 1510, values=True, where="heavy multi-value bucket")
+    run_case(x, 1510, sorted_index=True, where="heavy multi-value bucket sorted")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_signed_zero_infinity_and_subnormal(dtype):
     N = 9000
     g = torch.Generator(device=DEV).manual_seed(5)

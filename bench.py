@@ -171,10 +171,16 @@ def indexer_bytes(s) -> int:
 
 
 def source_digest(paths) -> str:
+    """Hash of the sources' code: comments and blank space are dropped, so
+    a comment edit does not void counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,7 +11,8 @@
 // wants 16 different keys per 16 lanes (64 bytes of each per instruction);
 // loaded that way a key row costs twice the cache-line requests of a
 // contiguous read, which bounds the load rate. So keys are loaded in whole
-// 1 KB runs (4 keys per instruction, three steps in flight per wave), written
+// 1 KB runs (4 keys per instruction; three register buffers per wave, two
+// steps in flight while one is computed), written
 // to a per-wave LDS area with each key's 16-byte chunks XOR-swizzled by the
 // key index, and read back in MFMA layout without bank conflicts. Every byte
 // of k is read from HBM exactly once. The query fragments and weights stay

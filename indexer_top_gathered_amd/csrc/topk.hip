@@ -9,34 +9,38 @@
 // word, complemented position in the low word), so the k largest composites
 // are the unique answer. The kernels never sort.
 //
-// Stage 1, one workgroup per (row, segment). The segment is read once from
-// HBM straight into registers, V 16-byte vectors per thread, all loads in
-// flight together, and turned into order keys in place (bf16 keys two per
-// 32-bit word). A threshold comes cheaply from "group maxima": group
-// (thread t, element e) holds element e of every vector of thread t, so its
-// members are spread evenly over the block. If at least k groups have a
-// maximum >= T then at least k scores are >= T, so T may reject everything
-// below it; one histogram round over the 512*E group maxima (E = 8 bf16 or
-// 4 float32 per vector) gives such a T. Random rows let a few percent
+// Stage 1, one workgroup per (row, segment). The segment is read from HBM
+// straight into registers in blocks of V 16-byte vectors per thread, all
+// loads of a block in flight together, and a block's scores become order
+// keys when it is taken up (bf16 keys two per 32-bit word). A threshold
+// comes cheaply from "group maxima": group (thread t, element e) holds
+// element e of every vector of thread t, so its members are spread evenly
+// over the block. If at least k groups have a maximum >= T then at least k
+// scores are >= T, so T may reject everything below it; one histogram round
+// over about 2k group maxima gives such a T. Random rows let a few percent
 // through and sorted rows about k, because the spread-out groups see the
 // whole range. Each vector is first tested by its maximum, so most are
-// dismissed with a handful of instructions; survivors go to an LDS buffer in
-// thread order (block prefix sum). A later block of a long segment is also
-// filtered by the exact k-th candidate so far. If a block's survivors would
-// overflow the buffer, that block is taken one vector at a time with exact
-// selects in between. At most 2k candidates leave the segment; more are
-// first cut to exactly k.
+// dismissed with a handful of instructions; survivors go to an LDS list in
+// thread order (block prefix sum). A later block of a long segment is
+// filtered by the exact k-th candidate so far; if its survivors would
+// overflow the list (a row rising along the segment), the block's own group
+// maxima give a higher bound, the list is cut to it, and later blocks are
+// held to it. Only if that overflows too is the block taken one vector at a
+// time with exact selects in between. At most 2k candidates leave the
+// segment; more are first cut to exactly k.
 //
-// Stage 2, one workgroup per row: load every segment's candidates at once,
-// compact them into LDS, select the row's k-th composite exactly, and write
-// the k winners (indices, optional value copies), in buffer order or sorted
-// by index.
+// Stage 2, one workgroup per row: load every segment's candidates into
+// registers at once, select the row's k-th composite exactly, and write the
+// k winners (indices, optional value copies), in buffer order or sorted by
+// index.
 //
-// Exact selection is a radix select whose 10-bit digits split the current
-// [lo, hi] range of the candidates into 1024 equal buckets (a histogram
-// round picks the bucket holding the K-th largest), so each round narrows
-// the range 1024-fold whatever the value distribution, and ties are split by
-// position.
+// Exact selection: one histogram round over the candidates' value keys
+// (2048 buckets over their actual range) finds the bucket of the K-th
+// largest. A bucket of up to 512 entries is gathered and ranked entry
+// against entry; a heavier one whose entries tie on one value is resolved by
+// position through a bitmap; any other goes to a radix select whose 10-bit
+// digits split the remaining range into 1024 equal buckets per round, so
+// each round narrows it 1024-fold whatever the value distribution.
 #include "dsa_internal.h"
 
 namespace dsa {

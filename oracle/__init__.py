@@ -65,6 +65,11 @@ def _load():
             lib.oracle_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                         ctypes.c_double]
             lib.oracle_step.restype = I
+            lib.oracle_topk_ragged.argtypes = [P, I, I, I, P, I, P, I]
+            lib.oracle_topk_ragged.restype = I
+            lib.oracle_step_ragged.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                               I, ctypes.c_double]
+            lib.oracle_step_ragged.restype = I
             lib.oracle_set_threads.argtypes = [I]
             lib.oracle_set_threads.restype = None
             lib.oracle_max_threads.argtypes = []
@@ -134,10 +139,33 @@ def topk(scores: np.ndarray, k: int, index_order: bool = False) -> np.ndarray:
     return idx
 
 
+def topk_ragged(scores: np.ndarray, lengths: np.ndarray, k: int,
+                index_order: bool = False) -> np.ndarray:
+    """Top-k over the first lengths[b] scores of each row; slots past
+    min(k, lengths[b]) hold -1. Same dtypes and orders as topk."""
+    scores = np.ascontiguousarray(scores)
+    if scores.dtype == np.uint16:
+        dt = BF16
+    elif scores.dtype == np.float32:
+        dt = F32
+    else:
+        raise TypeError("scores must be float32 or uint16 (bf16 bits)")
+    B, N = scores.shape
+    lengths = _c(lengths, np.int32)
+    assert lengths.shape == (B,)
+    idx = np.empty((B, k), np.int32)
+    rc = _load().oracle_topk_ragged(_ptr(scores), dt, B, N, _ptr(lengths), int(k), _ptr(idx),
+                                    int(bool(index_order)))
+    if rc != 0:
+        raise ValueError("oracle_topk_ragged: invalid arguments")
+    return idx
+
+
 def attend(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win: np.ndarray | None,
            scale: float) -> np.ndarray:
-    """Sparse attention. q uint16 [B,Hq,D], kv uint16 [B,N,D], idx int32 [B,k],
-    win uint16 [B,W,D] or None -> float64 [B,Hq,D]."""
+    """Sparse attention. q uint16 [B,Hq,D], kv uint16 [B,N,D], idx int32 [B,k]
+    (-1: an empty slot, no row), win uint16 [B,W,D] or None -> float64
+    [B,Hq,D]; a batch row with no rows at all gets zeros."""
     q = _c(q, np.uint16)
     kv = _c(kv, np.uint16)
     idx = _c(idx, np.int32)
@@ -184,4 +212,34 @@ def step(q_idx, k_idx, w, q, kv, win, k: int, scale: float):
                              float(scale))
     if rc != 0:
         raise ValueError("oracle_step: invalid arguments")
+    return scores, idx, out
+
+
+def step_ragged(q_idx, k_idx, w, q, kv, win, lengths, k: int, scale: float):
+    """The step over ragged rows (row b's top-k looks at its first lengths[b]
+    scores; empty slots, -1, take no part in attention). Returns (scores,
+    idx, out) as step does."""
+    q_idx = _c(q_idx, np.uint16)
+    k_idx = _c(k_idx, np.uint16)
+    w = _c(w, np.float32)
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    lengths = _c(lengths, np.int32)
+    B, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq, D = q.shape[1], q.shape[2]
+    if win is None or win.size == 0:
+        W = 0
+        win = np.zeros((1,), np.uint16)
+    else:
+        win = _c(win, np.uint16)
+        W = win.shape[1]
+    scores = np.empty((B, N), np.float32)
+    idx = np.empty((B, k), np.int32)
+    out = np.empty((B, Hq, D), np.float64)
+    rc = _load().oracle_step_ragged(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv),
+                                    _ptr(win), _ptr(lengths), _ptr(scores), _ptr(idx), _ptr(out),
+                                    B, N, H, DI, int(k), W, Hq, D, float(scale))
+    if rc != 0:
+        raise ValueError("oracle_step_ragged: invalid arguments")
     return scores, idx, out

@@ -25,6 +25,9 @@
  *  - top-k order: value descending, ties broken by lower index; -0 == +0.
  *  - attention: rows = selected compressed rows followed by the W window
  *    rows; the same row serves as key and value; plain softmax, no mask.
+ *  - ragged rows (an extension): row b has lengths[b] valid positions; its
+ *    top-k slots past min(k, lengths[b]) hold -1, and a -1 slot takes no
+ *    part in attention (a batch row with no rows gets zeros).
  *
  * Every floating-point step runs in double. bf16 inputs are decoded exactly.
  * OpenMP, when enabled, only splits independent batch rows; the result does
@@ -158,20 +161,65 @@ int oracle_topk(const void* scores, int dtype, int B, int N, int k,
 }
 
 /*
+ * Ragged rows (a reading beyond [CSA], whose block takes one compressed
+ * length T_c for the whole batch in its launch listing, with the sequence
+ * length a driver option): in a serving batch each sequence has its own
+ * length, so row b holds lengths[b] valid positions (0 <= lengths[b] <= N;
+ * later positions take no part). Its first min(k, lengths[b]) output slots
+ * hold the top-k of the valid prefix, in the same order as oracle_topk, and
+ * the remaining slots hold -1. Returns 0, or -1 on bad args.
+ */
+int oracle_topk_ragged(const void* scores, int dtype, int B, int N, const int32_t* lengths,
+                       int k, int32_t* idx, int index_order) {
+  if (B < 1 || N < 1 || k < 1 || k > N || (dtype != 0 && dtype != 1)) return -1;
+  for (int b = 0; b < B; ++b)
+    if (lengths[b] < 0 || lengths[b] > N) return -1;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* vals = (double*)malloc(sizeof(double) * (size_t)N);
+    keyed_t* tmp = (keyed_t*)malloc(sizeof(keyed_t) * (size_t)N);
+    if (!vals || !tmp) {
+#pragma omp atomic write
+      bad = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (int b = 0; b < B; ++b) {
+        const int n = lengths[b];
+        const int kk = k < n ? k : n;
+        int32_t* out = idx + (int64_t)b * k;
+        for (int j = 0; j < n; ++j) {
+          int64_t at = (int64_t)b * N + j;
+          vals[j] = dtype == 0 ? bf16_value(((const uint16_t*)scores)[at])
+                               : (double)((const float*)scores)[at];
+        }
+        if (kk > 0) topk_row(vals, n, kk, out, index_order, tmp);
+        for (int t = kk; t < k; ++t) out[t] = -1;
+      }
+    }
+    free(vals);
+    free(tmp);
+  }
+  return bad ? -1 : 0;
+}
+
+/*
  * Sparse multi-query attention for one decode token [CSA step 4; PTB]:
  *   R_b = rows kv[b, idx[b,0..k)] followed by rows win[b, 0..W)
  *   z[h,r] = scale * q[b,h,:] . R_b[r,:]
  *   p[h,:] = softmax over r of z[h,:]
  *   out[b,h,:] = sum_r p[h,r] * R_b[r,:]          (the row is key and value)
- * q: bf16 [B,Hq,D]; kv: bf16 [B,N,D]; idx: int32 [B,k] with values in [0,N);
- * win: bf16 [B,W,D] (unused when W == 0); out: double [B,Hq,D].
+ * q: bf16 [B,Hq,D]; kv: bf16 [B,N,D]; idx: int32 [B,k] with values in [0,N),
+ * or -1 for a slot that holds no row (ragged rows: it takes no part);
+ * win: bf16 [B,W,D] (unused when W == 0); out: double [B,Hq,D]. A batch row
+ * with no rows at all gets a zero output.
  * Returns 0, or -1 if an index is out of range.
  */
 int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                   const uint16_t* win, double* out, int B, int N, int k, int W,
                   int Hq, int D, double scale) {
   for (int64_t t = 0; t < (int64_t)B * k; ++t)
-    if (idx[t] < 0 || idx[t] >= N) return -1;
+    if (idx[t] < -1 || idx[t] >= N) return -1;
   const int R = k + W;
   if (R < 1) return -1;
 #pragma omp parallel
@@ -181,31 +229,38 @@ int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
 #pragma omp for schedule(static)
     for (int b = 0; b < B; ++b) {
+      int nr = 0;  /* rows that take part, gathered in slot order */
       for (int r = 0; r < R; ++r) {
+        if (r < k && idx[(int64_t)b * k + r] < 0) continue;
         const uint16_t* src =
             r < k ? kv + ((int64_t)b * N + idx[(int64_t)b * k + r]) * D
                   : win + ((int64_t)b * W + (r - k)) * D;
-        for (int d = 0; d < D; ++d) rows[(int64_t)r * D + d] = bf16_value(src[d]);
+        for (int d = 0; d < D; ++d) rows[(int64_t)nr * D + d] = bf16_value(src[d]);
+        ++nr;
       }
       for (int h = 0; h < Hq; ++h) {
         const uint16_t* qrow = q + ((int64_t)b * Hq + h) * D;
         for (int d = 0; d < D; ++d) qd[d] = bf16_value(qrow[d]);
+        double* o = out + ((int64_t)b * Hq + h) * D;
+        if (nr == 0) {
+          for (int d = 0; d < D; ++d) o[d] = 0.0;
+          continue;
+        }
         double m = -INFINITY;
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < nr; ++r) {
           double dot = 0.0;
           for (int d = 0; d < D; ++d) dot += qd[d] * rows[(int64_t)r * D + d];
           z[r] = scale * dot;
           if (z[r] > m) m = z[r];
         }
         double l = 0.0;
-        for (int r = 0; r < R; ++r) {
+        for (int r = 0; r < nr; ++r) {
           z[r] = exp(z[r] - m);
           l += z[r];
         }
-        double* o = out + ((int64_t)b * Hq + h) * D;
         for (int d = 0; d < D; ++d) {
           double acc = 0.0;
-          for (int r = 0; r < R; ++r) acc += z[r] * rows[(int64_t)r * D + d];
+          for (int r = 0; r < nr; ++r) acc += z[r] * rows[(int64_t)r * D + d];
           o[d] = acc / l;
         }
       }
@@ -228,5 +283,17 @@ int oracle_step(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
                 int DI, int k, int W, int Hq, int D, double scale) {
   oracle_indexer(q_idx, k_idx, w, scores, B, N, H, DI);
   if (oracle_topk(scores, 1, B, N, k, idx, 0) != 0) return -1;
+  return oracle_attend(q, kv, idx, win, out, B, N, k, W, Hq, D, scale);
+}
+
+/* The same step over ragged rows: the top-k of row b looks only at its
+ * first lengths[b] scores, and empty slots (-1) take no part in attention. */
+int oracle_step_ragged(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                       const uint16_t* q, const uint16_t* kv, const uint16_t* win,
+                       const int32_t* lengths, float* scores, int32_t* idx, double* out,
+                       int B, int N, int H, int DI, int k, int W, int Hq, int D,
+                       double scale) {
+  oracle_indexer(q_idx, k_idx, w, scores, B, N, H, DI);
+  if (oracle_topk_ragged(scores, 1, B, N, lengths, k, idx, 0) != 0) return -1;
   return oracle_attend(q, kv, idx, win, out, B, N, k, W, Hq, D, scale);
 }

@@ -319,3 +319,91 @@ def test_oracle_threads_do_not_change_results():
     oracle.set_threads(4)
     b = oracle.topk(x.numpy(), 50)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- ragged rows
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_ragged_matches_rank_definition_of_the_prefix(seed):
+    """Row b's answer is the rank-definition top-k of its first lengths[b]
+    scores, padded with -1; lengths 0, below k, equal to k and N occur."""
+    g = torch.Generator().manual_seed(400 + seed)
+    N, k = [(50, 7), (120, 30), (9, 9), (200, 64)][seed]
+    x = _rows_with_ties(g, 6, N, levels=[3, 7, 2, 50][seed])
+    lengths = np.array([0, 1, min(k - 1, N), k, N, N // 2], np.int32)
+    for dt in ("f32", "bf16"):
+        xs = x.numpy() if dt == "f32" else bf16_bits(x)
+        xv = x if dt == "f32" else x.to(torch.bfloat16).float()
+        got = oracle.topk_ragged(xs, lengths, k)
+        got_sorted = oracle.topk_ragged(xs, lengths, k, index_order=True)
+        for b in range(x.shape[0]):
+            n = int(lengths[b])
+            want = brute.rank_select(xv[b, :n].tolist(), min(k, n))
+            assert got[b].tolist() == want + [-1] * (k - len(want))
+            assert got_sorted[b].tolist() == sorted(want) + [-1] * (k - len(want))
+
+
+def test_topk_ragged_full_lengths_equal_topk():
+    g = torch.Generator().manual_seed(410)
+    x = torch.randn(4, 3000, generator=g)
+    lengths = np.full(4, 3000, np.int32)
+    assert np.array_equal(oracle.topk_ragged(x.numpy(), lengths, 100), oracle.topk(x.numpy(), 100))
+
+
+def test_topk_ragged_rejects_bad_lengths():
+    x = np.zeros((2, 10), np.float32)
+    with pytest.raises(ValueError):
+        oracle.topk_ragged(x, np.array([3, 11], np.int32), 4)
+    with pytest.raises(ValueError):
+        oracle.topk_ragged(x, np.array([-1, 3], np.int32), 4)
+
+
+def test_attend_empty_slots_equal_sdpa_on_the_remaining_rows():
+    """Slots holding -1 take no part: the result is fp64 SDPA over the rows
+    that remain (selected ones in slot order, then the window)."""
+    g = torch.Generator().manual_seed(411)
+    B, N, k, W, Hq, D = 3, 150, 20, 4, 16, 128
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    win = torch.randn(B, W, D, generator=g).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(N, generator=g)[:k] for _ in range(B)]).int()
+    idx[0, 5:] = -1          # a short row
+    idx[1, ::3] = -1         # holes anywhere
+    idx[2, :] = -1           # only the window remains
+    got = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), 0.05)
+    for b in range(B):
+        keep = idx[b][idx[b] >= 0].long()
+        rows = torch.cat([kv[b, keep], win[b]], dim=0).unsqueeze(0)
+        ref = _sdpa_ref(q[b:b + 1], rows, 0.05)
+        assert np.max(np.abs(got[b] - ref[0])) < 1e-12
+
+
+def test_attend_with_no_rows_is_zero():
+    g = torch.Generator().manual_seed(412)
+    q = torch.randn(2, 16, 128, generator=g).to(torch.bfloat16)
+    kv = torch.randn(2, 30, 128, generator=g).to(torch.bfloat16)
+    idx = np.full((2, 4), -1, np.int32)
+    idx[1, 2] = 7
+    out = oracle.attend(bf16_bits(q), bf16_bits(kv), idx, None, 0.1)
+    assert np.all(out[0] == 0.0)
+    assert np.array_equal(out[1], np.broadcast_to(kv[1, 7].double().numpy(), (16, 128)))
+    with pytest.raises(ValueError):
+        oracle.attend(bf16_bits(q), bf16_bits(kv), np.full((2, 4), -2, np.int32), None, 0.1)
+
+
+def test_step_ragged_is_the_composition():
+    s = workloads.StepShape(B=3, N=300, H_I=8, D_I=128, k=20, W=5, H_q=16, D=128)
+    inp = workloads.step_inputs(s, 77100)
+    b = {k_: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.numpy()) for k_, v in inp.items()}
+    lengths = np.array([300, 7, 0], np.int32)
+    scores, idx, out = oracle.step_ragged(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"],
+                                          b["kv_win"], lengths, s.k, s.scale)
+    assert np.array_equal(scores, oracle.indexer(b["q_idx"], b["k_idx"], b["w"]))
+    assert np.array_equal(idx, oracle.topk_ragged(scores, lengths, s.k))
+    assert np.array_equal(out, oracle.attend(b["q"], b["kv_cmp"], idx, b["kv_win"], s.scale))
+    # full lengths: the ordinary step
+    full = np.full(3, 300, np.int32)
+    a = oracle.step_ragged(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"], b["kv_win"],
+                           full, s.k, s.scale)
+    c = oracle.step(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"], b["kv_win"], s.k, s.scale)
+    assert all(np.array_equal(u, v) for u, v in zip(a, c))

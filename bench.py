@@ -21,7 +21,9 @@ runs on, `topk` the top-k-only workload (bf16 64 x 131072, k=512), and
 JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
 `topk-sampling` (float32 128 x 129280, k=1024, values), `topk-stress`
 (quantised rows, half sorted, 64 x 262144, k=2048, bf16 and float32) or
-`stress-step` (B=64, N=262144, k=2048, scores equal to the stress rows).
+`stress-step` (B=64, N=262144, k=2048, scores equal to the stress rows) or
+`ragged-step` (the production shape over rows of lengths uniform on [1, N],
+timed with dsa_decode_step_ragged next to the same call at full length).
 """
 from __future__ import annotations
 
@@ -50,7 +52,8 @@ def parse():
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
-                   choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step"])
+                   choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step",
+                            "ragged-step"])
     return p.parse_args()
 
 
@@ -72,6 +75,31 @@ def step_roofline_us(s) -> float:
     is_flops = 2 * b * s.N * s.H_I * s.D_I
     sa_bytes = step_bytes(s) - is_bytes
     sa_flops = 4 * b * s.H_q * (s.k + s.W) * s.D
+    peak_flops = 2.5e15
+    return 1e6 * (max(is_bytes / (HBM_PEAK_GBPS * 1e9), is_flops / peak_flops)
+                  + max(sa_bytes / (HBM_PEAK_GBPS * 1e9), sa_flops / peak_flops))
+
+
+def ragged_step_bytes(s, lengths) -> int:
+    """Compulsory bytes of a ragged decode step: as step_bytes with row b's
+    N keys replaced by its lengths[b] valid ones and its k gathered rows by
+    min(k, lengths[b])."""
+    total = 0
+    for n in (int(x) for x in lengths):
+        total += (s.H_I * s.D_I * 2 + n * s.D_I * 2 + s.H_I * 4 + s.H_q * s.D * 2
+                  + (min(s.k, n) + s.W) * s.D * 2 + s.H_q * s.D * 2)
+    return total
+
+
+def ragged_step_roofline_us(s, lengths) -> float:
+    """step_roofline_us over the valid keys and gathered rows only."""
+    n_sum = sum(int(x) for x in lengths)
+    g_sum = sum(min(s.k, int(x)) for x in lengths)
+    b = s.B
+    is_bytes = b * s.H_I * s.D_I * 2 + n_sum * s.D_I * 2 + b * s.H_I * 4
+    is_flops = 2 * n_sum * s.H_I * s.D_I
+    sa_bytes = ragged_step_bytes(s, lengths) - is_bytes
+    sa_flops = 4 * s.H_q * (g_sum + b * s.W) * s.D
     peak_flops = 2.5e15
     return 1e6 * (max(is_bytes / (HBM_PEAK_GBPS * 1e9), is_flops / peak_flops)
                   + max(sa_bytes / (HBM_PEAK_GBPS * 1e9), sa_flops / peak_flops))
@@ -128,6 +156,41 @@ def other_workload(args):
                      "frac_of_roofline": round(roof / us, 4), "rotating_input_copies": R,
                      "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
                                 "W": s.W, "H_q": s.H_q, "D": s.D}})
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "ragged-step":
+        # The production step's shape over a serving batch of mixed lengths,
+        # next to the same inputs at full length.
+        s = workloads.C4
+        lengths = workloads.serving_lengths(s.B, s.N, 6000)
+        lens = torch.from_numpy(lengths).to(dev)
+        full = torch.full((s.B,), s.N, dtype=torch.int32, device=dev)
+        R = max(1, min(256, -(-(1 << 30) // step_bytes(s))))
+        copies = [workloads.step_inputs(s, 6000 + 10 * r, device=dev) for r in range(R)]
+        dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
+        ws = torch.empty(dsa.dsa_decode_step_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        out = torch.empty((s.B, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+
+        def caller(lv):
+            def call(i):
+                c = copies[i % R]
+                dsa.dsa_decode_step_ragged(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                           c["kv_win"], lv, s.k, s.scale, out=out, ws=ws,
+                                           stream=stream)
+            return call
+        us = time_calls(caller(lens), args.warmup, args.steps, stream)
+        us_full = time_calls(caller(full), args.warmup, args.steps, stream)
+        one = ragged_step_bytes(s, lengths)
+        roof = ragged_step_roofline_us(s, lengths)
+        line.update({"us_per_step": round(us, 2), "value": round(one / (us * 1e-6) / 1e9, 1),
+                     "compulsory_bytes": one, "roofline_us": round(roof, 3),
+                     "frac_of_roofline": round(roof / us, 4),
+                     "mean_length": round(float(lengths.mean()), 1),
+                     "full_length_us_per_step": round(us_full, 2),
+                     "rotating_input_copies": R,
+                     "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
+                                "W": s.W, "H_q": s.H_q, "D": s.D,
+                                "lengths": "uniform on [1, N], seed 6000"}})
         print(json.dumps(line), flush=True)
         return
     # Top-k workloads.

@@ -111,7 +111,9 @@ DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, i
  *   R_b      = [kv_cmp[b, idx[b,i]] for i < k] followed by [kv_win[b,t] for t < W]
  *   out[b,h] = softmax_r(scale * q[b,h] . R_b[r]) @ R_b
  * q bf16 [B, H_q, D]; kv_cmp bf16 [B, N, D]; idx int32 [B, k] with values in
- * [0, N) (out-of-range values are clamped, the result is then unspecified);
+ * [0, N), or negative for an empty slot that takes no part (a batch row
+ * left with no rows at all gets a zero output); values >= N are clamped and
+ * the result is then unspecified;
  * kv_win bf16 [B, W, D] (may be NULL iff W == 0); out bf16 [B, H_q, D].
  * Softmax statistics and accumulation run in float32; out is rounded to
  * nearest even. Only dims->batch, n, topk, window, q_heads, head_dim, scale
@@ -136,6 +138,34 @@ DSA_EXPORT dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, co
                              const void* q, const void* kv_cmp, const void* kv_win,
                              void* out, int32_t* out_idx, const dsa_dims_t* dims,
                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Ragged rows. The CSA pull request launches its block with one compressed
+ * length T_c for the whole batch ("Launching a full block", with the
+ * sequence length a driver option); a serving batch holds sequences of
+ * different lengths. These calls take, in addition, lengths: int32 [B] in
+ * device memory, row b holding lengths[b] valid positions (a value below 0
+ * counts as 0, one above N as N). Positions at or beyond it take no part:
+ * they are never selected, whatever their scores.
+ *
+ * dsa_topk_ragged: as dsa_topk over each row's valid prefix. When
+ * lengths[b] < k, out_idx[b] holds the lengths[b] selected positions first
+ * (ascending when sorted_index == 1) and -1 in the remaining slots, and
+ * out_val (when given) holds negative infinity there. Workspace: as
+ * dsa_topk_workspace_bytes(B, N, k, dtype).
+ *
+ * dsa_decode_step_ragged: the step with the ragged top-k; empty slots (-1)
+ * take no part in attention. Workspace: dsa_decode_step_workspace_bytes.
+ */
+DSA_EXPORT dsa_status_t dsa_topk_ragged(const void* scores, dsa_dtype_t dtype, int B, int N,
+                             const int32_t* lengths, int k, int32_t* out_idx,
+                             void* out_val, int sorted_index, void* ws, size_t ws_bytes,
+                             void* stream);
+DSA_EXPORT dsa_status_t dsa_decode_step_ragged(const void* q_idx, const void* k_idx,
+                                    const float* w, const void* q, const void* kv_cmp,
+                                    const void* kv_win, const int32_t* lengths, void* out,
+                                    int32_t* out_idx, const dsa_dims_t* dims, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 DSA_EXPORT const char* dsa_status_string(dsa_status_t status);

@@ -8,11 +8,13 @@ from .binding import (  # noqa: F401
     DsaDims,
     DsaError,
     dsa_decode_step,
+    dsa_decode_step_ragged,
     dsa_decode_step_workspace_bytes,
     dsa_indexer_score,
     dsa_sparse_attend,
     dsa_sparse_attend_workspace_bytes,
     dsa_topk,
+    dsa_topk_ragged,
     dsa_topk_workspace_bytes,
     make_dims,
     status_string,

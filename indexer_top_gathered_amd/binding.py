@@ -27,6 +27,8 @@ EXPORTED = (
     "dsa_sparse_attend",
     "dsa_decode_step_workspace_bytes",
     "dsa_decode_step",
+    "dsa_topk_ragged",
+    "dsa_decode_step_ragged",
     "dsa_status_string",
 )
 
@@ -75,6 +77,10 @@ def _load() -> ctypes.CDLL:
     lib.dsa_decode_step_workspace_bytes.restype = S
     lib.dsa_decode_step.argtypes = [P, P, P, P, P, P, P, P, D, P, S, P]
     lib.dsa_decode_step.restype = I
+    lib.dsa_topk_ragged.argtypes = [P, I, I, I, P, I, P, P, I, P, S, P]
+    lib.dsa_topk_ragged.restype = I
+    lib.dsa_decode_step_ragged.argtypes = [P, P, P, P, P, P, P, P, P, D, P, S, P]
+    lib.dsa_decode_step_ragged.restype = I
     lib.dsa_status_string.argtypes = [I]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -156,10 +162,23 @@ def dsa_topk(scores, k: int, return_values: bool = False, sorted_index: bool = F
              out_idx=None, out_val=None, ws=None, stream=None):
     """Indices (int32 [B,k]) of the k largest scores per row, lower index
     first among ties; values are bit copies when return_values."""
+    return _topk(scores, None, k, return_values, sorted_index, out_idx, out_val, ws, stream)
+
+
+def dsa_topk_ragged(scores, lengths, k: int, return_values: bool = False,
+                    sorted_index: bool = False, out_idx=None, out_val=None, ws=None, stream=None):
+    """dsa_topk over each row's first lengths[b] scores (lengths: int32 [B]
+    on the device); slots past min(k, lengths[b]) hold -1 (values -inf)."""
+    return _topk(scores, lengths, k, return_values, sorted_index, out_idx, out_val, ws, stream)
+
+
+def _topk(scores, lengths, k, return_values, sorted_index, out_idx, out_val, ws, stream):
     if scores.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("scores must be bfloat16 or float32")
     _need(scores, "scores", scores.dtype)
     B, N = scores.shape
+    if lengths is not None:
+        _need(lengths, "lengths", torch.int32, (B,))
     dt = DSA_BF16 if scores.dtype == torch.bfloat16 else DSA_F32
     if out_idx is None:
         out_idx = torch.empty((B, k), dtype=torch.int32, device=scores.device)
@@ -170,9 +189,14 @@ def dsa_topk(scores, k: int, return_values: bool = False, sorted_index: bool = F
         _need(out_val, "out_val", scores.dtype, (B, k))
     nbytes = LIB.dsa_topk_workspace_bytes(B, N, int(k), dt)
     ws = _workspace(nbytes, scores.device, ws)
-    _check(LIB.dsa_topk(_ptr(scores), dt, B, N, int(k), _ptr(out_idx), _ptr(out_val),
-                        int(bool(sorted_index)), _ptr(ws), ws.numel(), _stream(stream)),
-           "dsa_topk")
+    if lengths is None:
+        _check(LIB.dsa_topk(_ptr(scores), dt, B, N, int(k), _ptr(out_idx), _ptr(out_val),
+                            int(bool(sorted_index)), _ptr(ws), ws.numel(), _stream(stream)),
+               "dsa_topk")
+    else:
+        _check(LIB.dsa_topk_ragged(_ptr(scores), dt, B, N, _ptr(lengths), int(k), _ptr(out_idx),
+                                   _ptr(out_val), int(bool(sorted_index)), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "dsa_topk_ragged")
     return (out_idx, out_val) if out_val is not None else out_idx
 
 
@@ -213,6 +237,20 @@ def dsa_decode_step_workspace_bytes(dims: DsaDims) -> int:
 def dsa_decode_step(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, out=None,
                     out_idx=None, ws=None, stream=None, return_idx: bool = False):
     """Indexer scores -> top-k -> sparse attention in one enqueue sequence."""
+    return _step(q_idx, k_idx, w, q, kv_cmp, kv_win, None, k, scale, out, out_idx, ws, stream,
+                 return_idx)
+
+
+def dsa_decode_step_ragged(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k: int, scale: float,
+                           out=None, out_idx=None, ws=None, stream=None,
+                           return_idx: bool = False):
+    """dsa_decode_step over ragged rows (lengths: int32 [B] on the device)."""
+    return _step(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k, scale, out, out_idx, ws, stream,
+                 return_idx)
+
+
+def _step(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k, scale, out, out_idx, ws, stream,
+          return_idx):
     B, H, DI = q_idx.shape
     N = k_idx.shape[1]
     Hq, D = q.shape[1], q.shape[2]
@@ -233,8 +271,16 @@ def dsa_decode_step(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, ou
         _need(out_idx, "out_idx", torch.int32, (B, k))
     dims = make_dims(B, N, H, DI, k, W, Hq, D, scale)
     ws = _workspace(LIB.dsa_decode_step_workspace_bytes(ctypes.byref(dims)), q.device, ws)
-    _check(LIB.dsa_decode_step(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
-                               _ptr(kv_win if W else None), _ptr(out), _ptr(out_idx),
-                               ctypes.byref(dims), _ptr(ws), ws.numel(), _stream(stream)),
-           "dsa_decode_step")
+    if lengths is None:
+        _check(LIB.dsa_decode_step(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
+                                   _ptr(kv_win if W else None), _ptr(out), _ptr(out_idx),
+                                   ctypes.byref(dims), _ptr(ws), ws.numel(), _stream(stream)),
+               "dsa_decode_step")
+    else:
+        _need(lengths, "lengths", torch.int32, (B,))
+        _check(LIB.dsa_decode_step_ragged(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q),
+                                          _ptr(kv_cmp), _ptr(kv_win if W else None),
+                                          _ptr(lengths), _ptr(out), _ptr(out_idx),
+                                          ctypes.byref(dims), _ptr(ws), ws.numel(),
+                                          _stream(stream)), "dsa_decode_step_ragged")
     return (out, out_idx) if out_idx is not None else out

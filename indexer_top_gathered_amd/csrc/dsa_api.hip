@@ -124,7 +124,7 @@ dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, const float
   if (s != DSA_SUCCESS) return s;
   return to_status(launch_indexer_score(static_cast<const uint16_t*>(q_idx),
                                         static_cast<const uint16_t*>(k_idx), w, scores, B, N,
-                                        H_I, static_cast<hipStream_t>(stream)));
+                                        H_I, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
@@ -132,9 +132,13 @@ size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
   return plan_topk(B, N, k, dtype).bytes;
 }
 
-dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k,
-                      int32_t* out_idx, void* out_val, int sorted_index, void* ws,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dsa_status_t topk_impl(const void* scores, dsa_dtype_t dtype, int B, int N, const int32_t* lengths,
+                       int k, int32_t* out_idx, void* out_val, int sorted_index, void* ws,
+                       size_t ws_bytes, void* stream) {
   if (!scores || !out_idx) return DSA_ERROR_INVALID_VALUE;
   if (!aligned16(scores) || !aligned16(ws) || (reinterpret_cast<uintptr_t>(out_idx) & 3u))
     return DSA_ERROR_INVALID_VALUE;
@@ -148,8 +152,27 @@ dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k
   if (ws_bytes < plan.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();
   if (s != DSA_SUCCESS) return s;
-  return to_status(launch_topk(scores, dtype, B, N, k, out_idx, out_val, sorted_index, plan, ws,
-                               static_cast<hipStream_t>(stream)));
+  return to_status(launch_topk(scores, dtype, B, N, k, out_idx, out_val, sorted_index, lengths,
+                               plan, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, int N, int k,
+                      int32_t* out_idx, void* out_val, int sorted_index, void* ws,
+                      size_t ws_bytes, void* stream) {
+  return topk_impl(scores, dtype, B, N, nullptr, k, out_idx, out_val, sorted_index, ws, ws_bytes,
+                   stream);
+}
+
+dsa_status_t dsa_topk_ragged(const void* scores, dsa_dtype_t dtype, int B, int N,
+                             const int32_t* lengths, int k, int32_t* out_idx, void* out_val,
+                             int sorted_index, void* ws, size_t ws_bytes, void* stream) {
+  if (!lengths || (reinterpret_cast<uintptr_t>(lengths) & 3u)) return DSA_ERROR_INVALID_VALUE;
+  return topk_impl(scores, dtype, B, N, lengths, k, out_idx, out_val, sorted_index, ws, ws_bytes,
+                   stream);
 }
 
 size_t dsa_sparse_attend_workspace_bytes(const dsa_dims_t* dims) {
@@ -184,9 +207,14 @@ size_t dsa_decode_step_workspace_bytes(const dsa_dims_t* dims) {
   return step_layout(*dims).bytes;
 }
 
-dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* w, const void* q,
-                             const void* kv_cmp, const void* kv_win, void* out, int32_t* out_idx,
-                             const dsa_dims_t* dims, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, const void* q,
+                       const void* kv_cmp, const void* kv_win, const int32_t* lengths, void* out,
+                       int32_t* out_idx, const dsa_dims_t* dims, void* ws, size_t ws_bytes,
+                       void* stream) {
   dsa_status_t s = check_attend_dims(dims);
   if (s != DSA_SUCCESS) return s;
   s = check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim);
@@ -208,14 +236,36 @@ dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* 
   const dsa_dims_t& d = *dims;
   hipError_t e = launch_indexer_score(static_cast<const uint16_t*>(q_idx),
                                       static_cast<const uint16_t*>(k_idx), w, scores, d.batch, d.n,
-                                      d.idx_heads, st);
+                                      d.idx_heads, lengths, st);
   if (e != hipSuccess) return DSA_ERROR_LAUNCH;
-  e = launch_topk(scores, DSA_F32, d.batch, d.n, d.topk, sel, nullptr, 0, L.tk, base + L.topk_off, st);
+  e = launch_topk(scores, DSA_F32, d.batch, d.n, d.topk, sel, nullptr, 0, lengths, L.tk,
+                  base + L.topk_off, st);
   if (e != hipSuccess) return DSA_ERROR_LAUNCH;
   e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp), sel,
                     static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), d, L.at,
                     base + L.attend_off, st);
   return to_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* w, const void* q,
+                             const void* kv_cmp, const void* kv_win, void* out, int32_t* out_idx,
+                             const dsa_dims_t* dims, void* ws, size_t ws_bytes, void* stream) {
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx, dims, ws, ws_bytes,
+                   stream);
+}
+
+dsa_status_t dsa_decode_step_ragged(const void* q_idx, const void* k_idx, const float* w,
+                                    const void* q, const void* kv_cmp, const void* kv_win,
+                                    const int32_t* lengths, void* out, int32_t* out_idx,
+                                    const dsa_dims_t* dims, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (!lengths || (reinterpret_cast<uintptr_t>(lengths) & 3u)) return DSA_ERROR_INVALID_VALUE;
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims, ws, ws_bytes,
+                   stream);
 }
 
 }  // extern "C"

@@ -180,8 +180,11 @@ __device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. Arguments are already checked.
 
+// lengths: int32 [B] in device memory, or NULL for full rows; with it,
+// scores at or past row b's length are not written.
 hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const float* w,
-                                float* s, int B, int N, int H, hipStream_t st);
+                                float* s, int B, int N, int H, const int32_t* lengths,
+                                hipStream_t st);
 
 struct TopkPlan {
   bool fused;       // one workgroup per row does everything (no second kernel)
@@ -193,8 +196,10 @@ struct TopkPlan {
   size_t bytes;     // total workspace bytes
 };
 TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt);
+// lengths: int32 [B] in device memory (row b's valid positions), or NULL
+// for full rows.
 hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
-                       int32_t* out_idx, void* out_val, int sorted_index,
+                       int32_t* out_idx, void* out_val, int sorted_index, const int32_t* lengths,
                        const TopkPlan& plan, void* ws, hipStream_t st);
 
 struct AttendPlan {

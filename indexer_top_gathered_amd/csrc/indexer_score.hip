@@ -34,8 +34,15 @@ constexpr int kDI = 128;
 template <int MT>  // MT = number of 16-head tiles (1..4)
 __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const float* __restrict__ w, float* __restrict__ s, int N, int H, int keys_per_wg) {
+    const float* __restrict__ w, float* __restrict__ s, int N, int H, int keys_per_wg,
+    const int32_t* __restrict__ lengths) {
   const int b = blockIdx.y;
+  // Ragged rows: keys at or past the row's length are neither read nor
+  // scored. A workgroup wholly past it has nothing to do.
+  const int rlen = lengths ? min(max(lengths[b], 0), N) : N;
+  const int start = blockIdx.x * keys_per_wg;
+  if (start >= rlen) return;  // uniform
+  const int end = min(rlen, start + keys_per_wg);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int m = lane & 15;
@@ -67,8 +74,6 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
 
   const uint16_t* krow = k + (size_t)b * N * kDI;
   float* srow = s + (size_t)b * N;
-  const int start = blockIdx.x * keys_per_wg;
-  const int end = min(N, start + keys_per_wg);
 
   // Keys are loaded with whole 1 KB runs per instruction (4 keys x 256 B,
   // lane l: key 4j + l/16, 16-byte chunk l%16), then written to this wave's
@@ -79,7 +84,7 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
   auto load_step = [&](u32x4 (&r)[8], int key0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int key = min(key0 + 4 * j + (lane >> 4), N - 1);
+      const int key = min(key0 + 4 * j + (lane >> 4), rlen - 1);
       r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (size_t)key * kDI) + (lane & 15));
     }
   };
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
     mine += lane_xor32(mine);
     if (g < 2) {
       const int key = key0 + g * 16 + m;
-      if (key < N) srow[key] = mine;
+      if (key < rlen) srow[key] = mine;
     }
   };
   // Three register buffers in turn: two steps of loads in flight while one
@@ -150,7 +155,8 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
 }  // namespace
 
 hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const float* w,
-                                float* s, int B, int N, int H, hipStream_t st) {
+                                float* s, int B, int N, int H, const int32_t* lengths,
+                                hipStream_t st) {
   // Each wave keeps its query fragments (up to 16 KB per batch row) in
   // registers for its whole sweep. Aim for one round of about 256 workgroups
   // (one per CU measured fastest), each sweeping at most 32 rounds of 256
@@ -169,10 +175,10 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
   dim3 block(kIsThreads);
   const int mt = (H + 15) / 16;
   switch (mt) {
-    case 1: hipLaunchKernelGGL(indexer_score_kernel<1>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
-    case 2: hipLaunchKernelGGL(indexer_score_kernel<2>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
-    case 3: hipLaunchKernelGGL(indexer_score_kernel<3>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
-    default: hipLaunchKernelGGL(indexer_score_kernel<4>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
+    case 1: hipLaunchKernelGGL(indexer_score_kernel<1>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
+    case 2: hipLaunchKernelGGL(indexer_score_kernel<2>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
+    case 3: hipLaunchKernelGGL(indexer_score_kernel<3>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
+    default: hipLaunchKernelGGL(indexer_score_kernel<4>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
   }
   return hipGetLastError();
 }

@@ -27,6 +27,8 @@
 // partials (max, sum, and the unnormalised O in fp16 with one float32 scale
 // per head and dim half) that a combine kernel merges with the log-sum-exp
 // rule.
+#include <cfloat>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -39,6 +41,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Lazy-rescale margin in base-2 units: weights stay below 2^11.5 (about e^8).
 constexpr float kRescale2 = 11.5f;
 constexpr int kStages = 3;         // LDS tiles
+// Row-list entry of an empty slot (a negative index: no row, ragged rows).
+constexpr int kEmpty = -0x7FFFFFFF - 1;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -65,6 +69,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   uint32_t* Rbuf = lds;  // kStages tiles
   f32x4* xbuf = reinterpret_cast<f32x4*>(lds + kStages * kTile * ROW_WORDS);
   int32_t* srow = reinterpret_cast<int32_t*>(lds + kStages * kTile * ROW_WORDS + XWORDS);
+  int32_t* wempty = srow + rows_per_split;  // per wave: saw an empty slot
 
   // Workgroup -> work item (batch, split, head group), batch-major.
   // Workgroups are dispatched to the 8 XCDs round robin, so XCD x runs ids
@@ -139,17 +144,22 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   for (int kk = 0; kk < KS; ++kk) qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + kk * 32 + g * 8);
 
   // The split's source rows for the later tiles: >= 0 a compressed row,
-  // < 0 window row -(v+1).
+  // kEmpty an empty slot (negative index), other negatives window row
+  // -(v+1). Each wave notes whether it met an empty slot.
+  bool saw_empty = false;
   for (int r = r0 + tid; r < r1; r += THREADS) {
     int v;
     if (r < k) {
       v = irow[r];
-      v = v < 0 ? 0 : (v >= N ? N - 1 : v);  // out-of-range indices are clamped
+      saw_empty |= v < 0;
+      v = v < 0 ? kEmpty : (v >= N ? N - 1 : v);  // indices >= N are clamped
     } else {
       v = -(r - k) - 1;
     }
     srow[r - r0] = v;
   }
+  const bool wave_saw_empty = __ballot(saw_empty) != 0;  // all lanes take part
+  if (lane == 0) wempty[wave] = wave_saw_empty ? 1 : 0;
   // Settle the query loads here: otherwise the compiler places their waits
   // inside the tile loop, where they would also wait for the row copies in
   // flight.
@@ -162,7 +172,10 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   // The softmax runs in base 2: logits are scaled by scale*log2(e), so every
   // weight is one exp2. mrun is in those units.
   const float scale2 = scale * kLog2e;
-  float mrun = -INFINITY;  // running max of the scaled logits of head h
+  // Running max of the scaled logits of head h. It starts at -FLT_MAX, not
+  // -inf: a split whose slots are all empty keeps it, and its weights
+  // exp2(-inf - mrun) are still 0 with a finite (m, l = 0) partial.
+  float mrun = -FLT_MAX;
   float lrun = 0.0f;       // this lane's share of the running sum
 
   // Rows are copied from HBM straight into the LDS tiles (global_load_lds).
@@ -180,7 +193,9 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int rr = wave * kRowsPerWave + i;
       const int v = __builtin_amdgcn_readfirstlane(vr[i]);
-      const uint16_t* src = (v >= 0 ? kvb + (size_t)v * D : winb + (size_t)(-v - 1) * D) + (lane % ROW_LANES) * 8;
+      // An empty slot copies row 0 (finite data; its weight is zero).
+      const uint16_t* src = (v >= 0 ? kvb + (size_t)v * D : (v == kEmpty ? kvb : winb + (size_t)(-v - 1) * D)) +
+                            (lane % ROW_LANES) * 8;
       const uint32_t at = __builtin_amdgcn_readfirstlane(lds_byte_addr(dst + rr * ROW_WORDS));
       if (ROW_LANES == kWave || lane < ROW_LANES) dma_row16(src, at);
     }
@@ -210,6 +225,11 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   if (ntiles > 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRowsPerWave) : "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();  // tile 0 and the row list visible
+  int any_empty_v = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) any_empty_v |= wempty[w];
+  // The same in every lane; made scalar so the tile loop branches on it.
+  const bool any_empty = __builtin_amdgcn_readfirstlane(any_empty_v) != 0;
   f32x4 s0, s1;   // partial logits of the tile about to be finished
   partial_s(0, s0, s1);
   if (DSPLIT > 1) {
@@ -260,6 +280,18 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
         z[4 + i] = (t0 + 16 + 4 * g + i < r1) ? c1[i] * scale2 : -INFINITY;
       }
     }
+    if (any_empty) {  // uniform: empty slots get no weight
+      const int4 e0 = *reinterpret_cast<const int4*>(srow + t * kTile + 4 * g);
+      const int4 e1 = *reinterpret_cast<const int4*>(srow + t * kTile + 16 + 4 * g);
+      z[0] = e0.x == kEmpty ? -INFINITY : z[0];
+      z[1] = e0.y == kEmpty ? -INFINITY : z[1];
+      z[2] = e0.z == kEmpty ? -INFINITY : z[2];
+      z[3] = e0.w == kEmpty ? -INFINITY : z[3];
+      z[4] = e1.x == kEmpty ? -INFINITY : z[4];
+      z[5] = e1.y == kEmpty ? -INFINITY : z[5];
+      z[6] = e1.z == kEmpty ? -INFINITY : z[6];
+      z[7] = e1.w == kEmpty ? -INFINITY : z[7];
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx = fmaxf(mx, z[i]);
     mx = fmaxf(mx, lane_xor16(mx));
@@ -268,7 +300,8 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     // only moves when a tile's maximum exceeds it by more than kRescale2, so
     // the weights stay below 2^kRescale2 and the accumulators are rescaled
     // (for the whole wave at once) on few tiles only. The first tile always
-    // sets the reference (mrun starts at -inf).
+    // sets the reference (mrun starts at -FLT_MAX); a tile of empty slots
+    // only (mx = -inf) never does.
     if (__ballot(mx > mrun + kRescale2) != 0) {
       const float mnew = fmaxf(mrun, mx);  // finite: the tile holds at least one row
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
@@ -323,7 +356,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   l += lane_xor32(l);
   // Lane (m, g) holds O[h][dbase + 16*dt + 4g + i].
   if (splits == 1) {
-    const float inv = 1.0f / l;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // no row at all: zeros
     uint16_t* orow = out + ((size_t)b * Hq + h) * D + dbase;
 #pragma unroll
     for (int dt = 0; dt < DTW; ++dt) {
@@ -403,7 +436,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(
     float Mc = M;
 #pragma unroll
     for (int j = 0; j < SC; ++j) Mc = fmaxf(Mc, ml[j].x);
-    const float r = __expf(M - Mc);  // 0 on the first chunk (M = -inf)
+    // Every partial max is finite (a split with no rows wrote -FLT_MAX ln 2
+    // and l = 0), so Mc is too and r is 0 on the first chunk (M = -inf).
+    const float r = __expf(M - Mc);
     L *= r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] *= r;
@@ -421,7 +456,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(
     }
     M = Mc;
   }
-  const float inv = 1.0f / L;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no row at all: zeros
   u32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q] * inv, acc[2 * q + 1] * inv);
@@ -438,7 +473,7 @@ hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t*
   constexpr int ROW_WORDS = D / 2 + 4;
   constexpr int XWORDS = DSPLIT > 1 ? 2 * WAVES * kWave * 8 : 0;
   const size_t lds = ((size_t)kStages * kTile * ROW_WORDS + XWORDS) * sizeof(uint32_t) +
-                     (size_t)p.rows_per_split * sizeof(int32_t);
+                     ((size_t)p.rows_per_split + WAVES) * sizeof(int32_t);
   auto kern = sparse_attend_kernel<D, HG, DSPLIT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

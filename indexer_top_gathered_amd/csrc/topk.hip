@@ -623,6 +623,19 @@ __device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int 
 // FUSED (one segment covering the whole row): after stage 1 the workgroup
 // also selects the row's k winners from its LDS candidates and writes them,
 // so no stage 2 runs.
+// Output slots [from, k) of a row that has fewer than k valid positions
+// (ragged rows): index -1 and, when values are returned, negative infinity.
+template <bool BF16, int THREADS>
+__device__ __forceinline__ void pad_row(int32_t* oi, void* out_val, size_t out_off, int from, int k) {
+  for (int i = from + (int)threadIdx.x; i < k; i += THREADS) {
+    oi[i] = -1;
+    if (out_val) {
+      if (BF16) reinterpret_cast<uint16_t*>(out_val)[out_off + i] = 0xFF80u;
+      else reinterpret_cast<uint32_t*>(out_val)[out_off + i] = 0xFF800000u;
+    }
+  }
+}
+
 template <bool BF16, int kPer, int THREADS>
 __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t thr, const char* row,
                                        int N, int k, int32_t* oi, void* out_val, size_t out_off,
@@ -632,7 +645,8 @@ template <bool BF16, bool ALIGNED, int V, int THREADS, bool FUSED>
 __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     const void* __restrict__ scores, int N, int k, int seg_len, int segs,
     uint64_t* __restrict__ cand_out, uint32_t* __restrict__ cnt_out,
-    int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index) {
+    int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index,
+    const int32_t* __restrict__ lengths) {
   constexpr int E = BF16 ? 8 : 4;
   constexpr int CAP = seg_cap<THREADS>();
   static_assert(V * E <= 64, "the admission mask holds 64 bits");
@@ -643,8 +657,15 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   const size_t esz = BF16 ? 2 : 4;
   const void* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;
   const int64_t seg_start = (int64_t)sidx * seg_len;
-  const int64_t seg_end = min((int64_t)N, seg_start + seg_len);
+  // Ragged rows: positions at or past the row's length take no part.
+  const int64_t row_end = lengths ? (int64_t)min(max(lengths[b], 0), N) : (int64_t)N;
+  const int64_t seg_end = min(row_end, seg_start + seg_len);
   constexpr int64_t kBlock = (int64_t)THREADS * V * E;
+  if (seg_end <= seg_start) {  // nothing valid in this segment (uniform)
+    if (FUSED) pad_row<BF16, THREADS>(out_idx + (size_t)b * k, out_val, (size_t)b * k, 0, k);
+    else if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = 0;
+    return;
+  }
 
   for (int i = threadIdx.x; i < kHBins; i += THREADS) {
     sc.hist[0][i] = 0;
@@ -880,6 +901,7 @@ __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t t
         ++pos;
       }
     }
+    pad_row<BF16, THREADS>(oi, out_val, out_off, (int)min(nkeep, (uint32_t)k), k);
     return;
   }
   int P = 1;
@@ -913,6 +935,7 @@ __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t t
       else reinterpret_cast<uint32_t*>(out_val)[out_off + i] = reinterpret_cast<const uint32_t*>(row)[p];
     }
   }
+  pad_row<BF16, THREADS>(oi, out_val, out_off, nout, k);
 }
 
 template <bool BF16, int kPer>  // kPer: candidate slots per thread (segs * 2k <= 512 * kPer)
@@ -1050,16 +1073,19 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
         ++pos;
       }
     }
+    // A ragged row with fewer than k valid positions: -1 in the rest.
+    pad_row<BF16, kMergeThreads>(oi, out_val, (size_t)b * k, (int)min(nkeep, (uint32_t)k), k);
     return;
   }
   // Sorted by index: the winners' positions go to LDS, padded to a power of
   // two, then a bitonic sort.
   int P = 1;
   while (P < k) P <<= 1;
+  const int nout = (int)min(nkeep, (uint32_t)k);
 #pragma unroll
   for (int j = 0; j < kPer; ++j)
     if (v[j] && v[j] >= thr && pos < (uint32_t)k) pos_lds[pos++] = min(composite_pos(v[j]), (uint32_t)(N - 1));
-  for (int i = k + tid; i < P; i += kMergeThreads) pos_lds[i] = 0xFFFFFFFFu;
+  for (int i = nout + tid; i < P; i += kMergeThreads) pos_lds[i] = 0xFFFFFFFFu;
   lds_barrier();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -1076,7 +1102,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       lds_barrier();
     }
   }
-  for (int i = tid; i < k; i += kMergeThreads) {
+  for (int i = tid; i < nout; i += kMergeThreads) {
     const uint32_t p = pos_lds[i];
     oi[i] = (int32_t)p;
     if (out_val) {
@@ -1084,6 +1110,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       else reinterpret_cast<uint32_t*>(out_val)[(size_t)b * k + i] = reinterpret_cast<const uint32_t*>(row)[p];
     }
   }
+  pad_row<BF16, kMergeThreads>(oi, out_val, (size_t)b * k, nout, k);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1098,7 +1125,7 @@ hipError_t allow_lds(K kernel, size_t bytes) {
 template <bool BF16, bool AL, int V, int THREADS, bool FUSED>
 hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
                       uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
-                      hipStream_t st) {
+                      const int32_t* lengths, hipStream_t st) {
   int P = 1;
   while (P < k) P <<= 1;
   const size_t lds = (size_t)seg_cap<THREADS>() * sizeof(uint64_t) + (FUSED ? (size_t)P * sizeof(uint32_t) : 0);
@@ -1106,31 +1133,31 @@ hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p
   hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.segs, B), dim3(THREADS), lds, st, scores, N, k, p.seg_len, p.segs,
-                     cand, cnt, out_idx, out_val, sorted_index);
+                     cand, cnt, out_idx, out_val, sorted_index, lengths);
   return hipGetLastError();
 }
 
 template <bool BF16, bool AL, int THREADS, bool FUSED>
 hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
                         uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
-                        hipStream_t st) {
+                        const int32_t* lengths, hipStream_t st) {
   switch (p.vec) {
-    case 1: return launch_seg<BF16, AL, 1, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
-    case 2: return launch_seg<BF16, AL, 2, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
-    case 4: return launch_seg<BF16, AL, 4, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
-    default: return launch_seg<BF16, AL, 8, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, st);
+    case 1: return launch_seg<BF16, AL, 1, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
+    case 2: return launch_seg<BF16, AL, 2, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
+    case 4: return launch_seg<BF16, AL, 4, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
+    default: return launch_seg<BF16, AL, 8, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
   }
 }
 
 template <bool BF16, bool AL>
 hipError_t launch_stage1(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
                          uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
-                         hipStream_t st) {
+                         const int32_t* lengths, hipStream_t st) {
   if (p.fused)
     return launch_seg_v<BF16, AL, kRowThreads, true>(scores, B, N, k, p, cand, cnt, out_idx, out_val,
-                                                     sorted_index, st);
+                                                     sorted_index, lengths, st);
   return launch_seg_v<BF16, AL, kTkThreads, false>(scores, B, N, k, p, cand, cnt, out_idx, out_val,
-                                                   sorted_index, st);
+                                                   sorted_index, lengths, st);
 }
 
 }  // namespace
@@ -1182,7 +1209,7 @@ TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
 }
 
 hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
-                       int32_t* out_idx, void* out_val, int sorted_index,
+                       int32_t* out_idx, void* out_val, int sorted_index, const int32_t* lengths,
                        const TopkPlan& plan, void* ws, hipStream_t st) {
   uint64_t* cand = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + plan.cand_off);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + plan.cnt_off);
@@ -1190,10 +1217,10 @@ hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
   const int E = bf16 ? 8 : 4;
   const bool aligned = (N % E) == 0 && (reinterpret_cast<uintptr_t>(scores) % 16) == 0;
   hipError_t e;
-  if (bf16) e = aligned ? launch_stage1<true, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st)
-                        : launch_stage1<true, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st);
-  else e = aligned ? launch_stage1<false, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st)
-                   : launch_stage1<false, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, st);
+  if (bf16) e = aligned ? launch_stage1<true, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st)
+                        : launch_stage1<true, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
+  else e = aligned ? launch_stage1<false, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st)
+                   : launch_stage1<false, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
   if (e != hipSuccess || plan.fused) return e;
   int P = 1;
   while (P < k) P <<= 1;

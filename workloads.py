@@ -22,6 +22,7 @@ from __future__ import annotations
 import math
 from dataclasses import dataclass, replace
 
+import numpy as np
 import torch
 
 
@@ -103,6 +104,23 @@ def step_inputs(s: StepShape, seed_base: int, device="cpu") -> dict:
         "kv_win": _normal((s.B, s.W, s.D), _gen(device, sb + 5), device, torch.bfloat16),
     }
     return out
+
+
+def ragged_lengths(B: int, N: int, k: int, seed: int) -> np.ndarray:
+    """int32 [B] sequence lengths for a ragged batch: the edge values 0, 1,
+    k - 1, k, k + 1 and N first (those within [0, N]), then lengths drawn
+    log-uniformly from [1, N], so short and long sequences mix."""
+    edges = [v for v in (0, 1, k - 1, k, k + 1, N) if 0 <= v <= N]
+    rng = np.random.default_rng(seed)
+    rest = np.exp(rng.uniform(0.0, np.log(N), size=max(B - len(edges), 0)))
+    out = np.array(edges[:B] + [int(min(N, max(1, round(x)))) for x in rest], dtype=np.int32)
+    return out[:B]
+
+
+def serving_lengths(B: int, N: int, seed: int) -> np.ndarray:
+    """int32 [B] sequence lengths of a serving batch: uniform on [1, N]."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(1, N + 1, size=B).astype(np.int32)
 
 
 def normal_rows(B: int, N: int, dtype: str, seed: int, device="cpu", std: float = 1.0):

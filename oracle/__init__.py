@@ -70,6 +70,14 @@ def _load():
             lib.oracle_step_ragged.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                I, ctypes.c_double]
             lib.oracle_step_ragged.restype = I
+            lib.oracle_indexer_mt.argtypes = [P, P, P, P, I, I, I, I, I]
+            lib.oracle_indexer_mt.restype = None
+            lib.oracle_attend_mt.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I,
+                                             ctypes.c_double]
+            lib.oracle_attend_mt.restype = I
+            lib.oracle_step_mt.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                           I, ctypes.c_double]
+            lib.oracle_step_mt.restype = I
             lib.oracle_set_threads.argtypes = [I]
             lib.oracle_set_threads.restype = None
             lib.oracle_max_threads.argtypes = []
@@ -242,4 +250,79 @@ def step_ragged(q_idx, k_idx, w, q, kv, win, lengths, k: int, scale: float):
                                     B, N, H, DI, int(k), W, Hq, D, float(scale))
     if rc != 0:
         raise ValueError("oracle_step_ragged: invalid arguments")
+    return scores, idx, out
+
+
+def _window(win, lead: tuple, D: int):
+    """(array, W) for a window argument that may be None or empty."""
+    if win is None or win.size == 0:
+        return np.zeros((1,), np.uint16), 0
+    win = _c(win, np.uint16)
+    W = win.shape[len(lead)]
+    assert win.shape == lead + (W, D)
+    return win, W
+
+
+def indexer_mt(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Indexer scores with T query tokens per batch row sharing its keys.
+    q_idx uint16 [B,T,H,D], k_idx uint16 [B,N,D], w float32 [B,T,H] ->
+    float32 [B,T,N]."""
+    q_idx = _c(q_idx, np.uint16)
+    k_idx = _c(k_idx, np.uint16)
+    w = _c(w, np.float32)
+    B, T, H, D = q_idx.shape
+    N = k_idx.shape[1]
+    assert k_idx.shape == (B, N, D) and w.shape == (B, T, H)
+    s = np.empty((B, T, N), np.float32)
+    _load().oracle_indexer_mt(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(s), B, T, N, H, D)
+    return s
+
+
+def attend_mt(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win, scale: float) -> np.ndarray:
+    """Sparse attention with T query tokens per batch row sharing its
+    compressed rows. q uint16 [B,T,Hq,D], kv uint16 [B,N,D], idx int32
+    [B,T,k] (-1: empty slot), win uint16 [B,T,W,D] or None -> float64
+    [B,T,Hq,D]."""
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    idx = _c(idx, np.int32)
+    B, T, Hq, D = q.shape
+    N = kv.shape[1]
+    k = idx.shape[2]
+    assert kv.shape == (B, N, D) and idx.shape == (B, T, k)
+    win, W = _window(win, (B, T), D)
+    out = np.empty((B, T, Hq, D), np.float64)
+    rc = _load().oracle_attend_mt(_ptr(q), _ptr(kv), _ptr(idx), _ptr(win), _ptr(out),
+                                  B, T, N, k, W, Hq, D, float(scale))
+    if rc != 0:
+        raise ValueError("oracle_attend_mt: index out of range or empty row set")
+    return out
+
+
+def step_mt(q_idx, k_idx, w, q, kv, win, lengths, k: int, scale: float):
+    """The step with T query tokens per batch row (shapes as indexer_mt and
+    attend_mt; lengths int32 [B,T] or None for full rows). Returns (scores
+    float32 [B,T,N], idx int32 [B,T,k] in value-desc order, out float64
+    [B,T,Hq,D])."""
+    q_idx = _c(q_idx, np.uint16)
+    k_idx = _c(k_idx, np.uint16)
+    w = _c(w, np.float32)
+    q = _c(q, np.uint16)
+    kv = _c(kv, np.uint16)
+    B, T, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq, D = q.shape[2], q.shape[3]
+    win, W = _window(win, (B, T), D)
+    if lengths is not None:
+        lengths = _c(lengths, np.int32)
+        assert lengths.shape == (B, T)
+    scores = np.empty((B, T, N), np.float32)
+    idx = np.empty((B, T, k), np.int32)
+    out = np.empty((B, T, Hq, D), np.float64)
+    rc = _load().oracle_step_mt(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv), _ptr(win),
+                                None if lengths is None else _ptr(lengths), _ptr(scores),
+                                _ptr(idx), _ptr(out), B, T, N, H, DI, int(k), W, Hq, D,
+                                float(scale))
+    if rc != 0:
+        raise ValueError("oracle_step_mt: invalid arguments")
     return scores, idx, out

@@ -28,6 +28,10 @@
  *  - ragged rows (an extension): row b has lengths[b] valid positions; its
  *    top-k slots past min(k, lengths[b]) hold -1, and a -1 slot takes no
  *    part in attention (a batch row with no rows gets zeros).
+ *  - several query tokens per batch row (an extension): T consecutive query
+ *    rows share one row of keys (indexer keys and compressed KV); each has
+ *    its own queries, weights, window, length and selection, and is in
+ *    every other respect an independent decode row.
  *
  * Every floating-point step runs in double. bf16 inputs are decoded exactly.
  * OpenMP, when enabled, only splits independent batch rows; the result does
@@ -75,12 +79,13 @@ void oracle_bf16_decode(const uint16_t* in, double* out, int64_t n) {
  *   s[b,j] = sum_h w[b,h] * max(0, sum_d q[b,h,d] * k[b,j,d])
  * q: bf16 [B,H,D], k: bf16 [B,N,D], w: float [B,H], s: float [B,N].
  */
-void oracle_indexer(const uint16_t* q, const uint16_t* k, const float* w,
-                    float* s, int B, int N, int H, int D) {
+static void indexer_rows(const uint16_t* q, const uint16_t* k, const float* w,
+                         float* s, int B, int T, int N, int H, int D) {
+  /* query row b reads the keys of batch row b / T */
 #pragma omp parallel for schedule(static)
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; b < B * T; ++b) {
     for (int j = 0; j < N; ++j) {
-      const uint16_t* krow = k + ((int64_t)b * N + j) * D;
+      const uint16_t* krow = k + ((int64_t)(b / T) * N + j) * D;
       double total = 0.0;
       for (int h = 0; h < H; ++h) {
         const uint16_t* qrow = q + ((int64_t)b * H + h) * D;
@@ -92,6 +97,18 @@ void oracle_indexer(const uint16_t* q, const uint16_t* k, const float* w,
       s[(int64_t)b * N + j] = (float)total;
     }
   }
+}
+
+void oracle_indexer(const uint16_t* q, const uint16_t* k, const float* w,
+                    float* s, int B, int N, int H, int D) {
+  indexer_rows(q, k, w, s, B, 1, N, H, D);
+}
+
+/* T query tokens per batch row: q bf16 [B*T,H,D], w [B*T,H], s [B*T,N];
+ * k bf16 [B,N,D] is shared by the T tokens of a row. */
+void oracle_indexer_mt(const uint16_t* q, const uint16_t* k, const float* w,
+                       float* s, int B, int T, int N, int H, int D) {
+  indexer_rows(q, k, w, s, B, T, N, H, D);
 }
 
 /*
@@ -215,10 +232,11 @@ int oracle_topk_ragged(const void* scores, int dtype, int B, int N, const int32_
  * with no rows at all gets a zero output.
  * Returns 0, or -1 if an index is out of range.
  */
-int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                  const uint16_t* win, double* out, int B, int N, int k, int W,
-                  int Hq, int D, double scale) {
-  for (int64_t t = 0; t < (int64_t)B * k; ++t)
+static int attend_rows(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                       const uint16_t* win, double* out, int B, int T, int N, int k,
+                       int W, int Hq, int D, double scale) {
+  /* query row b gathers from the compressed rows of batch row b / T */
+  for (int64_t t = 0; t < (int64_t)B * T * k; ++t)
     if (idx[t] < -1 || idx[t] >= N) return -1;
   const int R = k + W;
   if (R < 1) return -1;
@@ -228,12 +246,12 @@ int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
     double* z = (double*)malloc(sizeof(double) * (size_t)R);
     double* qd = (double*)malloc(sizeof(double) * (size_t)D);
 #pragma omp for schedule(static)
-    for (int b = 0; b < B; ++b) {
+    for (int b = 0; b < B * T; ++b) {
       int nr = 0;  /* rows that take part, gathered in slot order */
       for (int r = 0; r < R; ++r) {
         if (r < k && idx[(int64_t)b * k + r] < 0) continue;
         const uint16_t* src =
-            r < k ? kv + ((int64_t)b * N + idx[(int64_t)b * k + r]) * D
+            r < k ? kv + ((int64_t)(b / T) * N + idx[(int64_t)b * k + r]) * D
                   : win + ((int64_t)b * W + (r - k)) * D;
         for (int d = 0; d < D; ++d) rows[(int64_t)nr * D + d] = bf16_value(src[d]);
         ++nr;
@@ -272,6 +290,20 @@ int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
   return 0;
 }
 
+int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                  const uint16_t* win, double* out, int B, int N, int k, int W,
+                  int Hq, int D, double scale) {
+  return attend_rows(q, kv, idx, win, out, B, 1, N, k, W, Hq, D, scale);
+}
+
+/* T query tokens per batch row: q [B*T,Hq,D], idx [B*T,k], win [B*T,W,D],
+ * out [B*T,Hq,D]; kv [B,N,D] is shared by the T tokens of a row. */
+int oracle_attend_mt(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                     const uint16_t* win, double* out, int B, int T, int N, int k,
+                     int W, int Hq, int D, double scale) {
+  return attend_rows(q, kv, idx, win, out, B, T, N, k, W, Hq, D, scale);
+}
+
 /*
  * The whole decode step [CSA, steps 2 -> 3 -> 4]: indexer scores, then the
  * top-k of each score row, then attention over the selected rows plus the
@@ -296,4 +328,21 @@ int oracle_step_ragged(const uint16_t* q_idx, const uint16_t* k_idx, const float
   oracle_indexer(q_idx, k_idx, w, scores, B, N, H, DI);
   if (oracle_topk_ragged(scores, 1, B, N, lengths, k, idx, 0) != 0) return -1;
   return oracle_attend(q, kv, idx, win, out, B, N, k, W, Hq, D, scale);
+}
+
+/* The step with T query tokens per batch row: the indexer scores every
+ * token against its row's keys, each token's score row gets its own top-k
+ * (over its first lengths[b*T+t] positions when lengths is given, else all
+ * N), and each token attends over its own selection and window. */
+int oracle_step_mt(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
+                   const uint16_t* q, const uint16_t* kv, const uint16_t* win,
+                   const int32_t* lengths, float* scores, int32_t* idx, double* out,
+                   int B, int T, int N, int H, int DI, int k, int W, int Hq, int D,
+                   double scale) {
+  if (T < 1) return -1;
+  oracle_indexer_mt(q_idx, k_idx, w, scores, B, T, N, H, DI);
+  const int rc = lengths ? oracle_topk_ragged(scores, 1, B * T, N, lengths, k, idx, 0)
+                         : oracle_topk(scores, 1, B * T, N, k, idx, 0);
+  if (rc != 0) return -1;
+  return oracle_attend_mt(q, kv, idx, win, out, B, T, N, k, W, Hq, D, scale);
 }

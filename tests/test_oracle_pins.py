@@ -407,3 +407,104 @@ def test_step_ragged_is_the_composition():
                            full, s.k, s.scale)
     c = oracle.step(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"], b["kv_win"], s.k, s.scale)
     assert all(np.array_equal(u, v) for u, v in zip(a, c))
+
+
+# ---------------------------------------------------------------- several query tokens per row
+
+def _mt_inputs(g, B, T, N, H, DI, Hq, D, W):
+    q_idx = torch.randn(B, T, H, DI, generator=g).to(torch.bfloat16)
+    k_idx = torch.randn(B, N, DI, generator=g).to(torch.bfloat16)
+    w = torch.rand(B, T, H, generator=g).float()
+    q = torch.randn(B, T, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    win = torch.randn(B, T, W, D, generator=g).to(torch.bfloat16)
+    return q_idx, k_idx, w, q, kv, win
+
+
+def test_indexer_mt_equals_fp64_einsum():
+    """Token t of row b scores against row b's keys: torch fp64 einsum of
+    the definition, rounded to fp32, at most 1 ulp away (sum order)."""
+    g = torch.Generator().manual_seed(501)
+    B, T, N, H, DI = 3, 3, 97, 5, 128
+    q_idx, k_idx, w, *_ = _mt_inputs(g, B, T, N, H, DI, 16, 128, 1)
+    got = oracle.indexer_mt(bf16_bits(q_idx), bf16_bits(k_idx), w.numpy())
+    dots = torch.einsum("bthd,bnd->btnh", q_idx.double(), k_idx.double())
+    ref = (torch.relu(dots) * w.double()[:, :, None, :]).sum(-1).float().numpy()
+    assert got.shape == (B, T, N)
+    assert np.all(np.abs(got - ref) <= np.spacing(np.abs(ref)))
+    # the keys are really shared: a token scored against another row's keys differs
+    assert not np.array_equal(got[0, 0], got[1, 0])
+
+
+def test_indexer_mt_token_equals_the_single_token_indexer():
+    g = torch.Generator().manual_seed(502)
+    B, T, N, H, DI = 2, 4, 130, 8, 128
+    q_idx, k_idx, w, *_ = _mt_inputs(g, B, T, N, H, DI, 16, 128, 1)
+    qb, kb, wn = bf16_bits(q_idx), bf16_bits(k_idx), w.numpy()
+    got = oracle.indexer_mt(qb, kb, wn)
+    for t in range(T):
+        assert np.array_equal(got[:, t], oracle.indexer(qb[:, t], kb, wn[:, t]))
+
+
+def test_attend_mt_equals_sdpa_per_token():
+    """Each token attends over its own selection from row b's compressed
+    rows (empty slots left out) and its own window: fp64 SDPA."""
+    g = torch.Generator().manual_seed(503)
+    B, T, N, k, W, Hq, D = 2, 3, 120, 17, 4, 16, 128
+    _, _, _, q, kv, win = _mt_inputs(g, B, T, N, 4, 128, Hq, D, W)
+    idx = torch.stack([torch.stack([torch.randperm(N, generator=g)[:k] for _ in range(T)])
+                       for _ in range(B)]).int()
+    idx[0, 1, 6:] = -1
+    idx[1, 2, ::2] = -1
+    got = oracle.attend_mt(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), 0.06)
+    assert got.shape == (B, T, Hq, D)
+    for b in range(B):
+        for t in range(T):
+            keep = idx[b, t][idx[b, t] >= 0].long()
+            rows = torch.cat([kv[b, keep], win[b, t]], dim=0).unsqueeze(0)
+            ref = _sdpa_ref(q[b, t].unsqueeze(0), rows, 0.06)
+            assert np.max(np.abs(got[b, t] - ref[0])) < 1e-12
+
+
+def test_step_mt_is_the_composition_and_tokens_are_independent():
+    g = torch.Generator().manual_seed(504)
+    B, T, N, H, DI, k, W, Hq, D = 2, 3, 260, 8, 128, 19, 5, 16, 128
+    q_idx, k_idx, w, q, kv, win = _mt_inputs(g, B, T, N, H, DI, Hq, D, W)
+    a = [bf16_bits(q_idx), bf16_bits(k_idx), w.numpy(), bf16_bits(q), bf16_bits(kv),
+         bf16_bits(win)]
+    lengths = np.array([[260, 40, 3], [0, 19, 200]], np.int32)
+    scores, idx, out = oracle.step_mt(*a, lengths, k, 0.08)
+    assert np.array_equal(scores, oracle.indexer_mt(a[0], a[1], a[2]))
+    flat = oracle.topk_ragged(scores.reshape(B * T, N), lengths.reshape(-1), k)
+    assert np.array_equal(idx, flat.reshape(B, T, k))
+    assert np.array_equal(out, oracle.attend_mt(a[3], a[4], idx, a[5], 0.08))
+    # no lengths: every token sees all N positions
+    s2, i2, o2 = oracle.step_mt(*a, None, k, 0.08)
+    assert np.array_equal(i2, oracle.topk(s2.reshape(B * T, N), k).reshape(B, T, k))
+    # changing token 1's own inputs leaves tokens 0 and 2 as they were
+    a2 = [x.copy() for x in a]
+    a2[0][:, 1] = a2[0][:, 1][:, ::-1]
+    a2[3][:, 1] = 0
+    a2[5][:, 1] = a2[5][:, 0]
+    s3, i3, o3 = oracle.step_mt(*a2, lengths, k, 0.08)
+    for t in (0, 2):
+        assert np.array_equal(s3[:, t], scores[:, t]) and np.array_equal(i3[:, t], idx[:, t])
+        assert np.array_equal(o3[:, t], out[:, t])
+    assert not np.array_equal(o3[:, 1], out[:, 1])
+
+
+def test_step_mt_with_one_token_is_the_step():
+    s = workloads.StepShape(B=3, N=300, H_I=8, D_I=128, k=20, W=5, H_q=16, D=128)
+    inp = workloads.step_inputs(s, 77200)
+    b = {k_: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.numpy()) for k_, v in inp.items()}
+    one = oracle.step_mt(b["q_idx"][:, None], b["k_idx"], b["w"][:, None], b["q"][:, None],
+                         b["kv_cmp"], b["kv_win"][:, None], None, s.k, s.scale)
+    ref = oracle.step(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"], b["kv_win"], s.k,
+                      s.scale)
+    assert all(np.array_equal(u[:, 0], v) for u, v in zip(one, ref))
+    lengths = np.array([300, 7, 0], np.int32)
+    one = oracle.step_mt(b["q_idx"][:, None], b["k_idx"], b["w"][:, None], b["q"][:, None],
+                         b["kv_cmp"], b["kv_win"][:, None], lengths[:, None], s.k, s.scale)
+    ref = oracle.step_ragged(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"], b["kv_win"],
+                             lengths, s.k, s.scale)
+    assert all(np.array_equal(u[:, 0], v) for u, v in zip(one, ref))

@@ -23,7 +23,9 @@ JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
 (quantised rows, half sorted, 64 x 262144, k=2048, bf16 and float32) or
 `stress-step` (B=64, N=262144, k=2048, scores equal to the stress rows) or
 `ragged-step` (the production shape over rows of lengths uniform on [1, N],
-timed with dsa_decode_step_ragged next to the same call at full length).
+timed with dsa_decode_step_ragged next to the same call at full length) or
+`mtp-step` (the production shape with 2 query tokens per batch row sharing
+its keys, dsa_decode_step_mt, next to 1 and 4 tokens).
 """
 from __future__ import annotations
 
@@ -53,7 +55,7 @@ def parse():
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
                    choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step",
-                            "ragged-step"])
+                            "ragged-step", "mtp-step"])
     return p.parse_args()
 
 
@@ -100,6 +102,29 @@ def ragged_step_roofline_us(s, lengths) -> float:
     is_flops = 2 * n_sum * s.H_I * s.D_I
     sa_bytes = ragged_step_bytes(s, lengths) - is_bytes
     sa_flops = 4 * s.H_q * (g_sum + b * s.W) * s.D
+    peak_flops = 2.5e15
+    return 1e6 * (max(is_bytes / (HBM_PEAK_GBPS * 1e9), is_flops / peak_flops)
+                  + max(sa_bytes / (HBM_PEAK_GBPS * 1e9), sa_flops / peak_flops))
+
+
+def mt_step_bytes(s, T: int) -> int:
+    """Compulsory bytes of a step with T query tokens per batch row: the
+    keys (K_I) read once for all tokens; per token its indexer query and
+    weights, its q, its gathered rows and window, and its output."""
+    b = s.B
+    return (b * s.N * s.D_I * 2
+            + T * b * (s.H_I * s.D_I * 2 + s.H_I * 4 + s.H_q * s.D * 2
+                       + (s.k + s.W) * s.D * 2 + s.H_q * s.D * 2))
+
+
+def mt_step_roofline_us(s, T: int) -> float:
+    """step_roofline_us with T tokens: indexer bytes counted once, its
+    flops and every attention term T times."""
+    b = s.B
+    is_bytes = b * s.N * s.D_I * 2 + T * b * (s.H_I * s.D_I * 2 + s.H_I * 4)
+    is_flops = 2 * T * b * s.N * s.H_I * s.D_I
+    sa_bytes = mt_step_bytes(s, T) - is_bytes
+    sa_flops = 4 * T * b * s.H_q * (s.k + s.W) * s.D
     peak_flops = 2.5e15
     return 1e6 * (max(is_bytes / (HBM_PEAK_GBPS * 1e9), is_flops / peak_flops)
                   + max(sa_bytes / (HBM_PEAK_GBPS * 1e9), sa_flops / peak_flops))
@@ -191,6 +216,48 @@ def other_workload(args):
                      "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
                                 "W": s.W, "H_q": s.H_q, "D": s.D,
                                 "lengths": "uniform on [1, N], seed 6000"}})
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "mtp-step":
+        # The production step's shape with T = 2 query tokens per batch row
+        # (one draft token), next to T = 1 and T = 4; the keys are read once
+        # per step whatever T is.
+        s = workloads.C4
+        R = max(1, min(256, -(-(1 << 30) // step_bytes(s))))
+        results = []
+        for T in (1, 2, 4):
+            copies = [workloads.mt_step_inputs(s, T, 7000 + 10 * r, device=dev) for r in range(R)]
+            dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
+            ws = torch.empty(dsa.dsa_decode_step_mt_workspace_bytes(dims, T), dtype=torch.uint8,
+                             device=dev)
+            out = torch.empty((s.B, T, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+            sc = torch.empty((s.B, T, s.N), dtype=torch.float32, device=dev)
+
+            def call(i, T=T, copies=copies, ws=ws, out=out):
+                c = copies[i % R]
+                dsa.dsa_decode_step_mt(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                       c["kv_win"], s.k, s.scale, out=out, ws=ws, stream=stream)
+
+            def call_is(i, copies=copies, sc=sc):
+                c = copies[i % R]
+                dsa.dsa_indexer_score_mt(c["q_idx"], c["k_idx"], c["w"], scores=sc,
+                                         stream=stream)
+            us = time_calls(call, args.warmup, args.steps, stream)
+            us_is = time_calls(call_is, args.warmup, args.steps, stream)
+            one = mt_step_bytes(s, T)
+            roof = mt_step_roofline_us(s, T)
+            results.append({"tokens": T, "us_per_step": round(us, 2),
+                            "us_per_token": round(us / T, 2),
+                            "effective_GBps": round(one / (us * 1e-6) / 1e9, 1),
+                            "compulsory_bytes": one, "roofline_us": round(roof, 3),
+                            "frac_of_roofline": round(roof / us, 4),
+                            "indexer_us": round(us_is, 2)})
+            del copies
+        two = results[1]
+        line.update({"us_per_step": two["us_per_step"], "value": two["effective_GBps"],
+                     "results": results, "rotating_input_copies": R,
+                     "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
+                                "W": s.W, "H_q": s.H_q, "D": s.D, "tokens": 2}})
         print(json.dumps(line), flush=True)
         return
     # Top-k workloads.

@@ -167,6 +167,45 @@ DSA_EXPORT dsa_status_t dsa_decode_step_ragged(const void* q_idx, const void* k_
                                     int32_t* out_idx, const dsa_dims_t* dims, void* ws,
                                     size_t ws_bytes, void* stream);
 
+/*
+ * Several query tokens per batch row. Speculative (multi-token) decoding and
+ * prompt chunks bring T > 1 query tokens per sequence in one step; the CSA
+ * pull request's driver has a phase option (decode or prefill) and its
+ * review asks for prefill profiles. Reading: the T tokens of batch row b
+ * share its keys (k_idx[b] and kv_cmp[b]); each has its own indexer query
+ * and weights, its own score row and selection, its own attention query and
+ * window, and its own valid length. Token t of row b is query row b*T + t of
+ * every per-token tensor, and is computed exactly as one decode row. The
+ * indexer reads each key row once for all T tokens. 1 <= T <= 4.
+ *
+ * dsa_indexer_score_mt: q_idx bf16 [B, T, H_I, D_I]; k_idx bf16 [B, N, D_I];
+ *   w float [B, T, H_I]; scores float [B, T, N]. Shape limits as
+ *   dsa_indexer_score, with B*T*N < 2^31.
+ * dsa_sparse_attend_mt: q bf16 [B, T, H_q, D]; kv_cmp bf16 [B, N, D]; idx
+ *   int32 [B, T, k] (negative: empty slot); kv_win bf16 [B, T, W, D] (may be
+ *   NULL iff W == 0); out bf16 [B, T, H_q, D]; dims->batch = B (rows of
+ *   kv_cmp), B*T <= 65535. Workspace: dsa_sparse_attend_mt_workspace_bytes.
+ * dsa_decode_step_mt: the step over those tensors, with lengths int32 [B, T]
+ *   in device memory (token t of row b looks at its first lengths[b*T+t]
+ *   positions, as dsa_decode_step_ragged) or NULL for full rows; out_idx
+ *   int32 [B, T, k] or NULL. Workspace: dsa_decode_step_mt_workspace_bytes.
+ * With T == 1 each call computes exactly what its one-token counterpart does.
+ */
+DSA_EXPORT dsa_status_t dsa_indexer_score_mt(const void* q_idx, const void* k_idx,
+                                  const float* w, float* scores, int B, int T, int N,
+                                  int H_I, int D_I, void* stream);
+DSA_EXPORT size_t dsa_sparse_attend_mt_workspace_bytes(const dsa_dims_t* dims, int T);
+DSA_EXPORT dsa_status_t dsa_sparse_attend_mt(const void* q, const void* kv_cmp,
+                                  const int32_t* idx, const void* kv_win, void* out,
+                                  const dsa_dims_t* dims, int T, void* ws, size_t ws_bytes,
+                                  void* stream);
+DSA_EXPORT size_t dsa_decode_step_mt_workspace_bytes(const dsa_dims_t* dims, int T);
+DSA_EXPORT dsa_status_t dsa_decode_step_mt(const void* q_idx, const void* k_idx,
+                                const float* w, const void* q, const void* kv_cmp,
+                                const void* kv_win, const int32_t* lengths, void* out,
+                                int32_t* out_idx, const dsa_dims_t* dims, int T, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 DSA_EXPORT const char* dsa_status_string(dsa_status_t status);
 

@@ -8,10 +8,14 @@ from .binding import (  # noqa: F401
     DsaDims,
     DsaError,
     dsa_decode_step,
+    dsa_decode_step_mt,
+    dsa_decode_step_mt_workspace_bytes,
     dsa_decode_step_ragged,
     dsa_decode_step_workspace_bytes,
     dsa_indexer_score,
+    dsa_indexer_score_mt,
     dsa_sparse_attend,
+    dsa_sparse_attend_mt,
     dsa_sparse_attend_workspace_bytes,
     dsa_topk,
     dsa_topk_ragged,

@@ -29,6 +29,11 @@ EXPORTED = (
     "dsa_decode_step",
     "dsa_topk_ragged",
     "dsa_decode_step_ragged",
+    "dsa_indexer_score_mt",
+    "dsa_sparse_attend_mt_workspace_bytes",
+    "dsa_sparse_attend_mt",
+    "dsa_decode_step_mt_workspace_bytes",
+    "dsa_decode_step_mt",
     "dsa_status_string",
 )
 
@@ -81,6 +86,16 @@ def _load() -> ctypes.CDLL:
     lib.dsa_topk_ragged.restype = I
     lib.dsa_decode_step_ragged.argtypes = [P, P, P, P, P, P, P, P, P, D, P, S, P]
     lib.dsa_decode_step_ragged.restype = I
+    lib.dsa_indexer_score_mt.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.dsa_indexer_score_mt.restype = I
+    lib.dsa_sparse_attend_mt_workspace_bytes.argtypes = [D, I]
+    lib.dsa_sparse_attend_mt_workspace_bytes.restype = S
+    lib.dsa_sparse_attend_mt.argtypes = [P, P, P, P, P, D, I, P, S, P]
+    lib.dsa_sparse_attend_mt.restype = I
+    lib.dsa_decode_step_mt_workspace_bytes.argtypes = [D, I]
+    lib.dsa_decode_step_mt_workspace_bytes.restype = S
+    lib.dsa_decode_step_mt.argtypes = [P, P, P, P, P, P, P, P, P, D, I, P, S, P]
+    lib.dsa_decode_step_mt.restype = I
     lib.dsa_status_string.argtypes = [I]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -148,6 +163,22 @@ def dsa_indexer_score(q_idx, k_idx, w, scores=None, stream=None):
     _need(scores, "scores", torch.float32, (B, N))
     _check(LIB.dsa_indexer_score(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, N, H, DI,
                                  _stream(stream)), "dsa_indexer_score")
+    return scores
+
+
+def dsa_indexer_score_mt(q_idx, k_idx, w, scores=None, stream=None):
+    """T query tokens per batch row sharing its keys: q_idx bf16 [B,T,H,D_I],
+    k_idx [B,N,D_I], w float32 [B,T,H] -> scores float32 [B,T,N]."""
+    B, T, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, DI))
+    _need(w, "w", torch.float32, (B, T, H))
+    if scores is None:
+        scores = torch.empty((B, T, N), dtype=torch.float32, device=q_idx.device)
+    _need(scores, "scores", torch.float32, (B, T, N))
+    _check(LIB.dsa_indexer_score_mt(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, T, N, H,
+                                    DI, _stream(stream)), "dsa_indexer_score_mt")
     return scores
 
 
@@ -228,6 +259,30 @@ def dsa_sparse_attend(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, s
     return out
 
 
+def dsa_sparse_attend_mt(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, stream=None):
+    """T query tokens per batch row sharing its compressed rows: q bf16
+    [B,T,H_q,D], kv_cmp [B,N,D], idx int32 [B,T,k], kv_win [B,T,W,D] or None
+    -> bf16 [B,T,H_q,D]."""
+    B, T, Hq, D = q.shape
+    N = kv_cmp.shape[1]
+    k = idx.shape[2]
+    W = 0 if kv_win is None else kv_win.shape[2]
+    _need(q, "q", torch.bfloat16)
+    _need(kv_cmp, "kv_cmp", torch.bfloat16, (B, N, D))
+    _need(idx, "idx", torch.int32, (B, T, k))
+    if kv_win is not None:
+        _need(kv_win, "kv_win", torch.bfloat16, (B, T, W, D))
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, T, Hq, D))
+    dims = make_dims(B, N, 1, 128, k, W, Hq, D, scale)
+    ws = _workspace(LIB.dsa_sparse_attend_mt_workspace_bytes(ctypes.byref(dims), T), q.device, ws)
+    _check(LIB.dsa_sparse_attend_mt(_ptr(q), _ptr(kv_cmp), _ptr(idx), _ptr(kv_win if W else None),
+                                    _ptr(out), ctypes.byref(dims), T, _ptr(ws), ws.numel(),
+                                    _stream(stream)), "dsa_sparse_attend_mt")
+    return out
+
+
 # ------------------------------------------------------------------ fused step
 
 def dsa_decode_step_workspace_bytes(dims: DsaDims) -> int:
@@ -283,4 +338,43 @@ def _step(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k, scale, out, out_idx, w
                                           _ptr(lengths), _ptr(out), _ptr(out_idx),
                                           ctypes.byref(dims), _ptr(ws), ws.numel(),
                                           _stream(stream)), "dsa_decode_step_ragged")
+    return (out, out_idx) if out_idx is not None else out
+
+
+def dsa_decode_step_mt_workspace_bytes(dims: DsaDims, T: int) -> int:
+    return int(LIB.dsa_decode_step_mt_workspace_bytes(ctypes.byref(dims), int(T)))
+
+
+def dsa_decode_step_mt(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, lengths=None,
+                       out=None, out_idx=None, ws=None, stream=None, return_idx: bool = False):
+    """The step with T query tokens per batch row sharing its keys: q_idx
+    bf16 [B,T,H_I,D_I], k_idx [B,N,D_I], w float32 [B,T,H_I], q [B,T,H_q,D],
+    kv_cmp [B,N,D], kv_win [B,T,W,D] or None, lengths int32 [B,T] or None
+    -> out bf16 [B,T,H_q,D] (and idx int32 [B,T,k])."""
+    B, T, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq, D = q.shape[2], q.shape[3]
+    W = 0 if kv_win is None else kv_win.shape[2]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, DI))
+    _need(w, "w", torch.float32, (B, T, H))
+    _need(q, "q", torch.bfloat16, (B, T, Hq, D))
+    _need(kv_cmp, "kv_cmp", torch.bfloat16, (B, N, D))
+    if kv_win is not None:
+        _need(kv_win, "kv_win", torch.bfloat16, (B, T, W, D))
+    if lengths is not None:
+        _need(lengths, "lengths", torch.int32, (B, T))
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (B, T, Hq, D))
+    if return_idx and out_idx is None:
+        out_idx = torch.empty((B, T, k), dtype=torch.int32, device=q.device)
+    if out_idx is not None:
+        _need(out_idx, "out_idx", torch.int32, (B, T, k))
+    dims = make_dims(B, N, H, DI, k, W, Hq, D, scale)
+    ws = _workspace(LIB.dsa_decode_step_mt_workspace_bytes(ctypes.byref(dims), T), q.device, ws)
+    _check(LIB.dsa_decode_step_mt(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
+                                  _ptr(kv_win if W else None), _ptr(lengths), _ptr(out),
+                                  _ptr(out_idx), ctypes.byref(dims), T, _ptr(ws), ws.numel(),
+                                  _stream(stream)), "dsa_decode_step_mt")
     return (out, out_idx) if out_idx is not None else out

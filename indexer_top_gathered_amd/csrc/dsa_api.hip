@@ -42,11 +42,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 dsa_status_t to_status(hipError_t e) { return e == hipSuccess ? DSA_SUCCESS : DSA_ERROR_LAUNCH; }
 
-// Shape checks of the indexer stage.
-dsa_status_t check_indexer_shape(int B, int N, int H, int DI) {
-  if (B < 1 || N < 1 || H < 1 || DI < 1) return DSA_ERROR_INVALID_VALUE;
-  if (DI != 128 || H > 64) return DSA_ERROR_NOT_SUPPORTED;
-  if ((long long)B * N > 0x7FFFFFFFLL) return DSA_ERROR_NOT_SUPPORTED;
+// Shape checks of the indexer stage (T query tokens per batch row).
+dsa_status_t check_indexer_shape(int B, int N, int H, int DI, int T = 1) {
+  if (B < 1 || N < 1 || H < 1 || DI < 1 || T < 1) return DSA_ERROR_INVALID_VALUE;
+  if (DI != 128 || H > 64 || T > kMaxTokens) return DSA_ERROR_NOT_SUPPORTED;
+  if ((long long)B * T * N > 0x7FFFFFFFLL || B > 65535) return DSA_ERROR_NOT_SUPPORTED;
   return DSA_SUCCESS;
 }
 
@@ -72,22 +72,30 @@ dsa_status_t check_attend_dims(const dsa_dims_t* d) {
   return DSA_SUCCESS;
 }
 
-// Workspace layout of the fused step.
+// The attention dims of T query tokens per batch row: one query row each.
+dsa_dims_t query_rows(const dsa_dims_t& d, int T) {
+  dsa_dims_t r = d;
+  r.batch = (int32_t)((long long)d.batch * T > 0x7FFFFFFFLL ? 0x7FFFFFFF : d.batch * T);
+  return r;
+}
+
+// Workspace layout of the fused step (T query tokens per batch row).
 struct StepLayout {
   size_t scores_off, idx_off, topk_off, attend_off, bytes;
   TopkPlan tk;
   AttendPlan at;
 };
 
-StepLayout step_layout(const dsa_dims_t& d) {
+StepLayout step_layout(const dsa_dims_t& d, int T) {
   StepLayout L{};
-  L.tk = plan_topk(d.batch, d.n, d.topk, DSA_F32);
-  L.at = plan_attend(d);
+  const dsa_dims_t dq = query_rows(d, T);
+  L.tk = plan_topk(dq.batch, d.n, d.topk, DSA_F32);
+  L.at = plan_attend(dq);
   size_t off = 0;
   L.scores_off = off;
-  off = align_up(off + (size_t)d.batch * d.n * sizeof(float), 256);
+  off = align_up(off + (size_t)dq.batch * d.n * sizeof(float), 256);
   L.idx_off = off;
-  off = align_up(off + (size_t)d.batch * d.topk * sizeof(int32_t), 256);
+  off = align_up(off + (size_t)dq.batch * d.topk * sizeof(int32_t), 256);
   L.topk_off = off;
   off = align_up(off + L.tk.bytes, 256);
   L.attend_off = off;
@@ -124,7 +132,23 @@ dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, const float
   if (s != DSA_SUCCESS) return s;
   return to_status(launch_indexer_score(static_cast<const uint16_t*>(q_idx),
                                         static_cast<const uint16_t*>(k_idx), w, scores, B, N,
-                                        H_I, nullptr, static_cast<hipStream_t>(stream)));
+                                        H_I, 1, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+dsa_status_t dsa_indexer_score_mt(const void* q_idx, const void* k_idx, const float* w,
+                                  float* scores, int B, int T, int N, int H_I, int D_I,
+                                  void* stream) {
+  if (!q_idx || !k_idx || !w || !scores) return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(scores) ||
+      (reinterpret_cast<uintptr_t>(w) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
+  dsa_status_t s = check_indexer_shape(B, N, H_I, D_I, T);
+  if (s != DSA_SUCCESS) return s;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  return to_status(launch_indexer_score(static_cast<const uint16_t*>(q_idx),
+                                        static_cast<const uint16_t*>(k_idx), w, scores, B, N,
+                                        H_I, T, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
@@ -176,35 +200,57 @@ dsa_status_t dsa_topk_ragged(const void* scores, dsa_dtype_t dtype, int B, int N
 }
 
 size_t dsa_sparse_attend_workspace_bytes(const dsa_dims_t* dims) {
-  if (check_attend_dims(dims) != DSA_SUCCESS) return 0;
+  return dsa_sparse_attend_mt_workspace_bytes(dims, 1);
+}
+
+size_t dsa_sparse_attend_mt_workspace_bytes(const dsa_dims_t* dims, int T) {
+  if (!dims || T < 1 || T > kMaxTokens) return 0;
+  const dsa_dims_t dq = query_rows(*dims, T);
+  if (check_attend_dims(&dq) != DSA_SUCCESS) return 0;
   // Never report 0 for a valid shape, so a zero result always means "invalid".
-  const size_t b = plan_attend(*dims).bytes;
+  const size_t b = plan_attend(dq).bytes;
   return b ? b : 256;
 }
 
 dsa_status_t dsa_sparse_attend(const void* q, const void* kv_cmp, const int32_t* idx,
                                const void* kv_win, void* out, const dsa_dims_t* dims, void* ws,
                                size_t ws_bytes, void* stream) {
-  dsa_status_t s = check_attend_dims(dims);
+  return dsa_sparse_attend_mt(q, kv_cmp, idx, kv_win, out, dims, 1, ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_sparse_attend_mt(const void* q, const void* kv_cmp, const int32_t* idx,
+                                  const void* kv_win, void* out, const dsa_dims_t* dims, int T,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  if (!dims || T < 1) return DSA_ERROR_INVALID_VALUE;
+  if (T > kMaxTokens) return DSA_ERROR_NOT_SUPPORTED;
+  const dsa_dims_t dq = query_rows(*dims, T);
+  dsa_status_t s = check_attend_dims(&dq);
   if (s != DSA_SUCCESS) return s;
   if (!q || !kv_cmp || !idx || !out || !ws || (dims->window > 0 && !kv_win))
     return DSA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(kv_cmp) || !aligned16(out) || !aligned16(ws) ||
       (kv_win && !aligned16(kv_win)) || (reinterpret_cast<uintptr_t>(idx) & 3u))
     return DSA_ERROR_INVALID_VALUE;
-  const AttendPlan plan = plan_attend(*dims);
+  const AttendPlan plan = plan_attend(dq);
   if (ws_bytes < (plan.bytes ? plan.bytes : 256)) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();
   if (s != DSA_SUCCESS) return s;
   return to_status(launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp),
                                  idx, static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out),
-                                 *dims, plan, ws, static_cast<hipStream_t>(stream)));
+                                 dq, plan, T, ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t dsa_decode_step_workspace_bytes(const dsa_dims_t* dims) {
-  if (check_attend_dims(dims) != DSA_SUCCESS) return 0;
-  if (check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim) != DSA_SUCCESS) return 0;
-  return step_layout(*dims).bytes;
+  return dsa_decode_step_mt_workspace_bytes(dims, 1);
+}
+
+size_t dsa_decode_step_mt_workspace_bytes(const dsa_dims_t* dims, int T) {
+  if (!dims || T < 1 || T > kMaxTokens) return 0;
+  const dsa_dims_t dq = query_rows(*dims, T);
+  if (check_attend_dims(&dq) != DSA_SUCCESS) return 0;
+  if (check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim, T) != DSA_SUCCESS)
+    return 0;
+  return step_layout(*dims, T).bytes;
 }
 
 }  // extern "C"
@@ -213,19 +259,23 @@ namespace {
 
 dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, const void* q,
                        const void* kv_cmp, const void* kv_win, const int32_t* lengths, void* out,
-                       int32_t* out_idx, const dsa_dims_t* dims, void* ws, size_t ws_bytes,
-                       void* stream) {
-  dsa_status_t s = check_attend_dims(dims);
+                       int32_t* out_idx, const dsa_dims_t* dims, int T, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!dims || T < 1) return DSA_ERROR_INVALID_VALUE;
+  if (T > kMaxTokens) return DSA_ERROR_NOT_SUPPORTED;
+  const dsa_dims_t dq = query_rows(*dims, T);
+  dsa_status_t s = check_attend_dims(&dq);
   if (s != DSA_SUCCESS) return s;
-  s = check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim);
+  s = check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim, T);
   if (s != DSA_SUCCESS) return s;
   if (!q_idx || !k_idx || !w || !q || !kv_cmp || !out || !ws || (dims->window > 0 && !kv_win))
     return DSA_ERROR_INVALID_VALUE;
   if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(kv_cmp) ||
       !aligned16(out) || !aligned16(ws) || (kv_win && !aligned16(kv_win)) ||
-      (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(out_idx) & 3u))
+      (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(out_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lengths) & 3u))
     return DSA_ERROR_INVALID_VALUE;
-  const StepLayout L = step_layout(*dims);
+  const StepLayout L = step_layout(*dims, T);
   if (ws_bytes < L.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();
   if (s != DSA_SUCCESS) return s;
@@ -236,13 +286,13 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
   const dsa_dims_t& d = *dims;
   hipError_t e = launch_indexer_score(static_cast<const uint16_t*>(q_idx),
                                       static_cast<const uint16_t*>(k_idx), w, scores, d.batch, d.n,
-                                      d.idx_heads, lengths, st);
+                                      d.idx_heads, T, lengths, st);
   if (e != hipSuccess) return DSA_ERROR_LAUNCH;
-  e = launch_topk(scores, DSA_F32, d.batch, d.n, d.topk, sel, nullptr, 0, lengths, L.tk,
+  e = launch_topk(scores, DSA_F32, dq.batch, d.n, d.topk, sel, nullptr, 0, lengths, L.tk,
                   base + L.topk_off, st);
   if (e != hipSuccess) return DSA_ERROR_LAUNCH;
   e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp), sel,
-                    static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), d, L.at,
+                    static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), dq, L.at, T,
                     base + L.attend_off, st);
   return to_status(e);
 }
@@ -254,8 +304,8 @@ extern "C" {
 dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* w, const void* q,
                              const void* kv_cmp, const void* kv_win, void* out, int32_t* out_idx,
                              const dsa_dims_t* dims, void* ws, size_t ws_bytes, void* stream) {
-  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx, dims, ws, ws_bytes,
-                   stream);
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx, dims, 1, ws,
+                   ws_bytes, stream);
 }
 
 dsa_status_t dsa_decode_step_ragged(const void* q_idx, const void* k_idx, const float* w,
@@ -263,9 +313,18 @@ dsa_status_t dsa_decode_step_ragged(const void* q_idx, const void* k_idx, const 
                                     const int32_t* lengths, void* out, int32_t* out_idx,
                                     const dsa_dims_t* dims, void* ws, size_t ws_bytes,
                                     void* stream) {
-  if (!lengths || (reinterpret_cast<uintptr_t>(lengths) & 3u)) return DSA_ERROR_INVALID_VALUE;
-  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims, ws, ws_bytes,
-                   stream);
+  if (!lengths) return DSA_ERROR_INVALID_VALUE;
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims, 1, ws,
+                   ws_bytes, stream);
+}
+
+dsa_status_t dsa_decode_step_mt(const void* q_idx, const void* k_idx, const float* w,
+                                const void* q, const void* kv_cmp, const void* kv_win,
+                                const int32_t* lengths, void* out, int32_t* out_idx,
+                                const dsa_dims_t* dims, int T, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims, T, ws,
+                   ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -180,11 +180,14 @@ __device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error. Arguments are already checked.
 
-// lengths: int32 [B] in device memory, or NULL for full rows; with it,
-// scores at or past row b's length are not written.
+// tokens (1..kMaxTokens) query tokens per batch row share its keys: q
+// [B, tokens, H, 128], w [B, tokens, H], s [B, tokens, N]. lengths: int32
+// [B, tokens] in device memory, or NULL for full rows; with it, a token's
+// scores at or past its length are not written.
+constexpr int kMaxTokens = 4;
 hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const float* w,
-                                float* s, int B, int N, int H, const int32_t* lengths,
-                                hipStream_t st);
+                                float* s, int B, int N, int H, int tokens,
+                                const int32_t* lengths, hipStream_t st);
 
 struct TopkPlan {
   bool fused;       // one workgroup per row does everything (no second kernel)
@@ -212,8 +215,10 @@ struct AttendPlan {
   size_t bytes;
 };
 AttendPlan plan_attend(const dsa_dims_t& d);
+// d.batch counts query rows; tokens consecutive query rows share one row of
+// kv (kv holds d.batch / tokens rows).
 hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                          const uint16_t* win, uint16_t* out, const dsa_dims_t& d,
-                         const AttendPlan& plan, void* ws, hipStream_t st);
+                         const AttendPlan& plan, int tokens, void* ws, hipStream_t st);
 
 }  // namespace dsa

@@ -152,11 +152,159 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
   }
 }
 
+// Several query tokens per batch row (draft tokens, or a chunk of a prompt)
+// share the row's keys. The workgroup streams and stages each key step once,
+// exactly as above, and scores it for every token in turn, so the keys are
+// read from HBM once for all the tokens. Registers hold one token's query
+// fragments, so all the tokens' query rows and weights are staged in LDS at
+// the start (rows padded to 272 B: the 16 lanes of a fragment read land on
+// different banks) and each token's are read back per step. Per token the
+// arithmetic and its order are those of the one-token kernel.
+constexpr int kQPitch = kDI * 2 + 16;  // bytes per staged query row
+
+template <int MT>
+__global__ __launch_bounds__(kIsThreads) void indexer_score_mt_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ w, float* __restrict__ s, int N, int H, int T, int keys_per_wg,
+    const int32_t* __restrict__ lengths) {
+  extern __shared__ u32x4 lds_mt[];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int m = lane & 15;
+  const int g = lane >> 4;
+
+  // Each token's valid length; the keys swept are those of the longest.
+  int tlen[kMaxTokens];
+  int rmax = 0;
+#pragma unroll
+  for (int t = 0; t < kMaxTokens; ++t) {
+    tlen[t] = t < T ? (lengths ? min(max(lengths[b * T + t], 0), N) : N) : 0;
+    rmax = max(rmax, tlen[t]);
+  }
+  const int start = blockIdx.x * keys_per_wg;
+  if (start >= rmax) return;  // uniform
+  const int end = min(rmax, start + keys_per_wg);
+
+  // LDS: the 8 waves' key stages (8 KB each), then the query rows of all
+  // tokens (T x MT*16 rows of kQPitch bytes, zero past H), then the weights.
+  constexpr int kRowsPerToken = MT * 16;
+  u32x4* st = lds_mt + wave * (32 * 16);
+  char* qs = reinterpret_cast<char*>(lds_mt + kIsWaves * 32 * 16);
+  float* wl = reinterpret_cast<float*>(qs + (size_t)T * kRowsPerToken * kQPitch);
+  for (int c = threadIdx.x; c < T * kRowsPerToken * 16; c += kIsThreads) {
+    const int row = c >> 4, chunk = c & 15;
+    const int t = row / kRowsPerToken, head = row % kRowsPerToken;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (head < H)
+      v = *reinterpret_cast<const u32x4*>(q + (((size_t)b * T + t) * H + head) * kDI + chunk * 8);
+    *reinterpret_cast<u32x4*>(qs + (size_t)row * kQPitch + chunk * 16) = v;
+  }
+  for (int i = threadIdx.x; i < T * kRowsPerToken; i += kIsThreads) {
+    const int t = i / kRowsPerToken, head = i % kRowsPerToken;
+    wl[i] = head < H ? w[((size_t)b * T + t) * H + head] : 0.0f;
+  }
+  __syncthreads();
+
+  const uint16_t* krow = k + (size_t)b * N * kDI;
+  auto load_step = [&](u32x4 (&r)[8], int key0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = min(key0 + 4 * j + (lane >> 4), end - 1);
+      r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (size_t)key * kDI) + (lane & 15));
+    }
+  };
+  auto score_step = [&](const u32x4 (&r)[8], int key0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int qk = 4 * j + (lane >> 4);
+      st[qk * 16 + ((lane & 15) ^ (qk & 15))] = r[j];
+    }
+    bf16x8 kb[kIsTiles][4];
+#pragma unroll
+    for (int tt = 0; tt < kIsTiles; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int qk = 16 * tt + m;
+        kb[tt][kk] = __builtin_bit_cast(bf16x8, st[qk * 16 + ((4 * kk + g) ^ m)]);
+      }
+    for (int t = 0; t < T; ++t) {
+      // One 16-head tile at a time, so that only its query fragments are
+      // live; each accumulator still takes the k-steps in order.
+      const char* qt = qs + (size_t)t * kRowsPerToken * kQPitch;
+      f32x4 acc[kIsTiles][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        bf16x8 qa[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          qa[kk] = *reinterpret_cast<const bf16x8*>(qt + (size_t)(mt * 16 + m) * kQPitch + kk * 64 + g * 16);
+#pragma unroll
+        for (int tt = 0; tt < kIsTiles; ++tt) acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int tt = 0; tt < kIsTiles; ++tt) acc[tt][mt] = mfma16x16x32(qa[kk], kb[tt][kk], acc[tt][mt]);
+      }
+      float p[kIsTiles] = {0.0f, 0.0f};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float4 wq = *reinterpret_cast<const float4*>(wl + t * kRowsPerToken + mt * 16 + g * 4);
+        const float wv[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+        for (int tt = 0; tt < kIsTiles; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p[tt] += wv[i] * fmaxf(acc[tt][mt][i], 0.0f);
+      }
+      float mine = (g & 1) ? p[1] : p[0];
+      const float other = (g & 1) ? p[0] : p[1];
+      mine += lane_xor16(other);
+      mine += lane_xor32(mine);
+      int tl = tlen[0];
+#pragma unroll
+      for (int u = 1; u < kMaxTokens; ++u) tl = t == u ? tlen[u] : tl;
+      if (g < 2) {
+        const int key = key0 + g * 16 + m;
+        if (key < tl) s[((size_t)b * T + t) * N + key] = mine;
+      }
+    }
+  };
+  u32x4 ra[8], rb[8], rc[8];
+  int key0 = start + wave * kIsKeysPerStep;
+  const int nsteps = key0 < end ? (end - key0 + kIsKeysPerRound - 1) / kIsKeysPerRound : 0;
+  if (nsteps > 0) load_step(ra, key0);
+  if (nsteps > 1) load_step(rb, key0 + kIsKeysPerRound);
+  for (int i = 0; i < nsteps; i += 3) {
+    if (i + 2 < nsteps) load_step(rc, key0 + (i + 2) * kIsKeysPerRound);
+    score_step(ra, key0 + i * kIsKeysPerRound);
+    if (i + 1 >= nsteps) break;
+    if (i + 3 < nsteps) load_step(ra, key0 + (i + 3) * kIsKeysPerRound);
+    score_step(rb, key0 + (i + 1) * kIsKeysPerRound);
+    if (i + 2 >= nsteps) break;
+    if (i + 4 < nsteps) load_step(rb, key0 + (i + 4) * kIsKeysPerRound);
+    score_step(rc, key0 + (i + 2) * kIsKeysPerRound);
+  }
+}
+
+template <int MT>
+hipError_t launch_mt(const uint16_t* q, const uint16_t* k, const float* w, float* s, int N, int H,
+                     int T, int keys_per_wg, const int32_t* lengths, dim3 grid, hipStream_t st) {
+  const size_t lds = (size_t)kIsWaves * 32 * 16 * sizeof(u32x4) +
+                     (size_t)T * MT * 16 * (kQPitch + sizeof(float));
+  auto kern = indexer_score_mt_kernel<MT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(kIsThreads), lds, st, q, k, w, s, N, H, T, keys_per_wg,
+                     lengths);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const float* w,
-                                float* s, int B, int N, int H, const int32_t* lengths,
-                                hipStream_t st) {
+                                float* s, int B, int N, int H, int tokens,
+                                const int32_t* lengths, hipStream_t st) {
   // Each wave keeps its query fragments (up to 16 KB per batch row) in
   // registers for its whole sweep. Aim for one round of about 256 workgroups
   // (one per CU measured fastest), each sweeping at most 32 rounds of 256
@@ -174,6 +322,14 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
   dim3 grid((N + keys_per_wg - 1) / keys_per_wg, B);
   dim3 block(kIsThreads);
   const int mt = (H + 15) / 16;
+  if (tokens > 1) {
+    switch (mt) {
+      case 1: return launch_mt<1>(q, k, w, s, N, H, tokens, keys_per_wg, lengths, grid, st);
+      case 2: return launch_mt<2>(q, k, w, s, N, H, tokens, keys_per_wg, lengths, grid, st);
+      case 3: return launch_mt<3>(q, k, w, s, N, H, tokens, keys_per_wg, lengths, grid, st);
+      default: return launch_mt<4>(q, k, w, s, N, H, tokens, keys_per_wg, lengths, grid, st);
+    }
+  }
   switch (mt) {
     case 1: hipLaunchKernelGGL(indexer_score_kernel<1>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
     case 2: hipLaunchKernelGGL(indexer_score_kernel<2>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
     uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
     int N, int k, int W, int Hq, float scale, int rows_per_split, int splits, int nitems,
-    int hgroups) {
+    int hgroups, int tokens) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int THREADS = WAVES * kWave;
   constexpr int HW = HG * 16;           // query heads per workgroup
@@ -101,7 +101,9 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
 
   const int ntiles = (r1 - r0 + kTile - 1) / kTile;
   const int32_t* irow = idx + (size_t)b * k;
-  const uint16_t* kvb = kv + (size_t)b * N * D;
+  // Query row b is token b % tokens of batch row b / tokens, whose
+  // compressed rows it gathers from.
+  const uint16_t* kvb = kv + (size_t)(b / tokens) * N * D;
   const uint16_t* winb = win ? win + (size_t)b * W * D : nullptr;
 
   // The first two tiles' copies go out first, their row indices read with
@@ -468,7 +470,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 template <int D, int HG, int DSPLIT>
 hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                            const uint16_t* win, uint16_t* out, uint16_t* po, float* pml,
-                           const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
+                           const dsa_dims_t& d, const AttendPlan& p, int tokens, hipStream_t st) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int ROW_WORDS = D / 2 + 4;
   constexpr int XWORDS = DSPLIT > 1 ? 2 * WAVES * kWave * 8 : 0;
@@ -483,7 +485,7 @@ hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t*
   const int grid = (nitems + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
                      pml, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split, p.splits,
-                     nitems, hgroups);
+                     nitems, hgroups, tokens);
   return hipGetLastError();
 }
 
@@ -516,19 +518,19 @@ AttendPlan plan_attend(const dsa_dims_t& d) {
 
 hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                          const uint16_t* win, uint16_t* out, const dsa_dims_t& d,
-                         const AttendPlan& p, void* ws, hipStream_t st) {
+                         const AttendPlan& p, int tokens, void* ws, hipStream_t st) {
   uint16_t* po = p.splits > 1 ? reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
   float* pml = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const int hgw = p.heads_per_wg / 16;  // 16-head groups per workgroup
   hipError_t e;
   if (d.head_dim == 512) {
-    if (hgw == 4) e = launch_attend_t<512, 4, 2>(q, kv, idx, win, out, po, pml, d, p, st);
-    else if (hgw == 2) e = launch_attend_t<512, 2, 2>(q, kv, idx, win, out, po, pml, d, p, st);
-    else e = launch_attend_t<512, 1, 2>(q, kv, idx, win, out, po, pml, d, p, st);
+    if (hgw == 4) e = launch_attend_t<512, 4, 2>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
+    else if (hgw == 2) e = launch_attend_t<512, 2, 2>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
+    else e = launch_attend_t<512, 1, 2>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
   } else {
-    if (hgw == 4) e = launch_attend_t<128, 4, 1>(q, kv, idx, win, out, po, pml, d, p, st);
-    else if (hgw == 2) e = launch_attend_t<128, 2, 1>(q, kv, idx, win, out, po, pml, d, p, st);
-    else e = launch_attend_t<128, 1, 1>(q, kv, idx, win, out, po, pml, d, p, st);
+    if (hgw == 4) e = launch_attend_t<128, 4, 1>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
+    else if (hgw == 2) e = launch_attend_t<128, 2, 1>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
+    else e = launch_attend_t<128, 1, 1>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
   }
   if (e != hipSuccess || p.splits == 1) return e;
   const int Hq = d.q_heads;

@@ -106,6 +106,23 @@ def step_inputs(s: StepShape, seed_base: int, device="cpu") -> dict:
     return out
 
 
+def mt_step_inputs(s: StepShape, T: int, seed_base: int, device="cpu") -> dict:
+    """Inputs of a step with T query tokens per batch row: the keys (k_idx,
+    kv_cmp) per row as step_inputs, the per-token tensors with a token axis
+    after the batch axis (q_idx [B,T,H_I,D_I], w [B,T,H_I], q [B,T,H_q,D],
+    kv_win [B,T,W,D]); same distributions as step_inputs."""
+    sb = seed_base
+    return {
+        "q_idx": _normal((s.B, T, s.H_I, s.D_I), _gen(device, sb + 0), device, torch.bfloat16),
+        "k_idx": _normal((s.B, s.N, s.D_I), _gen(device, sb + 1), device, torch.bfloat16),
+        "w": torch.rand((s.B, T, s.H_I), generator=_gen(device, sb + 2), device=device,
+                        dtype=torch.float32),
+        "q": _normal((s.B, T, s.H_q, s.D), _gen(device, sb + 3), device, torch.bfloat16),
+        "kv_cmp": _normal((s.B, s.N, s.D), _gen(device, sb + 4), device, torch.bfloat16),
+        "kv_win": _normal((s.B, T, s.W, s.D), _gen(device, sb + 5), device, torch.bfloat16),
+    }
+
+
 def ragged_lengths(B: int, N: int, k: int, seed: int) -> np.ndarray:
     """int32 [B] sequence lengths for a ragged batch: the edge values 0, 1,
     k - 1, k, k + 1 and N first (those within [0, N]), then lengths drawn

@@ -14,8 +14,11 @@ Printed: one JSON line. `value` is the step's effective bandwidth (its
 compulsory bytes - every input read once, the output written once - divided
 by the time per step), `us_per_step` the time per step, `roofline` the
 dominant kernel (indexer scoring) measured with HIP events on the stream it
-runs on, `topk` the top-k-only workload (bf16 64 x 131072, k=512), and
-`cpu_baseline` the CPU oracle timed on this host.
+runs on (with `measured_hbm`, the rates of a plain torch row reduction
+and copy on 1 GiB, and the indexer's fraction of that read rate),
+`single_call_latency` the median, p10 and p90 of single steps each run
+after a 512 MiB cache-evicting write, `topk` the top-k-only workload (bf16
+64 x 131072, k=512), and `cpu_baseline` the CPU oracle timed on this host.
 
 `--workload` times one of the other workloads instead (for profiling; one
 JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
@@ -51,6 +54,9 @@ def parse():
     p.add_argument("--copies", type=int, default=8, help="rotating input copies")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-topk", action="store_true")
+    p.add_argument("--latency-calls", type=int, default=100,
+                   help="single-call latency samples, each after a cache-evicting write "
+                        "(0 to skip)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
@@ -334,6 +340,60 @@ def traffic_from_profile(kernel_srcs):
         return None
 
 
+def single_call_latency(call, n: int, dev, stream) -> dict:
+    """Latency of one call from cold caches: before each call a 512 MiB
+    buffer is written (twice the 256 MB Infinity Cache, far beyond the L2s),
+    then the call alone is bracketed by events. Median, p10 and p90 in us."""
+    import torch
+    import numpy as np
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    samples = []
+    for i in range(n):
+        scratch.fill_(i & 0xFF)
+        e0.record(stream)
+        call(i)
+        e1.record(stream)
+        e1.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    a = np.array(samples)
+    return {"calls": n, "median_us": round(float(np.median(a)), 2),
+            "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2),
+            "eviction": "512 MiB device write before each call"}
+
+
+def bandwidth_probe(dev, stream) -> dict:
+    """Measured HBM rates of plain torch kernels on 1 GiB, for the roofline
+    fraction against what this GPU delivers as well as against 8 TB/s: a
+    read-only row reduction (sums of rows of 4096 floats; of the torch
+    reductions tried it streams fastest, a whole-tensor sum reaches about
+    two thirds of it) and a copy (read + write)."""
+    import torch
+    n = 1 << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name, fn, nbytes in (("read_GBps (row sums, 1 GiB)", lambda: x.view(-1, 4096).sum(1), n),
+                             ("copy_GBps (read + write, 1 GiB each)", lambda: y.copy_(x), 2 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        out[name] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    del x, y
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -402,6 +462,12 @@ def main():
                 "traffic": traffic, "kernel": "indexer_score_kernel<4>",
                 "us_per_launch": round(is_us, 3), "bytes_per_launch": is_bytes}
 
+    if args.latency_calls > 0:
+        probe = bandwidth_probe(dev, stream)
+        read = probe["read_GBps (row sums, 1 GiB)"]
+        roofline["measured_hbm"] = probe
+        roofline["frac_of_measured_read"] = round(achieved / read, 4)
+
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -414,6 +480,8 @@ def main():
         "roofline": roofline,
     }
     del scores
+    if args.latency_calls > 0:
+        line["single_call_latency"] = single_call_latency(step, args.latency_calls, dev, stream)
 
     if not args.no_topk:
         t = workloads.C2

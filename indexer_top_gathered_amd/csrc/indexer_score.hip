@@ -31,20 +31,21 @@ constexpr int kIsKeysPerStep = 16 * kIsTiles;     // keys per wave per step
 constexpr int kIsKeysPerRound = kIsWaves * kIsKeysPerStep;  // 256 per workgroup round
 constexpr int kDI = 128;
 
+// One workgroup's sweep over keys [start, end) of batch row b: start is a
+// multiple of 256 keys, end at most the row's valid length. st: this wave's
+// 8 KB LDS staging area.
 template <int MT>  // MT = number of 16-head tiles (1..4)
-__global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const float* __restrict__ w, float* __restrict__ s, int N, int H, int keys_per_wg,
-    const int32_t* __restrict__ lengths) {
-  const int b = blockIdx.y;
-  // Ragged rows: keys at or past the row's length are neither read nor
-  // scored. A workgroup wholly past it has nothing to do.
-  const int rlen = lengths ? min(max(lengths[b], 0), N) : N;
-  const int start = blockIdx.x * keys_per_wg;
-  if (start >= rlen) return;  // uniform
-  const int end = min(rlen, start + keys_per_wg);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+__device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
+                                          const uint16_t* __restrict__ k,
+                                          const float* __restrict__ w, float* __restrict__ s,
+                                          int b, int N, int H, int start, int end, u32x4* st) {
+  // The thread index passes through an empty asm statement, so that the
+  // values derived from it are formed per call: a caller that sweeps
+  // several rows in a loop does not keep them live across its iterations.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int m = lane & 15;
   const int g = lane >> 4;
 
@@ -79,12 +80,10 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
   // lane l: key 4j + l/16, 16-byte chunk l%16), then written to this wave's
   // LDS area with the chunk of key q at slot (chunk ^ q%16), so that the MFMA
   // fragment reads (16 different keys, one chunk) hit 16 different slots.
-  __shared__ u32x4 stage_lds[kIsWaves][32 * 16];  // 8 KB per wave: 32 keys x 16 chunks
-  u32x4* st = stage_lds[wave];
   auto load_step = [&](u32x4 (&r)[8], int key0) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int key = min(key0 + 4 * j + (lane >> 4), rlen - 1);
+      const int key = min(key0 + 4 * j + (lane >> 4), end - 1);
       r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (size_t)key * kDI) + (lane & 15));
     }
   };
@@ -130,7 +129,7 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
     mine += lane_xor32(mine);
     if (g < 2) {
       const int key = key0 + g * 16 + m;
-      if (key < rlen) srow[key] = mine;
+      if (key < end) srow[key] = mine;
     }
   };
   // Three register buffers in turn: two steps of loads in flight while one
@@ -149,6 +148,71 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
     if (i + 2 >= nsteps) break;
     if (i + 4 < nsteps) load_step(rb, key0 + (i + 4) * kIsKeysPerRound);
     score_step(rc, key0 + (i + 2) * kIsKeysPerRound);
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ w, float* __restrict__ s, int N, int H, int keys_per_wg) {
+  __shared__ u32x4 stage_lds[kIsWaves][32 * 16];  // 8 KB per wave: 32 keys x 16 chunks
+  const int b = blockIdx.y;
+  const int start = blockIdx.x * keys_per_wg;
+  const int end = min(N, start + keys_per_wg);
+  sweep_row<MT>(q, k, w, s, b, N, H, start, end, stage_lds[threadIdx.x / kWave]);
+}
+
+// Ragged rows (lengths given): keys at or past a row's length are neither
+// read nor scored. The rounds of 256 keys that hold valid keys, taken over
+// all rows in order, are split evenly over the workgroups, so every
+// workgroup streams about the same number of valid keys whatever the mix of
+// lengths; a workgroup's share may span rows, and it loads the query
+// fragments of each row it enters.
+__device__ __forceinline__ uint32_t valid_rounds(const int32_t* lengths, int b, int N) {
+  const int len = min(max(lengths[b], 0), N);
+  return (uint32_t)((len + kIsKeysPerRound - 1) / kIsKeysPerRound);
+}
+
+template <int MT>
+__global__ __launch_bounds__(kIsThreads) void indexer_score_ragged_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ w, float* __restrict__ s, int B, int N, int H,
+    const int32_t* __restrict__ lengths) {
+  __shared__ u32x4 stage_lds[kIsWaves][32 * 16];
+  const int lane = threadIdx.x & (kWave - 1);
+  // Every wave derives the same split: all rows' valid rounds, then this
+  // workgroup's range [lo, hi) of them.
+  uint32_t total = 0;
+  for (int b0 = 0; b0 < B; b0 += kWave) {
+    const uint32_t r = b0 + lane < B ? valid_rounds(lengths, b0 + lane, N) : 0u;
+    total += wave_reduce<OpAdd>(r);
+  }
+  const uint32_t lo = (uint32_t)((uint64_t)blockIdx.x * total / gridDim.x);
+  const uint32_t hi = (uint32_t)((uint64_t)(blockIdx.x + 1) * total / gridDim.x);
+  if (lo >= hi) return;  // uniform
+  // Walk this range a row at a time. Only wave-uniform values (the next
+  // round, and the first row and cumulative rounds of the current chunk of
+  // 64 rows) live across a row's sweep.
+  uint32_t cur = lo;
+  int b0 = 0;
+  uint32_t base = 0;
+  while (cur < hi && b0 < B) {
+    const uint32_t r = b0 + lane < B ? valid_rounds(lengths, b0 + lane, N) : 0u;
+    const uint32_t incl = base + wave_scan_incl(r);
+    const uint64_t past = __ballot(incl <= cur);  // rows wholly before cur
+    if (past == ~0ull) {  // cur lies beyond this chunk
+      base = lane_read(incl, kWave - 1);
+      b0 += kWave;
+      continue;
+    }
+    const int j = __builtin_ctzll(~past);  // the row holding round cur
+    const uint32_t e0 = lane_read(incl - r, j), e1 = lane_read(incl, j);
+    const int b = b0 + j;
+    const int len = min(max(lengths[b], 0), N);
+    const int start = (int)((cur - e0) * kIsKeysPerRound);
+    const int end = min(len, (int)((min(hi, e1) - e0) * kIsKeysPerRound));
+    sweep_row<MT>(q, k, w, s, b, N, H, start, end, stage_lds[threadIdx.x / kWave]);
+    cur = min(hi, e1);
   }
 }
 
@@ -330,11 +394,23 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
       default: return launch_mt<4>(q, k, w, s, N, H, tokens, keys_per_wg, lengths, grid, st);
     }
   }
+  if (lengths) {
+    // One workgroup per CU (fewer when the rows hold fewer rounds in all),
+    // each taking an equal share of the valid rounds.
+    const dim3 rgrid((unsigned)(total_rounds < 256 ? total_rounds : 256));
+    switch (mt) {
+      case 1: hipLaunchKernelGGL(indexer_score_ragged_kernel<1>, rgrid, block, 0, st, q, k, w, s, B, N, H, lengths); break;
+      case 2: hipLaunchKernelGGL(indexer_score_ragged_kernel<2>, rgrid, block, 0, st, q, k, w, s, B, N, H, lengths); break;
+      case 3: hipLaunchKernelGGL(indexer_score_ragged_kernel<3>, rgrid, block, 0, st, q, k, w, s, B, N, H, lengths); break;
+      default: hipLaunchKernelGGL(indexer_score_ragged_kernel<4>, rgrid, block, 0, st, q, k, w, s, B, N, H, lengths); break;
+    }
+    return hipGetLastError();
+  }
   switch (mt) {
-    case 1: hipLaunchKernelGGL(indexer_score_kernel<1>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
-    case 2: hipLaunchKernelGGL(indexer_score_kernel<2>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
-    case 3: hipLaunchKernelGGL(indexer_score_kernel<3>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
-    default: hipLaunchKernelGGL(indexer_score_kernel<4>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg, lengths); break;
+    case 1: hipLaunchKernelGGL(indexer_score_kernel<1>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
+    case 2: hipLaunchKernelGGL(indexer_score_kernel<2>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
+    case 3: hipLaunchKernelGGL(indexer_score_kernel<3>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
+    default: hipLaunchKernelGGL(indexer_score_kernel<4>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
   }
   return hipGetLastError();
 }

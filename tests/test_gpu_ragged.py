@@ -233,3 +233,17 @@ def test_ragged_step_full_lengths_equal_dsa_decode_step():
     torch.cuda.synchronize()
     assert torch.equal(ia, ib)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,N,zero_frac", [(150, 3000, 0.3), (200, 777, 0.9), (70, 40000, 0.0)])
+def test_ragged_step_many_rows(B, N, zero_frac):
+    """More than 64 rows: the indexer walks its share of the valid rounds
+    across several 64-row chunks, over rows of length 0 and shares that
+    start and end inside rows."""
+    s = workloads.StepShape(B=B, N=N, H_I=8, D_I=128, k=min(64, N), W=0, H_q=16, D=128)
+    inp = workloads.step_inputs(s, 35000 + B, device=DEV)
+    rng = np.random.default_rng(B + N)
+    lengths = rng.integers(1, N + 1, size=B).astype(np.int32)
+    lengths[rng.random(B) < zero_frac] = 0
+    lengths[-1] = N
+    run_ragged_step(s, inp, lengths, f"{B} rows")

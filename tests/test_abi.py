@@ -121,3 +121,39 @@ def test_valid_call_without_device_reports_device_error(lib):
     L = lib.LIB
     v = ctypes.c_void_p
     assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 1, 10, 8, 128, None) == DEVICE
+
+
+def test_ragged_and_multi_token_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    ok = _dims(lib)
+    # ragged: lengths are required and 4-byte aligned
+    assert L.dsa_topk_ragged(v(P), 0, 4, 100, None, 10, v(P), None, 0, v(P), 1 << 20,
+                             None) == INVALID
+    assert L.dsa_topk_ragged(v(P), 0, 4, 100, v(P + 2), 10, v(P), None, 0, v(P), 1 << 20,
+                             None) == INVALID
+    assert L.dsa_decode_step_ragged(v(P), v(P), v(P), v(P), v(P), v(P), None, v(P), None,
+                                    ctypes.byref(ok), v(P), 1 << 30, None) == INVALID
+    # several tokens: 1 <= T <= 4, B*T within the attention limit
+    one = lib.dsa_decode_step_workspace_bytes(ok)
+    assert L.dsa_decode_step_mt_workspace_bytes(ctypes.byref(ok), 1) == one
+    assert L.dsa_sparse_attend_mt_workspace_bytes(ctypes.byref(ok), 1) == \
+        lib.dsa_sparse_attend_workspace_bytes(ok)
+    two = L.dsa_decode_step_mt_workspace_bytes(ctypes.byref(ok), 2)
+    assert two > one
+    for T in (0, 5):
+        assert L.dsa_decode_step_mt_workspace_bytes(ctypes.byref(ok), T) == 0
+        assert L.dsa_sparse_attend_mt_workspace_bytes(ctypes.byref(ok), T) == 0
+    assert L.dsa_indexer_score_mt(v(P), v(P), v(P), v(P), 1, 0, 10, 8, 128, None) == INVALID
+    assert L.dsa_indexer_score_mt(v(P), v(P), v(P), v(P), 1, 5, 10, 8, 128, None) == NOT_SUPPORTED
+    assert L.dsa_indexer_score_mt(v(P), v(P), v(P), v(P + 8), 1, 2, 10, 8, 128, None) == INVALID
+    assert L.dsa_sparse_attend_mt(v(P), v(P), v(P), v(P), v(P), ctypes.byref(ok), 5, v(P),
+                                  1 << 30, None) == NOT_SUPPORTED
+    assert L.dsa_decode_step_mt(v(P), v(P), v(P), v(P), v(P), v(P), None, v(P), None,
+                                ctypes.byref(ok), 0, v(P), 1 << 30, None) == INVALID
+    assert L.dsa_decode_step_mt(v(P), v(P), v(P), v(P), v(P), v(P), v(P + 2), v(P), None,
+                                ctypes.byref(ok), 2, v(P), 1 << 30, None) == INVALID
+    assert L.dsa_decode_step_mt(v(P), v(P), v(P), v(P), v(P), v(P), None, v(P), None,
+                                ctypes.byref(ok), 2, v(P), two - 1, None) == WS_SMALL
+    big = _dims(lib, B=20000)
+    assert L.dsa_decode_step_mt_workspace_bytes(ctypes.byref(big), 4) == 0  # B*T > 65535

@@ -222,8 +222,8 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_ragged_kernel(
 // read from HBM once for all the tokens. Registers hold one token's query
 // fragments, so all the tokens' query rows and weights are staged in LDS at
 // the start (rows padded to 272 B: the 16 lanes of a fragment read land on
-// different banks) and each token's are read back per step. Per token the
-// arithmetic and its order are those of the one-token kernel.
+// different banks) and each token's are read back once per pair of steps.
+// Per token the arithmetic and its order are those of the one-token kernel.
 constexpr int kQPitch = kDI * 2 + 16;  // bytes per staged query row
 
 template <int MT>
@@ -278,13 +278,15 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_mt_kernel(
       r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (size_t)key * kDI) + (lane & 15));
     }
   };
-  auto score_step = [&](const u32x4 (&r)[8], int key0) {
+  // Steps are scored in pairs: the two steps' key fragments stay in
+  // registers, so each token's query fragments are read from LDS once per
+  // 64 keys and feed 16 MFMAs each.
+  auto stage_read = [&](const u32x4 (&r)[8], bf16x8 (&kb)[kIsTiles][4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int qk = 4 * j + (lane >> 4);
       st[qk * 16 + ((lane & 15) ^ (qk & 15))] = r[j];
     }
-    bf16x8 kb[kIsTiles][4];
 #pragma unroll
     for (int tt = 0; tt < kIsTiles; ++tt)
 #pragma unroll
@@ -292,61 +294,66 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_mt_kernel(
         const int qk = 16 * tt + m;
         kb[tt][kk] = __builtin_bit_cast(bf16x8, st[qk * 16 + ((4 * kk + g) ^ m)]);
       }
+  };
+  auto score_pair = [&](const bf16x8 (&ka)[kIsTiles][4], const bf16x8 (&kc)[kIsTiles][4], int key0,
+                        bool two) __attribute__((always_inline)) {
     for (int t = 0; t < T; ++t) {
-      // One 16-head tile at a time, so that only its query fragments are
-      // live; each accumulator still takes the k-steps in order.
       const char* qt = qs + (size_t)t * kRowsPerToken * kQPitch;
-      f32x4 acc[kIsTiles][MT];
+      float p[2 * kIsTiles] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         bf16x8 qa[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           qa[kk] = *reinterpret_cast<const bf16x8*>(qt + (size_t)(mt * 16 + m) * kQPitch + kk * 64 + g * 16);
+        f32x4 acc[2 * kIsTiles];
 #pragma unroll
-        for (int tt = 0; tt < kIsTiles; ++tt) acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 2 * kIsTiles; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int tt = 0; tt < kIsTiles; ++tt) acc[tt][mt] = mfma16x16x32(qa[kk], kb[tt][kk], acc[tt][mt]);
-      }
-      float p[kIsTiles] = {0.0f, 0.0f};
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+          for (int tt = 0; tt < kIsTiles; ++tt) {
+            acc[tt] = mfma16x16x32(qa[kk], ka[tt][kk], acc[tt]);
+            acc[kIsTiles + tt] = mfma16x16x32(qa[kk], kc[tt][kk], acc[kIsTiles + tt]);
+          }
         const float4 wq = *reinterpret_cast<const float4*>(wl + t * kRowsPerToken + mt * 16 + g * 4);
         const float wv[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
-        for (int tt = 0; tt < kIsTiles; ++tt)
+        for (int u = 0; u < 2 * kIsTiles; ++u)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p[tt] += wv[i] * fmaxf(acc[tt][mt][i], 0.0f);
+          for (int i = 0; i < 4; ++i) p[u] += wv[i] * fmaxf(acc[u][i], 0.0f);
       }
-      float mine = (g & 1) ? p[1] : p[0];
-      const float other = (g & 1) ? p[0] : p[1];
-      mine += lane_xor16(other);
-      mine += lane_xor32(mine);
       int tl = tlen[0];
 #pragma unroll
       for (int u = 1; u < kMaxTokens; ++u) tl = t == u ? tlen[u] : tl;
-      if (g < 2) {
-        const int key = key0 + g * 16 + m;
-        if (key < tl) s[((size_t)b * T + t) * N + key] = mine;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float mine = (g & 1) ? p[2 * h + 1] : p[2 * h];
+        const float other = (g & 1) ? p[2 * h] : p[2 * h + 1];
+        mine += lane_xor16(other);
+        mine += lane_xor32(mine);
+        if (g < 2 && (h == 0 || two)) {
+          const int key = key0 + h * kIsKeysPerRound + g * 16 + m;
+          if (key < tl) s[((size_t)b * T + t) * N + key] = mine;
+        }
       }
     }
   };
-  u32x4 ra[8], rb[8], rc[8];
+  // Two register buffers: a pair's loads are issued as soon as the previous
+  // pair is staged, and land while that pair is scored.
+  u32x4 ra[8], rb[8];
+  bf16x8 ka[kIsTiles][4], kc[kIsTiles][4];
   int key0 = start + wave * kIsKeysPerStep;
   const int nsteps = key0 < end ? (end - key0 + kIsKeysPerRound - 1) / kIsKeysPerRound : 0;
   if (nsteps > 0) load_step(ra, key0);
   if (nsteps > 1) load_step(rb, key0 + kIsKeysPerRound);
-  for (int i = 0; i < nsteps; i += 3) {
-    if (i + 2 < nsteps) load_step(rc, key0 + (i + 2) * kIsKeysPerRound);
-    score_step(ra, key0 + i * kIsKeysPerRound);
-    if (i + 1 >= nsteps) break;
-    if (i + 3 < nsteps) load_step(ra, key0 + (i + 3) * kIsKeysPerRound);
-    score_step(rb, key0 + (i + 1) * kIsKeysPerRound);
-    if (i + 2 >= nsteps) break;
-    if (i + 4 < nsteps) load_step(rb, key0 + (i + 4) * kIsKeysPerRound);
-    score_step(rc, key0 + (i + 2) * kIsKeysPerRound);
+  for (int i = 0; i < nsteps; i += 2) {
+    const bool two = i + 1 < nsteps;
+    stage_read(ra, ka);
+    if (two) stage_read(rb, kc);
+    if (i + 2 < nsteps) load_step(ra, key0 + (i + 2) * kIsKeysPerRound);
+    if (i + 3 < nsteps) load_step(rb, key0 + (i + 3) * kIsKeysPerRound);
+    score_pair(ka, kc, key0 + i * kIsKeysPerRound, two);
   }
 }
 

@@ -306,24 +306,43 @@ def indexer_bytes(s) -> int:
     return b * s.N * s.D_I * 2 + b * s.H_I * s.D_I * 2 + b * s.H_I * 4 + b * s.N * 4
 
 
-def source_digest(paths) -> str:
-    """Hash of the sources' code: comments and blank space are dropped, so
-    a comment edit does not void counters taken on the same code."""
+def source_digest(parts) -> str:
+    """Hash of the code a kernel is built and launched from. parts: paths,
+    or (path, start, stop) to take the text from the first `start` up to the
+    first `stop` after it (None: the file's start or end). Comments and
+    blank space are dropped, so a comment edit does not void counters taken
+    on the same code."""
     import re
     h = hashlib.sha256()
-    for path in paths:
+    for part in parts:
+        path, start, stop = (part, None, None) if isinstance(part, str) else part
         with open(path, encoding="utf-8") as f:
             text = f.read()
+        if start is not None:
+            text = text[text.index(start):]
+        if stop is not None:
+            text = text[:text.index(stop)]
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
+def indexer_source_parts():
+    """The one-token indexer's code: its row sweep and kernel (the file up
+    to the ragged kernel's first helper), its launcher, and the internal
+    header; the multi-token and ragged kernels are left out."""
+    csrc = os.path.join(ROOT, "indexer_top_gathered_amd", "csrc")
+    f = os.path.join(csrc, "indexer_score.hip")
+    return [(f, None, "__device__ __forceinline__ uint32_t valid_rounds("),
+            (f, "hipError_t launch_indexer_score(", None),
+            os.path.join(csrc, "dsa_internal.h")]
+
+
 def traffic_from_profile(kernel_srcs):
     """HBM bytes per launch recorded by the rocprofv3 counter runs, if they
-    were taken on the current kernel sources (the kernel's file and the
-    internal header it includes); else None."""
+    were taken on the current kernel code (source_digest of kernel_srcs);
+    else None."""
     path = os.path.join(ROOT, "profiles", "indexer_score_decode_step_counters.md")
     if not os.path.exists(path):
         return None
@@ -454,9 +473,7 @@ def main():
     is_us = e0.elapsed_time(e1) * 1e3 / args.steps
     is_bytes = indexer_bytes(s)
     achieved = is_bytes / (is_us * 1e-6) / 1e9
-    csrc = os.path.join(ROOT, "indexer_top_gathered_amd", "csrc")
-    traffic = traffic_from_profile([os.path.join(csrc, "indexer_score.hip"),
-                                    os.path.join(csrc, "dsa_internal.h")])
+    traffic = traffic_from_profile(indexer_source_parts())
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "kernel": "indexer_score_kernel<4>",

@@ -78,6 +78,8 @@ def _load():
             lib.oracle_step_mt.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                            I, ctypes.c_double]
             lib.oracle_step_mt.restype = I
+            lib.oracle_qproj.argtypes = [P, P, P, I, I, I]
+            lib.oracle_qproj.restype = None
             lib.oracle_set_threads.argtypes = [I]
             lib.oracle_set_threads.restype = None
             lib.oracle_max_threads.argtypes = []
@@ -326,3 +328,16 @@ def step_mt(q_idx, k_idx, w, q, kv, win, lengths, k: int, scale: float):
     if rc != 0:
         raise ValueError("oracle_step_mt: invalid arguments")
     return scores, idx, out
+
+
+def qproj(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Indexer query projection. x uint16 (bf16) [B, d_in], w uint16 [O, d_in]
+    -> float64 [B, O] = x @ w^T with exact products and double sums."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    B, d_in = x.shape
+    O = w.shape[0]
+    assert w.shape == (O, d_in)
+    out = np.empty((B, O), np.float64)
+    _load().oracle_qproj(_ptr(x), _ptr(w), _ptr(out), B, d_in, O)
+    return out

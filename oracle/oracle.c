@@ -28,6 +28,8 @@
  *  - ragged rows (an extension): row b has lengths[b] valid positions; its
  *    top-k slots past min(k, lengths[b]) hold -1, and a -1 slot takes no
  *    part in attention (a batch row with no rows gets zeros).
+ *  - indexer query projection: a plain matrix-vector product per batch row
+ *    (the projection weights are synthetic; the pages give no widths).
  *  - several query tokens per batch row (an extension): T consecutive query
  *    rows share one row of keys (indexer keys and compressed KV); each has
  *    its own queries, weights, window, length and selection, and is in
@@ -345,4 +347,25 @@ int oracle_step_mt(const uint16_t* q_idx, const uint16_t* k_idx, const float* w,
                          : oracle_topk(scores, 1, B * T, N, k, idx, 0);
   if (rc != 0) return -1;
   return oracle_attend_mt(q, kv, idx, win, out, B, T, N, k, W, Hq, D, scale);
+}
+
+/*
+ * Indexer query projection [CSA, step table, step 2: the indexer query is
+ * projected into 128 channels per head before scoring]:
+ *   out[b, o] = sum_i x[b, i] * w[o, i]
+ * x bf16 [B, d_in], w bf16 [O, d_in] (O = H_I * 128 output channels, row o
+ * of w holding output o's weights), out double [B, O]. Products of bf16
+ * values are exact in double; the sum runs in double in index order.
+ */
+void oracle_qproj(const uint16_t* x, const uint16_t* w, double* out, int B, int d_in, int O) {
+#pragma omp parallel for schedule(static)
+  for (int o = 0; o < O; ++o) {
+    const uint16_t* wrow = w + (int64_t)o * d_in;
+    for (int b = 0; b < B; ++b) {
+      const uint16_t* xrow = x + (int64_t)b * d_in;
+      double acc = 0.0;
+      for (int i = 0; i < d_in; ++i) acc += bf16_value(xrow[i]) * bf16_value(wrow[i]);
+      out[(int64_t)b * O + o] = acc;
+    }
+  }
 }

@@ -508,3 +508,33 @@ def test_step_mt_with_one_token_is_the_step():
     ref = oracle.step_ragged(b["q_idx"], b["k_idx"], b["w"], b["q"], b["kv_cmp"], b["kv_win"],
                              lengths, s.k, s.scale)
     assert all(np.array_equal(u[:, 0], v) for u, v in zip(one, ref))
+
+
+# ---------------------------------------------------------------- indexer query projection
+
+def test_qproj_equals_fp64_matmul():
+    g = torch.Generator().manual_seed(601)
+    B, d_in, O = 5, 1000, 300
+    x = torch.randn(B, d_in, generator=g).to(torch.bfloat16)
+    w = torch.randn(O, d_in, generator=g).to(torch.bfloat16)
+    got = oracle.qproj(bf16_bits(x), bf16_bits(w))
+    ref = (x.double() @ w.double().T).numpy()
+    assert got.shape == (B, O)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_qproj_one_hot_and_scaling_are_exact():
+    g = torch.Generator().manual_seed(602)
+    B, d_in, O = 3, 256, 64
+    w = torch.randn(O, d_in, generator=g).to(torch.bfloat16)
+    x = torch.zeros(B, d_in)
+    picks = [0, 77, 255]
+    for b, i in enumerate(picks):
+        x[b, i] = 1.0
+    got = oracle.qproj(bf16_bits(x.to(torch.bfloat16)), bf16_bits(w))
+    for b, i in enumerate(picks):
+        assert np.array_equal(got[b], w[:, i].double().numpy())  # selects a column of w
+    xs = torch.randn(B, d_in, generator=g).to(torch.bfloat16)
+    a = oracle.qproj(bf16_bits(xs), bf16_bits(w))
+    b2 = oracle.qproj(bf16_bits((xs.float() * 2).to(torch.bfloat16)), bf16_bits(w))
+    assert np.array_equal(b2, 2 * a)  # exact: powers of two scale every product exactly

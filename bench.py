@@ -28,7 +28,8 @@ JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
 `ragged-step` (the production shape over rows of lengths uniform on [1, N],
 timed with dsa_decode_step_ragged next to the same call at full length) or
 `mtp-step` (the production shape with 2 query tokens per batch row sharing
-its keys, dsa_decode_step_mt, next to 1 and 4 tokens).
+its keys, dsa_decode_step_mt, next to 1 and 4 tokens) or `qproj` (the
+indexer query projection of 16 rows, 4096 wide, onto 64 x 128 channels).
 """
 from __future__ import annotations
 
@@ -61,7 +62,7 @@ def parse():
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
                    choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step",
-                            "ragged-step", "mtp-step"])
+                            "ragged-step", "mtp-step", "qproj"])
     return p.parse_args()
 
 
@@ -222,6 +223,27 @@ def other_workload(args):
                      "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
                                 "W": s.W, "H_q": s.H_q, "D": s.D,
                                 "lengths": "uniform on [1, N], seed 6000"}})
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "qproj":
+        # The indexer query projection of a decode batch: B = 16 rows of a
+        # synthetic 4096-wide input onto 64 heads x 128 channels.
+        B, d_in, H = 16, 4096, 64
+        nbytes = H * 128 * d_in * 2 + B * d_in * 2 + B * H * 128 * 2
+        R = max(1, -(-(1 << 30) // nbytes))
+        copies = [workloads.qproj_inputs(B, d_in, H, 8000 + 10 * r, device=dev) for r in range(R)]
+        outq = torch.empty((B, H, 128), dtype=torch.bfloat16, device=dev)
+
+        def call(i):
+            c = copies[i % R]
+            dsa.dsa_indexer_qproj(c["x"], c["w_q"], H, q_idx=outq, stream=stream)
+        us = time_calls(call, args.warmup, args.steps, stream)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        line.update({"us": round(us, 2), "value": round(gbps, 1),
+                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                     "compulsory_bytes": nbytes, "rotating_input_copies": R,
+                     "config": {"B": B, "d_in": d_in, "H_I": H, "D_I": 128,
+                                "weights": "synthetic, N(0, 1/d_in)"}})
         print(json.dumps(line), flush=True)
         return
     if args.workload == "mtp-step":

@@ -85,6 +85,21 @@ DSA_EXPORT dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, 
                                void* stream);
 
 /*
+ * Indexer query projection (CSA pull request, "How the algorithm works",
+ * step table, step 2: the indexer query is projected into 128 channels per
+ * head; the pull request runs it as a hand-tiled GEMV):
+ *   q_idx[b, h, c] = sum_i x[b, i] * w_q[h*D_I + c, i]
+ * x bf16 [B, d_in] (the query input of each decode row); w_q bf16
+ * [H_I*D_I, d_in] (row h*D_I + c holds the weights of head h, channel c);
+ * q_idx bf16 [B, H_I, D_I] (output, the layout dsa_indexer_score reads).
+ * Products are exact, sums run in float32 in a fixed order, and the result
+ * is rounded to nearest even. Requires D_I == 128, 1 <= H_I <= 64 and d_in a
+ * multiple of 256 (else DSA_ERROR_NOT_SUPPORTED). No workspace.
+ */
+DSA_EXPORT dsa_status_t dsa_indexer_qproj(const void* x, const void* w_q, void* q_idx, int B,
+                               int d_in, int H_I, int D_I, void* stream);
+
+/*
  * Top-k selection (CSA pull request, step 3; "DeepSelect" project page):
  * for each of the B rows of `scores` (dtype bf16 or float32, [B, N]) the k
  * positions with the largest value, ties broken by the lower index. -0.0 and

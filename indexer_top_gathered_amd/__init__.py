@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     dsa_decode_step_mt_workspace_bytes,
     dsa_decode_step_ragged,
     dsa_decode_step_workspace_bytes,
+    dsa_indexer_qproj,
     dsa_indexer_score,
     dsa_indexer_score_mt,
     dsa_sparse_attend,

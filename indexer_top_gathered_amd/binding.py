@@ -34,6 +34,7 @@ EXPORTED = (
     "dsa_sparse_attend_mt",
     "dsa_decode_step_mt_workspace_bytes",
     "dsa_decode_step_mt",
+    "dsa_indexer_qproj",
     "dsa_status_string",
 )
 
@@ -96,6 +97,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_decode_step_mt_workspace_bytes.restype = S
     lib.dsa_decode_step_mt.argtypes = [P, P, P, P, P, P, P, P, P, D, I, P, S, P]
     lib.dsa_decode_step_mt.restype = I
+    lib.dsa_indexer_qproj.argtypes = [P, P, P, I, I, I, I, P]
+    lib.dsa_indexer_qproj.restype = I
     lib.dsa_status_string.argtypes = [I]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -164,6 +167,20 @@ def dsa_indexer_score(q_idx, k_idx, w, scores=None, stream=None):
     _check(LIB.dsa_indexer_score(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, N, H, DI,
                                  _stream(stream)), "dsa_indexer_score")
     return scores
+
+
+def dsa_indexer_qproj(x, w_q, H_I: int, q_idx=None, stream=None):
+    """Indexer query projection: x bf16 [B, d_in], w_q bf16 [H_I*128, d_in]
+    -> q_idx bf16 [B, H_I, 128] = x @ w_q^T (fp32 sums, rounded to bf16)."""
+    B, d_in = x.shape
+    _need(x, "x", torch.bfloat16)
+    _need(w_q, "w_q", torch.bfloat16, (H_I * 128, d_in))
+    if q_idx is None:
+        q_idx = torch.empty((B, H_I, 128), dtype=torch.bfloat16, device=x.device)
+    _need(q_idx, "q_idx", torch.bfloat16, (B, H_I, 128))
+    _check(LIB.dsa_indexer_qproj(_ptr(x), _ptr(w_q), _ptr(q_idx), B, d_in, int(H_I), 128,
+                                 _stream(stream)), "dsa_indexer_qproj")
+    return q_idx
 
 
 def dsa_indexer_score_mt(q_idx, k_idx, w, scores=None, stream=None):

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["dsa_api.hip", "indexer_score.hip", "topk.hip", "sparse_attend.hip"]
+SOURCES = ["dsa_api.hip", "indexer_score.hip", "topk.hip", "sparse_attend.hip", "qproj.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

@@ -151,6 +151,21 @@ dsa_status_t dsa_indexer_score_mt(const void* q_idx, const void* k_idx, const fl
                                         H_I, T, nullptr, static_cast<hipStream_t>(stream)));
 }
 
+dsa_status_t dsa_indexer_qproj(const void* x, const void* w_q, void* q_idx, int B, int d_in,
+                               int H_I, int D_I, void* stream) {
+  if (!x || !w_q || !q_idx) return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(w_q) || !aligned16(q_idx)) return DSA_ERROR_INVALID_VALUE;
+  if (B < 1 || d_in < 1 || H_I < 1 || D_I < 1) return DSA_ERROR_INVALID_VALUE;
+  if (D_I != 128 || H_I > 64 || d_in % 256 != 0 || B > 65535 * 16) return DSA_ERROR_NOT_SUPPORTED;
+  if ((long long)H_I * D_I * d_in > 0x7FFFFFFFLL || (long long)B * d_in > 0x7FFFFFFFLL)
+    return DSA_ERROR_NOT_SUPPORTED;
+  dsa_status_t s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  return to_status(launch_qproj(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_q),
+                                static_cast<uint16_t*>(q_idx), B, d_in, H_I * D_I,
+                                static_cast<hipStream_t>(stream)));
+}
+
 size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
   if (check_topk_shape(B, N, k, dtype) != DSA_SUCCESS) return 0;
   return plan_topk(B, N, k, dtype).bytes;

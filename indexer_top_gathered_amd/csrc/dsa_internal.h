@@ -189,6 +189,11 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
                                 float* s, int B, int N, int H, int tokens,
                                 const int32_t* lengths, hipStream_t st);
 
+// Indexer query projection: out bf16 [B, O] = x bf16 [B, d_in] @ w^T, w
+// bf16 [O, d_in]; d_in a multiple of 256, O of 32.
+hipError_t launch_qproj(const uint16_t* x, const uint16_t* w, uint16_t* out, int B, int d_in,
+                        int O, hipStream_t st);
+
 struct TopkPlan {
   bool fused;       // one workgroup per row does everything (no second kernel)
   int segs;         // segments per row

@@ -123,6 +123,17 @@ def mt_step_inputs(s: StepShape, T: int, seed_base: int, device="cpu") -> dict:
     }
 
 
+def qproj_inputs(B: int, d_in: int, H_I: int, seed: int, device="cpu") -> dict:
+    """Inputs of the indexer query projection: x ~ N(0,1) bf16 [B, d_in] and
+    synthetic weights w_q ~ N(0, 1/d_in) bf16 [H_I*128, d_in] (unit-variance
+    outputs)."""
+    return {
+        "x": _normal((B, d_in), _gen(device, seed + 0), device, torch.bfloat16),
+        "w_q": _normal((H_I * 128, d_in), _gen(device, seed + 1), device, torch.bfloat16,
+                       std=1.0 / math.sqrt(d_in)),
+    }
+
+
 def ragged_lengths(B: int, N: int, k: int, seed: int) -> np.ndarray:
     """int32 [B] sequence lengths for a ragged batch: the edge values 0, 1,
     k - 1, k, k + 1 and N first (those within [0, N]), then lengths drawn

@@ -94,7 +94,9 @@ DSA_EXPORT dsa_status_t dsa_indexer_score(const void* q_idx, const void* k_idx, 
  * q_idx bf16 [B, H_I, D_I] (output, the layout dsa_indexer_score reads).
  * Products are exact, sums run in float32 in a fixed order, and the result
  * is rounded to nearest even. Requires D_I == 128, 1 <= H_I <= 64 and d_in a
- * multiple of 256 (else DSA_ERROR_NOT_SUPPORTED). No workspace.
+ * multiple of 256 (else DSA_ERROR_NOT_SUPPORTED). No workspace. With H_I = 1
+ * and the key weights it gives the new token's indexer key ([B, 1, 128]),
+ * which the caller appends to k_idx.
  */
 DSA_EXPORT dsa_status_t dsa_indexer_qproj(const void* x, const void* w_q, void* q_idx, int B,
                                int d_in, int H_I, int D_I, void* stream);

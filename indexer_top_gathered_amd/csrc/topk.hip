@@ -679,30 +679,29 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   // Register blocks of THREADS*V*E scores. The first block sets a threshold
   // from its group maxima and is cut to its exact top k; later blocks are
   // only filtered against that k-th composite (which every later winner must
-  // beat), and the next block's loads are in flight while one is filtered.
+  // beat).
   //
   // A block wholly inside the segment (all but possibly the last) is read
   // by straight-line 16-byte loads, so all of them are in flight before the
   // first is used; scores become keys only when the block is taken up.
-  u32x4 kv[V], kn[V];
-  if (ALIGNED && seg_start + kBlock <= seg_end) {  // uniform
+  // Blocks are loaded into a ring of three register buffers, two blocks
+  // ahead of the one being taken up, so a block's loads have two blocks'
+  // processing time to land. (Rotating names through an unrolled loop keeps
+  // the buffers in place: a register copy of a block still in flight would
+  // wait for it.)
+  auto load_block = [&](u32x4 (&r)[V], int64_t at) __attribute__((always_inline)) {
+    if (ALIGNED && at + kBlock <= seg_end) {  // uniform
 #pragma unroll
-    for (int v = 0; v < V; ++v) kv[v] = load_raw_full<BF16>(row, seg_start + ((int64_t)v * THREADS + threadIdx.x) * E);
-  } else {
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      kv[v] = load_raw<BF16, ALIGNED>(row, seg_start + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
-  }
-  for (int64_t base = seg_start; base < seg_end; base += kBlock) {
-    const int64_t nb = base + kBlock;
-    if (ALIGNED && nb + kBlock <= seg_end) {  // uniform
-#pragma unroll
-      for (int v = 0; v < V; ++v) kn[v] = load_raw_full<BF16>(row, nb + ((int64_t)v * THREADS + threadIdx.x) * E);
-    } else if (nb < seg_end) {
+      for (int v = 0; v < V; ++v) r[v] = load_raw_full<BF16>(row, at + ((int64_t)v * THREADS + threadIdx.x) * E);
+    } else {
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        kn[v] = load_raw<BF16, ALIGNED>(row, nb + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+        r[v] = load_raw<BF16, ALIGNED>(row, at + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
     }
+  };
+  // Takes up the block held in kv, at row position base; true when the
+  // segment is finished (its survivors written straight to the workspace).
+  auto take_block = [&](u32x4 (&kv)[V], int64_t base) __attribute__((always_inline)) -> bool {
 #pragma unroll
     for (int v = 0; v < V; ++v) to_keys<BF16>(kv[v]);
     // A threshold from this block's group maxima (raw keys): at least k
@@ -798,7 +797,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       write_admitted<BF16, V, THREADS>(cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k), excl, kv,
                                        adm, base);
       if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = total;
-      return;
+      return true;
     }
     if (cnt + (int)total <= CAP) {
       write_admitted<BF16, V, THREADS>(cand, (uint32_t)cnt + excl, kv, adm, base);
@@ -844,8 +843,20 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       thr = t - 1;
       have_thr = true;
     }
-#pragma unroll
-    for (int v = 0; v < V; ++v) kv[v] = kn[v];
+    return false;
+  };
+  u32x4 ka[V], kb[V], kc[V];
+  load_block(ka, seg_start);
+  if (seg_start + kBlock < seg_end) load_block(kb, seg_start + kBlock);
+  for (int64_t base = seg_start; base < seg_end; base += 3 * kBlock) {
+    if (base + 2 * kBlock < seg_end) load_block(kc, base + 2 * kBlock);
+    if (take_block(ka, base)) return;
+    if (base + kBlock >= seg_end) break;
+    if (base + 3 * kBlock < seg_end) load_block(ka, base + 3 * kBlock);
+    if (take_block(kb, base + kBlock)) return;
+    if (base + 2 * kBlock >= seg_end) break;
+    if (base + 4 * kBlock < seg_end) load_block(kb, base + 4 * kBlock);
+    if (take_block(kc, base + 2 * kBlock)) return;
   }
   if (FUSED) {
     // The row's candidates are all here: select the k winners and write them.

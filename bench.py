@@ -28,8 +28,10 @@ JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
 `ragged-step` (the production shape over rows of lengths uniform on [1, N],
 timed with dsa_decode_step_ragged next to the same call at full length) or
 `mtp-step` (the production shape with 2 query tokens per batch row sharing
-its keys, dsa_decode_step_mt, next to 1 and 4 tokens) or `qproj` (the
-indexer query projection of 16 rows, 4096 wide, onto 64 x 128 channels).
+its keys, dsa_decode_step_mt, next to 1 and 4 tokens), `qproj` (the
+indexer query projection of 16 rows, 4096 wide, onto 64 x 128 channels) or
+`context-sweep` (the production step at N = 2K .. 32K compressed positions,
+8K .. 128K tokens at 4:1).
 """
 from __future__ import annotations
 
@@ -62,7 +64,7 @@ def parse():
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
                    choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step",
-                            "ragged-step", "mtp-step", "qproj"])
+                            "ragged-step", "mtp-step", "qproj", "context-sweep"])
     return p.parse_args()
 
 
@@ -223,6 +225,42 @@ def other_workload(args):
                      "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
                                 "W": s.W, "H_q": s.H_q, "D": s.D,
                                 "lengths": "uniform on [1, N], seed 6000"}})
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "context-sweep":
+        # The production step's shape at compressed lengths N = 2K .. 32K,
+        # i.e. 8K .. 128K tokens folded 4 to 1: the context range over which
+        # the CSA pull request reports its block latency.
+        import dataclasses
+        results = []
+        for N in (2048, 4096, 8192, 16384, 32768):
+            s = dataclasses.replace(workloads.C4, N=N)
+            one = step_bytes(s)
+            R = max(1, min(256, -(-(1 << 30) // one)))
+            copies = [workloads.step_inputs(s, 9000 + N + 10 * r, device=dev) for r in range(R)]
+            dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
+            ws = torch.empty(dsa.dsa_decode_step_workspace_bytes(dims), dtype=torch.uint8,
+                             device=dev)
+            out = torch.empty((s.B, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+
+            def call(i, copies=copies, ws=ws, out=out, s=s, R=R):
+                c = copies[i % R]
+                dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                    c["kv_win"], s.k, s.scale, out=out, ws=ws, stream=stream)
+            us = time_calls(call, args.warmup, args.steps, stream)
+            roof = step_roofline_us(s)
+            results.append({"N": N, "tokens": 4 * N, "us_per_step": round(us, 2),
+                            "effective_GBps": round(one / (us * 1e-6) / 1e9, 1),
+                            "roofline_us": round(roof, 3), "frac_of_roofline": round(roof / us, 4),
+                            "rotating_input_copies": R})
+            del copies
+        line.update({"us_per_step": results[-1]["us_per_step"],
+                     "value": results[-1]["effective_GBps"], "results": results,
+                     "latency_ratio_128k_over_8k": round(results[-1]["us_per_step"]
+                                                         / results[0]["us_per_step"], 3),
+                     "config": {"B": workloads.C4.B, "N": [r["N"] for r in results],
+                                "H_I": 64, "D_I": 128, "k": 1024, "W": 128, "H_q": 128,
+                                "D": 512}})
         print(json.dumps(line), flush=True)
         return
     if args.workload == "qproj":

@@ -247,3 +247,11 @@ def test_ragged_step_many_rows(B, N, zero_frac):
     lengths[rng.random(B) < zero_frac] = 0
     lengths[-1] = N
     run_ragged_step(s, inp, lengths, f"{B} rows")
+
+
+def test_ragged_step_workload_full():
+    """The ragged-step bench configuration at full size: the production
+    shape over lengths uniform on [1, N]."""
+    s = workloads.C4
+    inp = workloads.step_inputs(s, 6000, device=DEV)
+    run_ragged_step(s, inp, workloads.serving_lengths(s.B, s.N, 6000), "ragged-step workload")

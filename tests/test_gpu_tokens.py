@@ -158,3 +158,11 @@ def test_one_token_mt_calls_equal_the_one_token_calls():
     torch.cuda.synchronize()
     assert torch.equal(ia, ib[:, 0])
     assert torch.equal(a.view(torch.int16), b[:, 0].view(torch.int16))
+
+
+def test_mtp_step_workload_full():
+    """The mtp-step bench configuration at full size: the production shape
+    with 2 query tokens per row."""
+    s = workloads.C4
+    inp = workloads.mt_step_inputs(s, 2, 7000, device=DEV)
+    run_step_mt(s, 2, inp, None, "mtp-step workload")

@@ -17,8 +17,10 @@ dominant kernel (indexer scoring) measured with HIP events on the stream it
 runs on (with `measured_hbm`, the rates of a plain torch row reduction
 and copy on 1 GiB, and the indexer's fraction of that read rate),
 `single_call_latency` the median, p10 and p90 of single steps each run
-after a 512 MiB cache-evicting write, `topk` the top-k-only workload (bf16
-64 x 131072, k=512), and `cpu_baseline` the CPU oracle timed on this host.
+after a 512 MiB cache-evicting write, `torch_step` the same step written
+with plain torch ops on this GPU (context), `topk` the top-k-only workload
+(bf16 64 x 131072, k=512), and `cpu_baseline` the CPU oracle timed on this
+host.
 
 `--workload` times one of the other workloads instead (for profiling; one
 JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
@@ -419,6 +421,25 @@ def traffic_from_profile(kernel_srcs):
         return None
 
 
+def torch_step(c, s):
+    """The decode step written with plain torch ops on the GPU (context for
+    the fused kernels, as the pages compare against a naive baseline): a
+    batched matmul for the indexer (fp32 results, so that the selection is
+    the fused path's), torch.topk, a gather and matmul/softmax attention.
+    Right-hand matmul operands are made contiguous first."""
+    import torch
+    kt = c["k_idx"].transpose(1, 2).contiguous()                      # [B, 128, N]
+    dots = torch.bmm(c["q_idx"], kt, out_dtype=torch.float32)          # [B, H_I, N]
+    scores = (torch.relu(dots) * c["w"][:, :, None]).sum(1)            # [B, N]
+    idx = torch.topk(scores, s.k, dim=1, sorted=False).indices         # [B, k]
+    rows = torch.gather(c["kv_cmp"], 1, idx[:, :, None].expand(-1, -1, s.D))
+    rows = torch.cat([rows, c["kv_win"]], dim=1)                       # [B, k+W, D]
+    logits = torch.bmm(c["q"], rows.transpose(1, 2).contiguous(), out_dtype=torch.float32)
+    logits = logits * s.scale
+    p = torch.softmax(logits, dim=-1).to(torch.bfloat16)
+    return torch.bmm(p, rows.contiguous())                             # [B, H_q, D]
+
+
 def single_call_latency(call, n: int, dev, stream) -> dict:
     """Latency of one call from cold caches: before each call a 512 MiB
     buffer is written (twice the 256 MB Infinity Cache, far beyond the L2s),
@@ -559,6 +580,24 @@ def main():
     del scores
     if args.latency_calls > 0:
         line["single_call_latency"] = single_call_latency(step, args.latency_calls, dev, stream)
+        # The same step in plain torch ops on this GPU, over the same rotation
+        # (context only: a failure here is reported, not raised).
+        try:
+            n_ref = max(10, args.steps // 10)
+            with torch.cuda.stream(stream):
+                for i in range(3):
+                    torch_step(copies[i % R], s)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(n_ref):
+                    torch_step(copies[i % R], s)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            t_us = e0.elapsed_time(e1) * 1e3 / n_ref
+            line["torch_step"] = {"us": round(t_us, 2), "speedup": round(t_us / us_step, 2),
+                                  "ops": "bmm indexer, torch.topk, gather, bmm/softmax attention"}
+        except Exception as exc:  # noqa: BLE001
+            line["torch_step"] = {"error": str(exc)[:200]}
 
     if not args.no_topk:
         t = workloads.C2

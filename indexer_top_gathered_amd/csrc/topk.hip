@@ -41,6 +41,8 @@
 // position through a bitmap; any other goes to a radix select whose 10-bit
 // digits split the remaining range into 1024 equal buckets per round, so
 // each round narrows it 1024-fold whatever the value distribution.
+#include <type_traits>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -50,8 +52,10 @@ constexpr int kTkThreads = 512;    // stage-1 workgroups of a segmented row
 constexpr int kRowThreads = 512;   // one workgroup for a whole row
 // Rows of at most this many vectors per thread are taken whole by one
 // workgroup; for longer rows the per-thread work of one workgroup outweighs
-// the second kernel of the segmented path (measured on the 16 x 32768
-// float32 decode-step rows: 16.9 us whole vs 15.7 us segmented).
+// the second kernel of the segmented path (on the 16 x 32768 float32
+// decode-step rows: 16.9 us whole vs 15.7 us segmented; a 1024-thread
+// workgroup taking such a row as one block was 1.5 us slower than the
+// segmented path inside the decode step).
 constexpr int kRowFusedVec = 4;
 constexpr int kTkMaxVec = 8;       // vectors per thread per register block
 // LDS candidates of a stage-1 workgroup: k (<= 4096) plus one vector of
@@ -704,17 +708,15 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   auto take_block = [&](u32x4 (&kv)[V], int64_t base) __attribute__((always_inline)) -> bool {
 #pragma unroll
     for (int v = 0; v < V; ++v) to_keys<BF16>(kv[v]);
-    // A threshold from this block's group maxima (raw keys): at least k
-    // scores of the block, hence of the segment, are >= it. A group is
-    // element e of every vector of this thread.
-    auto block_threshold = [&]() __attribute__((always_inline)) -> uint32_t {
-      uint32_t g[E];
+    // The E group maxima over vectors [v0, v1) of this thread, as raw keys,
+    // into g[0..E).
+    auto group_maxima = [&](uint32_t* g, int v0, int v1) __attribute__((always_inline)) {
       if (BF16) {
         uint32_t m[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m[j] = kv[0][j];
+        for (int j = 0; j < 4; ++j) m[j] = kv[v0][j];
 #pragma unroll
-        for (int v = 1; v < V; ++v)
+        for (int v = v0 + 1; v < v1; ++v)
 #pragma unroll
           for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], kv[v][j]);
 #pragma unroll
@@ -725,16 +727,43 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          g[e] = kv[0][e];
+          g[e] = kv[v0][e];
 #pragma unroll
-          for (int v = 1; v < V; ++v) g[e] = max(g[e], kv[v][e]);
+          for (int v = v0 + 1; v < v1; ++v) g[e] = max(g[e], kv[v][e]);
         }
       }
+    };
+    // A threshold from this block's group maxima (raw keys): at least k
+    // scores of the block, hence of the segment, are >= it. A group is
+    // element e of every vector of this thread or, when k asks for more
+    // groups than that, of every vector in one of S equal parts of them.
+    constexpr uint32_t kNegZero = BF16 ? 0x8000u : 0x80000000u;
+    auto split_threshold = [&](auto parts) __attribute__((always_inline)) -> uint32_t {
+      constexpr int S = decltype(parts)::value;
+      uint32_t gs[S * E];
+#pragma unroll
+      for (int p = 0; p < S; ++p) group_maxima(gs + p * E, p * (V / S), (p + 1) * (V / S));
+      uint32_t t = group_threshold<THREADS, S * E>(gs, k, sc);
+      if (t == kNegZero) t -= 1;
+      return t;
+    };
+    auto block_threshold = [&]() __attribute__((always_inline)) -> uint32_t {
       // About 2k groups: fewer, larger groups cost fewer histogram atomics
-      // and still leave a threshold near the k-th largest score. Fold the E
-      // maxima per thread in halves (a zero slot means "no group") while
-      // half of them still give 2k groups.
+      // and still leave a threshold near the k-th largest score; with fewer
+      // than k groups the threshold would admit the whole block. (With
+      // k <= 4096 and 512 threads, 2k groups take at most 4E per thread for
+      // float32 and 2E for bf16.)
       const int gpt = (2 * k + THREADS - 1) / THREADS;  // wanted groups per thread
+      if constexpr (!BF16 && V >= 4) {
+        if (gpt > 2 * E) return split_threshold(std::integral_constant<int, 4>{});  // uniform
+      }
+      if constexpr (V >= 2) {
+        if (gpt > E) return split_threshold(std::integral_constant<int, 2>{});  // uniform
+      }
+      uint32_t g[E];
+      group_maxima(g, 0, V);
+      // Fold the E maxima per thread in halves (a zero slot means "no
+      // group") while half of them still give 2k groups.
 #pragma unroll
       for (int half = E / 2; half >= 1; half /= 2) {
         if (gpt <= half) {  // uniform
@@ -747,7 +776,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       }
       uint32_t t = group_threshold<THREADS, E>(g, k, sc);
       // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
-      if (t == (BF16 ? 0x8000u : 0x80000000u)) t -= 1;
+      if (t == kNegZero) t -= 1;
       return t;
     };
     auto admit_block = [&](uint32_t t) __attribute__((always_inline)) -> uint64_t {
@@ -845,18 +874,25 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     }
     return false;
   };
-  u32x4 ka[V], kb[V], kc[V];
-  load_block(ka, seg_start);
-  if (seg_start + kBlock < seg_end) load_block(kb, seg_start + kBlock);
-  for (int64_t base = seg_start; base < seg_end; base += 3 * kBlock) {
-    if (base + 2 * kBlock < seg_end) load_block(kc, base + 2 * kBlock);
-    if (take_block(ka, base)) return;
-    if (base + kBlock >= seg_end) break;
-    if (base + 3 * kBlock < seg_end) load_block(ka, base + 3 * kBlock);
-    if (take_block(kb, base + kBlock)) return;
-    if (base + 2 * kBlock >= seg_end) break;
-    if (base + 4 * kBlock < seg_end) load_block(kb, base + 4 * kBlock);
-    if (take_block(kc, base + 2 * kBlock)) return;
+  if constexpr (FUSED) {
+    // A whole row is one register block (the plan sizes V so).
+    u32x4 ka[V];
+    load_block(ka, seg_start);
+    take_block(ka, seg_start);
+  } else {
+    u32x4 ka[V], kb[V], kc[V];
+    load_block(ka, seg_start);
+    if (seg_start + kBlock < seg_end) load_block(kb, seg_start + kBlock);
+    for (int64_t base = seg_start; base < seg_end; base += 3 * kBlock) {
+      if (base + 2 * kBlock < seg_end) load_block(kc, base + 2 * kBlock);
+      if (take_block(ka, base)) return;
+      if (base + kBlock >= seg_end) break;
+      if (base + 3 * kBlock < seg_end) load_block(ka, base + 3 * kBlock);
+      if (take_block(kb, base + kBlock)) return;
+      if (base + 2 * kBlock >= seg_end) break;
+      if (base + 4 * kBlock < seg_end) load_block(kb, base + 4 * kBlock);
+      if (take_block(kc, base + 2 * kBlock)) return;
+    }
   }
   if (FUSED) {
     // The row's candidates are all here: select the k winners and write them.

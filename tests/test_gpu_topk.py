@@ -38,7 +38,8 @@ def _ties(B, N, levels, seed, dtype):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("N,k", [(1, 1), (5, 5), (7, 3), (100, 1), (4096, 4096), (4097, 100),
                                  (10001, 1000), (40000, 333), (131072, 512), (300000, 2048),
-                                 (50000, 4096)])
+                                 (50000, 4096), (8193, 1024), (16385, 4096), (32769, 777),
+                                 (65536, 2048), (8000, 4000)])
 def test_random_rows(dtype, N, k):
     B = 3 if N < 200000 else 2
     x = workloads.normal_rows(B, N, "bf16" if dtype == torch.bfloat16 else "f32", 1234 + N,

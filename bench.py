@@ -470,7 +470,11 @@ def bandwidth_probe(dev, stream) -> dict:
     fraction against what this GPU delivers as well as against 8 TB/s: a
     read-only row reduction (sums of rows of 4096 floats; of the torch
     reductions tried it streams fastest, a whole-tensor sum reaches about
-    two thirds of it) and a copy (read + write)."""
+    two thirds of it) and a copy (read + write). The row reduction is also
+    timed in calls of 128 MiB each, the indexer's key bytes per step, taken
+    in turn from the 8 eighths of the GiB (so none is served from the 256 MB
+    Infinity Cache): the rate a single launch of that size reaches, its
+    start and drain included."""
     import torch
     n = 1 << 30
     x = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -478,17 +482,26 @@ def bandwidth_probe(dev, stream) -> dict:
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     out = {}
-    for name, fn, nbytes in (("read_GBps (row sums, 1 GiB)", lambda: x.view(-1, 4096).sum(1), n),
-                             ("copy_GBps (read + write, 1 GiB each)", lambda: y.copy_(x), 2 * n)):
+    eighths = x.view(8, -1, 4096)
+    calls = [0]
+
+    def eighth_sum():
+        calls[0] += 1
+        return eighths[calls[0] % 8].sum(1)
+
+    for name, fn, nbytes, reps in (
+            ("read_GBps (row sums, 1 GiB)", lambda: x.view(-1, 4096).sum(1), n, 10),
+            ("copy_GBps (read + write, 1 GiB each)", lambda: y.copy_(x), 2 * n, 10),
+            ("read_GBps (row sums, 128 MiB per call)", eighth_sum, n // 8, 80)):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(10):
+        for _ in range(reps):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / 10
+        us = e0.elapsed_time(e1) * 1e3 / reps
         out[name] = round(nbytes / (us * 1e-6) / 1e9, 1)
     del x, y
     return out
@@ -565,6 +578,8 @@ def main():
         read = probe["read_GBps (row sums, 1 GiB)"]
         roofline["measured_hbm"] = probe
         roofline["frac_of_measured_read"] = round(achieved / read, 4)
+        roofline["frac_of_measured_read_same_size"] = round(
+            achieved / probe["read_GBps (row sums, 128 MiB per call)"], 4)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

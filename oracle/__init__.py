@@ -17,6 +17,7 @@ paragraphs.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -34,58 +35,89 @@ BF16 = 0
 F32 = 1
 
 
+def compile_source(src: str, dst: str) -> str:
+    """Compile a C oracle source with gcc (-O2, OpenMP, no fast math, no FMA
+    contraction) into the shared library dst."""
+    tmp = dst + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+           "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, dst)
+    return dst
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (-O2, OpenMP) into liboracle.so."""
+    """Compile oracle.c into liboracle.so."""
     if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
         return _LIB_PATH
-    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-           "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    return compile_source(_SRC, _LIB_PATH)
+
+
+def source_path() -> str:
+    """Path of oracle.c."""
+    return _SRC
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route every oracle call through the library at path for the duration
+    (a build of a deliberately altered copy of oracle.c: the tests use it to
+    show that the pins catch planted mistakes)."""
+    global _lib
+    lib = _configure(ctypes.CDLL(path))
+    with _lock:
+        saved = _lib
+        _lib = lib
+    try:
+        yield
+    finally:
+        with _lock:
+            _lib = saved
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            path = build(force=False)
-            lib = ctypes.CDLL(path)
-            P = ctypes.c_void_p
-            I = ctypes.c_int
-            lib.oracle_bf16_decode.argtypes = [P, P, ctypes.c_int64]
-            lib.oracle_bf16_decode.restype = None
-            lib.oracle_indexer.argtypes = [P, P, P, P, I, I, I, I]
-            lib.oracle_indexer.restype = None
-            lib.oracle_topk.argtypes = [P, I, I, I, I, P, I]
-            lib.oracle_topk.restype = I
-            lib.oracle_attend.argtypes = [P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double]
-            lib.oracle_attend.restype = I
-            lib.oracle_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
-                                        ctypes.c_double]
-            lib.oracle_step.restype = I
-            lib.oracle_topk_ragged.argtypes = [P, I, I, I, P, I, P, I]
-            lib.oracle_topk_ragged.restype = I
-            lib.oracle_step_ragged.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
-                                               I, ctypes.c_double]
-            lib.oracle_step_ragged.restype = I
-            lib.oracle_indexer_mt.argtypes = [P, P, P, P, I, I, I, I, I]
-            lib.oracle_indexer_mt.restype = None
-            lib.oracle_attend_mt.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I,
-                                             ctypes.c_double]
-            lib.oracle_attend_mt.restype = I
-            lib.oracle_step_mt.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
-                                           I, ctypes.c_double]
-            lib.oracle_step_mt.restype = I
-            lib.oracle_qproj.argtypes = [P, P, P, I, I, I]
-            lib.oracle_qproj.restype = None
-            lib.oracle_set_threads.argtypes = [I]
-            lib.oracle_set_threads.restype = None
-            lib.oracle_max_threads.argtypes = []
-            lib.oracle_max_threads.restype = I
-            _lib = lib
+            _lib = _configure(ctypes.CDLL(build(force=False)))
     return _lib
+
+
+def _configure(lib):
+    """Argument and result types of every oracle entry point."""
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_bf16_decode.argtypes = [P, P, ctypes.c_int64]
+    lib.oracle_bf16_decode.restype = None
+    lib.oracle_indexer.argtypes = [P, P, P, P, I, I, I, I]
+    lib.oracle_indexer.restype = None
+    lib.oracle_topk.argtypes = [P, I, I, I, I, P, I]
+    lib.oracle_topk.restype = I
+    lib.oracle_attend.argtypes = [P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double]
+    lib.oracle_attend.restype = I
+    lib.oracle_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                ctypes.c_double]
+    lib.oracle_step.restype = I
+    lib.oracle_topk_ragged.argtypes = [P, I, I, I, P, I, P, I]
+    lib.oracle_topk_ragged.restype = I
+    lib.oracle_step_ragged.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                       I, ctypes.c_double]
+    lib.oracle_step_ragged.restype = I
+    lib.oracle_indexer_mt.argtypes = [P, P, P, P, I, I, I, I, I]
+    lib.oracle_indexer_mt.restype = None
+    lib.oracle_attend_mt.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I,
+                                     ctypes.c_double]
+    lib.oracle_attend_mt.restype = I
+    lib.oracle_step_mt.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                   I, ctypes.c_double]
+    lib.oracle_step_mt.restype = I
+    lib.oracle_qproj.argtypes = [P, P, P, I, I, I]
+    lib.oracle_qproj.restype = None
+    lib.oracle_set_threads.argtypes = [I]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = I
+    return lib
 
 
 def set_threads(n: int) -> None:

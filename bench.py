@@ -23,7 +23,8 @@ with plain torch ops on this GPU (context), `topk` the top-k-only workload
 host.
 
 `--workload` times one of the other workloads instead (for profiling; one
-JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096),
+JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096; also
+replayed from one HIP graph holding a step per input copy),
 `topk-sampling` (float32 128 x 129280, k=1024, values), `topk-stress`
 (quantised rows, half sorted, 64 x 262144, k=2048, bf16 and float32) or
 `stress-step` (B=64, N=262144, k=2048, scores equal to the stress rows) or
@@ -157,6 +158,46 @@ def time_calls(fn, n_warm, n_timed, stream):
     return e0.elapsed_time(e1) * 1e3 / n_timed
 
 
+def graph_replay_us(s, copies, out, ws, steps) -> dict:
+    """The same steps captured into one HIP graph (one step per input copy,
+    in rotation order) and replayed back to back: the launch cost per step
+    without host enqueue. A failure here is reported, not raised."""
+    import torch
+    import indexer_top_gathered_amd as dsa
+    R = len(copies)
+
+    def record():
+        for c in copies:  # on the current stream: the capture stream inside the graph
+            dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                c["kv_win"], s.k, s.scale, out=out, ws=ws)
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            record()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            record()
+        torch.cuda.synchronize()
+        replays = max(2, steps // R)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * R)
+        del g
+        return {"us_per_step": round(us, 2), "steps_per_graph": R, "replays": replays}
+    except Exception as exc:  # noqa: BLE001
+        return {"error": str(exc)[:200]}
+
+
 def other_workload(args):
     """One JSON line for a workload other than the production step."""
     import torch
@@ -192,6 +233,8 @@ def other_workload(args):
                      "frac_of_roofline": round(roof / us, 4), "rotating_input_copies": R,
                      "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
                                 "W": s.W, "H_q": s.H_q, "D": s.D}})
+        if args.workload == "tiny-step":
+            line["graph"] = graph_replay_us(s, copies, out, ws, args.steps)
         print(json.dumps(line), flush=True)
         return
     if args.workload == "ragged-step":

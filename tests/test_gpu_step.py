@@ -59,6 +59,9 @@ def run_step(s: workloads.StepShape, inp: dict, where: str, rows=None):
     workloads.StepShape(B=3, N=1001, H_I=13, D_I=128, k=77, W=5, H_q=32, D=128),
     workloads.StepShape(B=2, N=9000, H_I=64, D_I=128, k=1024, W=128, H_q=128, D=512),
     workloads.StepShape(B=5, N=33333, H_I=64, D_I=128, k=2048, W=0, H_q=64, D=512),
+    workloads.StepShape(B=2, N=5000, H_I=64, D_I=128, k=4096, W=128, H_q=128, D=512),  # largest k
+    workloads.StepShape(B=200, N=700, H_I=8, D_I=128, k=64, W=16, H_q=16, D=128),     # many rows
+    workloads.StepShape(B=3, N=257, H_I=1, D_I=128, k=256, W=1, H_q=16, D=512),       # one head
 ])
 def test_small_steps(shape):
     inp = workloads.step_inputs(shape, 31000 + shape.N, device=DEV)

@@ -553,7 +553,7 @@ def bandwidth_probe(dev, stream) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(batch rows are independent, so N GPUs would each run this same kernel set "
               "on B/N rows).", file=sys.stderr)
         sys.exit(2)

@@ -157,3 +157,26 @@ def test_ragged_and_multi_token_argument_errors(lib):
                                 ctypes.byref(ok), 2, v(P), two - 1, None) == WS_SMALL
     big = _dims(lib, B=20000)
     assert L.dsa_decode_step_mt_workspace_bytes(ctypes.byref(big), 4) == 0  # B*T > 65535
+
+
+def test_package_import_fails_loudly_without_the_library(tmp_path):
+    # A copy of the Python package with no libdsa.so beside it: importing it
+    # must raise, never fall back to another implementation.
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "indexer_top_gathered_amd")
+    dst = tmp_path / "indexer_top_gathered_amd"
+    dst.mkdir()
+    for name in ("__init__.py", "binding.py"):
+        shutil.copy(os.path.join(pkg, name), dst / name)
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "try:\n"
+            "    import indexer_top_gathered_amd\n"
+            "except ImportError as e:\n"
+            "    print('ImportError:', e); sys.exit(3)\n"
+            "sys.exit(0)\n")
+    res = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 3, res.stdout + res.stderr
+    assert "libdsa.so is missing" in res.stdout

@@ -24,8 +24,12 @@ def declared_symbols():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB_PATH):
-        from indexer_top_gathered_amd import build
-        build.build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_dsa_build", os.path.join(ROOT, "indexer_top_gathered_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     from indexer_top_gathered_amd import binding
     return binding
 

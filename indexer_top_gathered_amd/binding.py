@@ -9,6 +9,8 @@ libdsa.so; if the library is missing, importing this module raises.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 
 import torch
@@ -65,7 +67,8 @@ class DsaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with indexer_top_gathered_amd.build.build()")
+            f"{LIB_PATH} is missing: build it with `python indexer_top_gathered_amd/build.py` "
+            "(or __graft_entry__.build() at the repository root)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     D = ctypes.POINTER(DsaDims)
@@ -122,6 +125,32 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _on_stream(fn):
+    """Run the wrapper with its `stream` argument as torch's current stream,
+    so that the outputs and the workspace it allocates belong to the stream
+    the kernels run on: the caching allocator then reuses a dropped
+    workspace only for work ordered after them on that stream. A raw
+    hipStream_t handle is wrapped as an external stream."""
+    pos = list(inspect.signature(fn).parameters).index("stream")
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        st = kwargs.get("stream", args[pos] if len(args) > pos else None)
+        if st is None:
+            return fn(*args, **kwargs)
+        if not isinstance(st, torch.cuda.Stream):
+            st = torch.cuda.ExternalStream(int(st))
+        if len(args) > pos:
+            args = args[:pos] + (st,) + args[pos + 1:]
+        else:
+            kwargs["stream"] = st
+        if st == torch.cuda.current_stream(st.device):
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(st):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -154,6 +183,7 @@ def make_dims(B, N, H_I, D_I, k, W, H_q, D, scale) -> DsaDims:
 
 # ------------------------------------------------------------------ indexer
 
+@_on_stream
 def dsa_indexer_score(q_idx, k_idx, w, scores=None, stream=None):
     """scores[b,j] = sum_h w[b,h] * relu(q_idx[b,h,:] . k_idx[b,j,:]) (float32 [B,N])."""
     B, H, DI = q_idx.shape
@@ -169,6 +199,7 @@ def dsa_indexer_score(q_idx, k_idx, w, scores=None, stream=None):
     return scores
 
 
+@_on_stream
 def dsa_indexer_qproj(x, w_q, H_I: int, q_idx=None, stream=None):
     """Indexer query projection: x bf16 [B, d_in], w_q bf16 [H_I*128, d_in]
     -> q_idx bf16 [B, H_I, 128] = x @ w_q^T (fp32 sums, rounded to bf16)."""
@@ -183,6 +214,7 @@ def dsa_indexer_qproj(x, w_q, H_I: int, q_idx=None, stream=None):
     return q_idx
 
 
+@_on_stream
 def dsa_indexer_score_mt(q_idx, k_idx, w, scores=None, stream=None):
     """T query tokens per batch row sharing its keys: q_idx bf16 [B,T,H,D_I],
     k_idx [B,N,D_I], w float32 [B,T,H] -> scores float32 [B,T,N]."""
@@ -206,6 +238,7 @@ def dsa_topk_workspace_bytes(B: int, N: int, k: int, dtype=torch.float32) -> int
     return int(LIB.dsa_topk_workspace_bytes(int(B), int(N), int(k), dt))
 
 
+@_on_stream
 def dsa_topk(scores, k: int, return_values: bool = False, sorted_index: bool = False,
              out_idx=None, out_val=None, ws=None, stream=None):
     """Indices (int32 [B,k]) of the k largest scores per row, lower index
@@ -213,6 +246,7 @@ def dsa_topk(scores, k: int, return_values: bool = False, sorted_index: bool = F
     return _topk(scores, None, k, return_values, sorted_index, out_idx, out_val, ws, stream)
 
 
+@_on_stream
 def dsa_topk_ragged(scores, lengths, k: int, return_values: bool = False,
                     sorted_index: bool = False, out_idx=None, out_val=None, ws=None, stream=None):
     """dsa_topk over each row's first lengths[b] scores (lengths: int32 [B]
@@ -254,6 +288,7 @@ def dsa_sparse_attend_workspace_bytes(dims: DsaDims) -> int:
     return int(LIB.dsa_sparse_attend_workspace_bytes(ctypes.byref(dims)))
 
 
+@_on_stream
 def dsa_sparse_attend(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, stream=None):
     """bf16 [B,H_q,D] = softmax(scale * q R^T) R over R = kv_cmp[idx] ++ kv_win."""
     B, Hq, D = q.shape
@@ -276,6 +311,7 @@ def dsa_sparse_attend(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, s
     return out
 
 
+@_on_stream
 def dsa_sparse_attend_mt(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, stream=None):
     """T query tokens per batch row sharing its compressed rows: q bf16
     [B,T,H_q,D], kv_cmp [B,N,D], idx int32 [B,T,k], kv_win [B,T,W,D] or None
@@ -306,6 +342,7 @@ def dsa_decode_step_workspace_bytes(dims: DsaDims) -> int:
     return int(LIB.dsa_decode_step_workspace_bytes(ctypes.byref(dims)))
 
 
+@_on_stream
 def dsa_decode_step(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, out=None,
                     out_idx=None, ws=None, stream=None, return_idx: bool = False):
     """Indexer scores -> top-k -> sparse attention in one enqueue sequence."""
@@ -313,6 +350,7 @@ def dsa_decode_step(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, ou
                  return_idx)
 
 
+@_on_stream
 def dsa_decode_step_ragged(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k: int, scale: float,
                            out=None, out_idx=None, ws=None, stream=None,
                            return_idx: bool = False):
@@ -362,6 +400,7 @@ def dsa_decode_step_mt_workspace_bytes(dims: DsaDims, T: int) -> int:
     return int(LIB.dsa_decode_step_mt_workspace_bytes(ctypes.byref(dims), int(T)))
 
 
+@_on_stream
 def dsa_decode_step_mt(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, lengths=None,
                        out=None, out_idx=None, ws=None, stream=None, return_idx: bool = False):
     """The step with T query tokens per batch row sharing its keys: q_idx

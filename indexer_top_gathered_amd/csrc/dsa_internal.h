@@ -168,13 +168,12 @@ __device__ __forceinline__ uint32_t lds_byte_addr(const void* p) {
 // is issued from inline assembly so that the compiler, which cannot tell
 // these LDS writes apart from later LDS reads, does not wait for every
 // outstanding copy before each read; the kernel waits with explicit vmcnt
-// values instead. No register is written asynchronously.
-// The kernels here use M0 for nothing else; the clobber documents the write
-// (the compiler reserves M0 and warns about the clobber; the build silences
-// that warning).
+// values instead. No register is written asynchronously. M0 is an input
+// operand ("{m0}"), so the compiler writes it and knows it is in use; the
+// s_nop gives the one wait state the ISA asks for between an M0 write and an
+// LDS-DMA load.
 __device__ __forceinline__ void dma_row16(const void* g, uint32_t lds_byte) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds_byte) : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(lds_byte) : "memory");
 }
 
 // ---------------------------------------------------------------- launchers

@@ -411,6 +411,25 @@ def indexer_bytes(s) -> int:
     return b * s.N * s.D_I * 2 + b * s.H_I * s.D_I * 2 + b * s.H_I * 4 + b * s.N * 4
 
 
+def topk_stage_bytes(B: int, N: int, k: int, esz: int, values: bool = False) -> int:
+    """Algorithmic bytes of one top-k call: the score rows read once, the
+    indices (and values) written once."""
+    return B * N * esz + B * k * 4 + (B * k * esz if values else 0)
+
+
+def attend_bytes(s) -> int:
+    """Algorithmic bytes of one sparse-attention call: q, the index array,
+    the k gathered rows and W window rows of every batch row read once (a
+    row is both K and V), the output written once."""
+    b = s.B
+    return (b * s.H_q * s.D * 2 + b * s.k * 4 + b * (s.k + s.W) * s.D * 2
+            + b * s.H_q * s.D * 2)
+
+
+def attend_flops(s) -> int:
+    return 4 * s.B * s.H_q * (s.k + s.W) * s.D
+
+
 def source_digest(parts) -> str:
     """Hash of the code a kernel is built and launched from. parts: paths,
     or (path, start, stop) to take the text from the first `start` up to the
@@ -433,35 +452,60 @@ def source_digest(parts) -> str:
     return h.hexdigest()[:16]
 
 
-def indexer_source_parts():
-    """The one-token indexer's code: its row sweep and kernel (the file up
-    to the ragged kernel's first helper), its launcher, and the internal
-    header; the multi-token and ragged kernels are left out."""
+def library_source_parts():
+    """Every source libdsa.so is built from (kernels, launchers, the ABI)."""
     csrc = os.path.join(ROOT, "indexer_top_gathered_amd", "csrc")
-    f = os.path.join(csrc, "indexer_score.hip")
-    return [(f, None, "__device__ __forceinline__ uint32_t valid_rounds("),
-            (f, "hipError_t launch_indexer_score(", None),
-            os.path.join(csrc, "dsa_internal.h")]
+    return [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))
+            if f.endswith((".hip", ".h"))]
 
 
-def traffic_from_profile(kernel_srcs):
-    """HBM bytes per launch recorded by the rocprofv3 counter runs, if they
-    were taken on the current kernel code (source_digest of kernel_srcs);
-    else None."""
-    path = os.path.join(ROOT, "profiles", "indexer_score_decode_step_counters.md")
-    if not os.path.exists(path):
-        return None
+COUNTERS = os.path.join(ROOT, "profiles", "decode_step_b16_n32768_counters.md")
+
+
+def traffic_from_profile():
+    """HBM bytes per dispatch of each kernel, from the two rocprofv3 counter
+    passes summarised in profiles/ (FETCH_SIZE and WRITE_SIZE, scaled by a
+    copy of known size), if they were taken on the current library sources
+    (source_digest of library_source_parts); else {}."""
+    if not os.path.exists(COUNTERS):
+        return {}
     vals = {}
-    for line in open(path):
+    for line in open(COUNTERS, encoding="utf-8"):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
-            vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel_source_sha256_16") != source_digest(kernel_srcs):
-        return None
+            vals[k.strip().strip("`")] = v.strip().strip("`")
+    if vals.get("library_source_sha256_16") != source_digest(library_source_parts()):
+        return {}
+    out = {}
+    for k, v in vals.items():
+        if k.startswith("hbm_bytes_per_dispatch "):
+            try:
+                out[k.split(" ", 1)[1]] = float(v)
+            except ValueError:
+                pass
+    return out
+
+
+def check_topk_output(idx, N: int, k: int, where: str) -> None:
+    """Every row holds k distinct positions in [0, N) (checked on the
+    device); raises otherwise."""
+    import torch
+    srt = torch.sort(idx.long(), dim=1).values
+    ok = (bool((srt[:, 0] >= 0).all()) and bool((srt[:, -1] < N).all())
+          and (k == 1 or bool((srt[:, 1:] != srt[:, :-1]).all())))
+    if idx.shape[1] != k or not ok:
+        raise RuntimeError(f"{where}: the timed output is not k distinct in-range indices")
+
+
+def cpu_model() -> str:
     try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def torch_step(c, s):
@@ -550,6 +594,23 @@ def bandwidth_probe(dev, stream) -> dict:
     return out
 
 
+def stage(name: str, kernels: str, nbytes: int, us: float, flops: int = 0, traffic=None) -> dict:
+    """One stage of the step against its own roofline: the larger of its
+    HBM time at 8 TB/s and its MFMA time at 2.5 PFLOP/s."""
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9) * 1e6
+    t_mfma = flops / 2.5e15 * 1e6
+    d = {"kernels": kernels, "us": round(us, 3), "algorithmic_bytes": nbytes,
+         "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+         "roofline_us": round(max(t_hbm, t_mfma), 3),
+         "frac": round(max(t_hbm, t_mfma) / us, 4),
+         "bound": "hbm" if t_hbm >= t_mfma else "mfma"}
+    if flops:
+        d["flops"] = flops
+        d["mfma_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 1)
+    d["traffic"] = traffic
+    return d
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -572,57 +633,91 @@ def main():
     dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
     ws = torch.empty(dsa.dsa_decode_step_workspace_bytes(dims), dtype=torch.uint8, device=dev)
     out = torch.empty((s.B, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+    oidx = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
         c = copies[i % R]
         dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"], c["kv_win"],
-                            s.k, s.scale, out=out, ws=ws, stream=stream)
+                            s.k, s.scale, out=out, out_idx=oidx, ws=ws, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    us_step = ms_per_step * 1e3
+    us_step = time_calls(step, args.warmup, args.steps, stream)
+    ms_per_step = us_step / 1e3
     sbytes = step_bytes(s)
     value = sbytes / (us_step * 1e-6) / 1e9
+    # The timed loop's last output: k distinct in-range indices per row, and
+    # bit-identical to an untimed call on the same inputs.
+    last = (args.steps - 1) % R
+    check_topk_output(oidx, s.N, s.k, "decode step")
+    c = copies[last]
+    out_chk, idx_chk = dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                           c["kv_win"], s.k, s.scale, return_idx=True)
+    torch.cuda.synchronize()
+    if not (torch.equal(idx_chk, oidx) and torch.equal(out_chk.view(torch.int16),
+                                                      out.view(torch.int16))):
+        raise RuntimeError("decode step: the timed output differs from an untimed call")
+    del out_chk, idx_chk
 
-    # Dominant kernel: indexer scoring, same launch configuration as inside
-    # the step, timed alone on the same stream over the same rotation.
+    # Each stage alone, in the step's launch configuration, on the same
+    # stream over the same rotation.
+    traffic = traffic_from_profile()
+
+    def tsum(*names):
+        vals = [traffic.get(n) for n in names]
+        return None if not vals or any(v is None for v in vals) else round(sum(vals))
+
     scores = torch.empty((s.B, s.N), dtype=torch.float32, device=dev)
-    for i in range(args.warmup):
+    sel = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
+    tws = torch.empty(dsa.dsa_topk_workspace_bytes(s.B, s.N, s.k, torch.float32),
+                      dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(256, dsa.dsa_sparse_attend_workspace_bytes(dims)), dtype=torch.uint8,
+                      device=dev)
+
+    def is_call(i):
         c = copies[i % R]
         dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"], scores=scores, stream=stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
+    is_us = time_calls(is_call, args.warmup, args.steps, stream)
+    # Score rows of every copy for the top-k and attention legs.
+    all_scores = [dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"]) for c in copies]
+    all_idx = [dsa.dsa_topk(sc, s.k) for sc in all_scores]
+
+    def tk_call(i):
+        dsa.dsa_topk(all_scores[i % R], s.k, out_idx=sel, ws=tws, stream=stream)
+    tk_us = time_calls(tk_call, args.warmup, args.steps, stream)
+
+    def sa_call(i):
         c = copies[i % R]
-        dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"], scores=scores, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    is_us = e0.elapsed_time(e1) * 1e3 / args.steps
-    is_bytes = indexer_bytes(s)
-    achieved = is_bytes / (is_us * 1e-6) / 1e9
-    traffic = traffic_from_profile(indexer_source_parts())
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": "indexer_score_kernel<4>",
-                "us_per_launch": round(is_us, 3), "bytes_per_launch": is_bytes}
+        dsa.dsa_sparse_attend(c["q"], c["kv_cmp"], all_idx[i % R], c["kv_win"], s.scale,
+                              out=out, ws=aws, stream=stream)
+    sa_us = time_calls(sa_call, args.warmup, args.steps, stream)
+    del all_scores, all_idx
+
+    kernels = {
+        "indexer": stage("indexer", "indexer_score_kernel<4>", indexer_bytes(s), is_us,
+                         flops=2 * s.B * s.N * s.H_I * s.D_I,
+                         traffic=tsum("indexer_score_kernel<4>")),
+        "topk": stage("topk", "topk_segment_kernel + topk_merge_kernel (float32 rows)",
+                      topk_stage_bytes(s.B, s.N, s.k, 4), tk_us),
+        "attention": stage("attention", "sparse_attend_kernel<512, 4, 2> + attend_combine_kernel<512>",
+                           attend_bytes(s), sa_us, flops=attend_flops(s)),
+    }
+    roof_us = step_roofline_us(s)
+    step_traffic = tsum(*[k for k in traffic]) if traffic else None
+    roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": step_traffic,
+                "what": "the whole decode step: compulsory bytes per step / time per step",
+                "roofline_us": round(roof_us, 3), "us_per_step": round(us_step, 2),
+                "frac_of_step_roofline": round(roof_us / us_step, 4),
+                "bytes_per_step": sbytes, "kernels": kernels}
 
     if args.latency_calls > 0:
         probe = bandwidth_probe(dev, stream)
-        read = probe["read_GBps (row sums, 1 GiB)"]
         roofline["measured_hbm"] = probe
-        roofline["frac_of_measured_read"] = round(achieved / read, 4)
-        roofline["frac_of_measured_read_same_size"] = round(
-            achieved / probe["read_GBps (row sums, 128 MiB per call)"], 4)
+        ia = kernels["indexer"]["achieved_GBps"]
+        kernels["indexer"]["frac_of_measured_read"] = round(
+            ia / probe["read_GBps (row sums, 1 GiB)"], 4)
+        kernels["indexer"]["frac_of_measured_read_same_size"] = round(
+            ia / probe["read_GBps (row sums, 128 MiB per call)"], 4)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -635,13 +730,17 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
     }
-    del scores
+    del scores, sel, tws, aws
+
+    line["graph"] = graph_replay_us(s, copies, out, ws, args.steps)
     if args.latency_calls > 0:
         line["single_call_latency"] = single_call_latency(step, args.latency_calls, dev, stream)
         # The same step in plain torch ops on this GPU, over the same rotation
         # (context only: a failure here is reported, not raised).
         try:
             n_ref = max(10, args.steps // 10)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 for i in range(3):
                     torch_step(copies[i % R], s)
@@ -662,34 +761,32 @@ def main():
         rows = [workloads.normal_rows(t.B, t.N, "bf16", 2006 + r, device=dev) for r in range(R)]
         tws = torch.empty(dsa.dsa_topk_workspace_bytes(t.B, t.N, t.k, torch.bfloat16),
                           dtype=torch.uint8, device=dev)
-        oidx = torch.empty((t.B, t.k), dtype=torch.int32, device=dev)
-        for i in range(args.warmup):
-            dsa.dsa_topk(rows[i % R], t.k, out_idx=oidx, ws=tws, stream=stream)
+        tidx = torch.empty((t.B, t.k), dtype=torch.int32, device=dev)
+
+        def tk2(i):
+            dsa.dsa_topk(rows[i % R], t.k, out_idx=tidx, ws=tws, stream=stream)
+        tk_us = time_calls(tk2, args.warmup, args.steps, stream)
+        check_topk_output(tidx, t.N, t.k, "top-k")
+        again = dsa.dsa_topk(rows[(args.steps - 1) % R], t.k)
         torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(args.steps):
-            dsa.dsa_topk(rows[i % R], t.k, out_idx=oidx, ws=tws, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        tk_us = e0.elapsed_time(e1) * 1e3 / args.steps
-        tbytes = t.B * t.N * 2 + t.B * t.k * 4
-        # torch.topk on the same rows, as the context ratio the pages report
-        for i in range(3):
+        if not torch.equal(again, tidx):
+            raise RuntimeError("top-k: the timed output differs from an untimed call")
+        tbytes = topk_stage_bytes(t.B, t.N, t.k, 2)
+
+        def ref(i):
             torch.topk(rows[i % R], t.k, dim=1, sorted=False)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        n_ref = max(10, args.steps // 10)
-        for i in range(n_ref):
-            torch.topk(rows[i % R], t.k, dim=1, sorted=False)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ref_us = e0.elapsed_time(e1) * 1e3 / n_ref
+        ref_us = time_calls(ref, 3, max(10, args.steps // 10), stream)
         gbps = tbytes / (tk_us * 1e-6) / 1e9
         line["topk"] = {"workload": "bf16 scores 64 x 131072, k=512, indices only, unsorted",
                         "us": round(tk_us, 2), "effective_GBps": round(gbps, 1),
-                        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "roofline_us": round(tbytes / (HBM_PEAK_GBPS * 1e9) * 1e6, 3),
                         "compulsory_bytes": tbytes, "torch_topk_us": round(ref_us, 2),
-                        "speedup_vs_torch_topk": round(ref_us / tk_us, 2)}
+                        "speedup_vs_torch_topk": round(ref_us / tk_us, 2),
+                        "output_checked": "k distinct in-range indices per row; equal to an "
+                                          "untimed call"}
+        line["metric_parts"] = {"topk_effective_GBps": round(gbps, 1),
+                                "decode_step_us": round(us_step, 2)}
         del rows
 
     if args.calibrate_copy_mib > 0:
@@ -732,6 +829,7 @@ def cpu_baseline(inp, s, sbytes):
     dt = (time.perf_counter() - t0) / reps
     return {"value": round(sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds_per_step": round(dt, 3), "host_cpus": ncpu,
+            "cpu_model": cpu_model(),
             "sample": f"the whole decode step (all 16 batch rows of the production shape), "
                       f"{reps} repetitions, mean time per step"}
 

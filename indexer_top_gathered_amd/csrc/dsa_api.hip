@@ -272,6 +272,21 @@ size_t dsa_decode_step_mt_workspace_bytes(const dsa_dims_t* dims, int T) {
 
 namespace {
 
+// Pointer checks of the fused step (the workspace is checked by the caller).
+dsa_status_t check_step_pointers(const void* q_idx, const void* k_idx, const float* w,
+                                 const void* q, const void* kv_cmp, const void* kv_win,
+                                 const int32_t* lengths, const void* out, const int32_t* out_idx,
+                                 int window) {
+  if (!q_idx || !k_idx || !w || !q || !kv_cmp || !out || (window > 0 && !kv_win))
+    return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(kv_cmp) ||
+      !aligned16(out) || (kv_win && !aligned16(kv_win)) ||
+      (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(out_idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(lengths) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
+  return DSA_SUCCESS;
+}
+
 dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, const void* q,
                        const void* kv_cmp, const void* kv_win, const int32_t* lengths, void* out,
                        int32_t* out_idx, const dsa_dims_t* dims, int T, void* ws,
@@ -283,13 +298,9 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
   if (s != DSA_SUCCESS) return s;
   s = check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim, T);
   if (s != DSA_SUCCESS) return s;
-  if (!q_idx || !k_idx || !w || !q || !kv_cmp || !out || !ws || (dims->window > 0 && !kv_win))
-    return DSA_ERROR_INVALID_VALUE;
-  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(q) || !aligned16(kv_cmp) ||
-      !aligned16(out) || !aligned16(ws) || (kv_win && !aligned16(kv_win)) ||
-      (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(out_idx) & 3u) ||
-      (reinterpret_cast<uintptr_t>(lengths) & 3u))
-    return DSA_ERROR_INVALID_VALUE;
+  s = check_step_pointers(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims->window);
+  if (s != DSA_SUCCESS) return s;
+  if (!ws || !aligned16(ws)) return DSA_ERROR_INVALID_VALUE;
   const StepLayout L = step_layout(*dims, T);
   if (ws_bytes < L.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();

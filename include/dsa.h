@@ -55,7 +55,8 @@ typedef enum {
   DSA_ERROR_NOT_SUPPORTED = 2,       /* shape outside the compiled range, not gfx950 */
   DSA_ERROR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the *_workspace_bytes value */
   DSA_ERROR_LAUNCH = 4,              /* a kernel launch failed */
-  DSA_ERROR_DEVICE = 5               /* no usable HIP device */
+  DSA_ERROR_DEVICE = 5,              /* no usable HIP device */
+  DSA_ERROR_SCRATCH_LIMIT = 6        /* beyond the static scratch of dsa_decode_step_noalloc */
 } dsa_status_t;
 
 /* Problem sizes of one decode step (the block shapes of "Launching a full
@@ -222,6 +223,28 @@ DSA_EXPORT dsa_status_t dsa_decode_step_mt(const void* q_idx, const void* k_idx,
                                 const void* kv_win, const int32_t* lengths, void* out,
                                 int32_t* out_idx, const dsa_dims_t* dims, int T, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code being captured into a
+ * HIP graph, tight serving loops, or harnesses that forbid hipMalloc. The
+ * same step as dsa_decode_step (same kernels, same results bit for bit), but
+ * its workspace is a static device array of DSA_NOALLOC_SCRATCH_BYTES inside
+ * the library instead of a caller buffer; the call itself allocates and
+ * frees nothing. Each GPU the library runs on holds its own copy of that
+ * array from the first call there until the process ends. Every call on one
+ * GPU shares that GPU's copy, so calls that may overlap on one GPU (on
+ * different streams, or from several host threads) race and must not be
+ * issued; calls ordered on one stream are fine. Nothing in the scratch needs
+ * to start at zero. A shape whose dsa_decode_step_workspace_bytes exceeds
+ * DSA_NOALLOC_SCRATCH_BYTES returns DSA_ERROR_SCRATCH_LIMIT and launches
+ * nothing (the production shape, B = 16, N = 32768, k = 1024, H_q = 128,
+ * D = 512, needs about 19 MiB). Arguments and other errors as dsa_decode_step.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+DSA_EXPORT dsa_status_t dsa_decode_step_noalloc(const void* q_idx, const void* k_idx,
+                                     const float* w, const void* q, const void* kv_cmp,
+                                     const void* kv_win, void* out, int32_t* out_idx,
+                                     const dsa_dims_t* dims, void* stream);
 
 /* A static, human-readable name for a status code (never NULL). */
 DSA_EXPORT const char* dsa_status_string(dsa_status_t status);

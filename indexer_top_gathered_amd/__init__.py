@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     dsa_decode_step,
     dsa_decode_step_mt,
     dsa_decode_step_mt_workspace_bytes,
+    NOALLOC_SCRATCH_BYTES,
+    dsa_decode_step_noalloc,
     dsa_decode_step_ragged,
     dsa_decode_step_workspace_bytes,
     dsa_indexer_qproj,

@@ -37,8 +37,12 @@ EXPORTED = (
     "dsa_decode_step_mt_workspace_bytes",
     "dsa_decode_step_mt",
     "dsa_indexer_qproj",
+    "dsa_decode_step_noalloc",
     "dsa_status_string",
 )
+
+# Size of the static workspace of dsa_decode_step_noalloc (DSA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class DsaDims(ctypes.Structure):
@@ -102,6 +106,8 @@ def _load() -> ctypes.CDLL:
     lib.dsa_decode_step_mt.restype = I
     lib.dsa_indexer_qproj.argtypes = [P, P, P, I, I, I, I, P]
     lib.dsa_indexer_qproj.restype = I
+    lib.dsa_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, D, P]
+    lib.dsa_decode_step_noalloc.restype = I
     lib.dsa_status_string.argtypes = [I]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -433,4 +439,33 @@ def dsa_decode_step_mt(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float,
                                   _ptr(kv_win if W else None), _ptr(lengths), _ptr(out),
                                   _ptr(out_idx), ctypes.byref(dims), T, _ptr(ws), ws.numel(),
                                   _stream(stream)), "dsa_decode_step_mt")
+    return (out, out_idx) if out_idx is not None else out
+
+
+@_on_stream
+def dsa_decode_step_noalloc(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, out,
+                            out_idx=None, stream=None):
+    """dsa_decode_step with the library's static workspace: the C call
+    allocates nothing, and this wrapper allocates nothing either (the caller
+    passes `out`, and `out_idx` if wanted). Calls that overlap on one GPU
+    share that workspace and race."""
+    B, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq, D = q.shape[1], q.shape[2]
+    W = 0 if kv_win is None else kv_win.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, DI))
+    _need(w, "w", torch.float32, (B, H))
+    _need(q, "q", torch.bfloat16, (B, Hq, D))
+    _need(kv_cmp, "kv_cmp", torch.bfloat16, (B, N, D))
+    if kv_win is not None:
+        _need(kv_win, "kv_win", torch.bfloat16, (B, W, D))
+    _need(out, "out", torch.bfloat16, (B, Hq, D))
+    if out_idx is not None:
+        _need(out_idx, "out_idx", torch.int32, (B, k))
+    dims = make_dims(B, N, H, DI, k, W, Hq, D, scale)
+    _check(LIB.dsa_decode_step_noalloc(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
+                                       _ptr(kv_win if W else None), _ptr(out), _ptr(out_idx),
+                                       ctypes.byref(dims), _stream(stream)),
+           "dsa_decode_step_noalloc")
     return (out, out_idx) if out_idx is not None else out

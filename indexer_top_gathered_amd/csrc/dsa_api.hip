@@ -3,6 +3,7 @@
 // before anything is enqueued; no entry point waits for the device.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "dsa_internal.h"
 
@@ -116,6 +117,9 @@ const char* dsa_status_string(dsa_status_t s) {
     case DSA_ERROR_WORKSPACE_TOO_SMALL: return "DSA_ERROR_WORKSPACE_TOO_SMALL: workspace too small";
     case DSA_ERROR_LAUNCH: return "DSA_ERROR_LAUNCH: kernel launch failed";
     case DSA_ERROR_DEVICE: return "DSA_ERROR_DEVICE: no usable HIP device";
+    case DSA_ERROR_SCRATCH_LIMIT:
+      return "DSA_ERROR_SCRATCH_LIMIT: the shape needs more workspace than the static scratch "
+             "buffer of dsa_decode_step_noalloc holds (DSA_NOALLOC_SCRATCH_BYTES)";
   }
   return "DSA_ERROR_UNKNOWN";
 }
@@ -351,6 +355,70 @@ dsa_status_t dsa_decode_step_mt(const void* q_idx, const void* k_idx, const floa
                                 void* stream) {
   return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims, T, ws,
                    ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no allocation
+// The workspace of dsa_decode_step_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends. Host code never uses the
+// array's name as an address (on the host it names a stand-in, not device
+// memory): the device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device (looked up on the
+// first call there), or an error status.
+dsa_status_t scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return DSA_ERROR_DEVICE;
+  }
+  if (dev >= kMaxDevices) return DSA_ERROR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return DSA_ERROR_DEVICE;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_decode_step_noalloc(const void* q_idx, const void* k_idx, const float* w,
+                                     const void* q, const void* kv_cmp, const void* kv_win,
+                                     void* out, int32_t* out_idx, const dsa_dims_t* dims,
+                                     void* stream) {
+  if (!dims) return DSA_ERROR_INVALID_VALUE;
+  dsa_status_t s = check_attend_dims(dims);
+  if (s != DSA_SUCCESS) return s;
+  s = check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim);
+  if (s != DSA_SUCCESS) return s;
+  s = check_step_pointers(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx,
+                          dims->window);
+  if (s != DSA_SUCCESS) return s;
+  const size_t need = step_layout(*dims, 1).bytes;
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERROR_SCRATCH_LIMIT;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  void* ws = nullptr;
+  s = scratch_ptr(&ws);
+  if (s != DSA_SUCCESS) return s;
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx, dims, 1, ws,
+                   (size_t)DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa.h")
 LIB_PATH = os.path.join(ROOT, "indexer_top_gathered_amd", "libdsa.so")
 
-SUCCESS, INVALID, NOT_SUPPORTED, WS_SMALL, LAUNCH, DEVICE = range(6)
+SUCCESS, INVALID, NOT_SUPPORTED, WS_SMALL, LAUNCH, DEVICE, SCRATCH_LIMIT = range(7)
 
 
 def declared_symbols():
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.status_string(s).startswith("DSA_")
     assert "UNKNOWN" in lib.status_string(99)
 
@@ -118,6 +118,28 @@ def test_attend_and_step_argument_errors(lib):
                              ctypes.byref(ok), v(P), need, None) == INVALID
 
 
+def test_noalloc_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    ok = _dims(lib)
+    args = [v(P)] * 7 + [None]
+    d = _dims(lib, D=64)
+    assert L.dsa_decode_step_noalloc(*args, ctypes.byref(d), None) == NOT_SUPPORTED
+    d = _dims(lib, k=0)
+    assert L.dsa_decode_step_noalloc(*args, ctypes.byref(d), None) == INVALID
+    assert L.dsa_decode_step_noalloc(*args, None, None) == INVALID
+    bad = [v(P)] * 6 + [None, None]  # no output
+    assert L.dsa_decode_step_noalloc(*bad, ctypes.byref(ok), None) == INVALID
+    # the stress shape (64 x 262144) needs far more than the static scratch
+    big = _dims(lib, B=64, N=262144, H_I=64, k=2048, W=128, H_q=128, D=512)
+    assert lib.dsa_decode_step_workspace_bytes(big) > lib.NOALLOC_SCRATCH_BYTES
+    assert L.dsa_decode_step_noalloc(*args, ctypes.byref(big), None) == SCRATCH_LIMIT
+    # the production shape fits
+    prod = _dims(lib, B=16, N=32768, H_I=64, k=1024, W=128, H_q=128, D=512)
+    assert lib.dsa_decode_step_workspace_bytes(prod) <= lib.NOALLOC_SCRATCH_BYTES
+    assert "DSA_NOALLOC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
+
+
 def test_valid_call_without_device_reports_device_error(lib):
     import torch
     if torch.cuda.is_available():
@@ -125,6 +147,8 @@ def test_valid_call_without_device_reports_device_error(lib):
     L = lib.LIB
     v = ctypes.c_void_p
     assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 1, 10, 8, 128, None) == DEVICE
+    assert L.dsa_decode_step_noalloc(*([v(P)] * 7), None, ctypes.byref(_dims(lib)),
+                                     None) == DEVICE
 
 
 def test_ragged_and_multi_token_argument_errors(lib):

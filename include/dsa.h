@@ -75,7 +75,8 @@ typedef struct {
 
 /*
  * Lightning-indexer scores (CSA pull request, "How the algorithm works",
- * step 2: a multi-query product, a ReLU and a per-head weight):
+ * step 2): each head's query dotted with every key, clipped at zero, scaled
+ * by the head's weight and added over heads:
  *   scores[b,j] = sum_{h<H_I} w[b,h] * max(0, sum_{d<D_I} q_idx[b,h,d] * k_idx[b,j,d])
  * q_idx  bf16 [B, H_I, D_I]; k_idx bf16 [B, N, D_I]; w float [B, H_I];
  * scores float [B, N] (output). Products are exact, sums run in float32
@@ -123,9 +124,10 @@ DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, i
                       size_t ws_bytes, void* stream);
 
 /*
- * Sparse multi-query attention (CSA pull request, step 4: gather the selected
- * KV rows, add the sliding window, run multi-query attention; K and V are the
- * same embedding, per "The top-k on the GPSIMD engine"):
+ * Sparse multi-query attention (CSA pull request, step 4, and "The top-k on
+ * the GPSIMD engine"): every query head of a batch row attends over the
+ * compressed rows the top-k picked followed by the window of recent raw
+ * rows; one tensor holds both keys and values:
  *   R_b      = [kv_cmp[b, idx[b,i]] for i < k] followed by [kv_win[b,t] for t < W]
  *   out[b,h] = softmax_r(scale * q[b,h] . R_b[r]) @ R_b
  * q bf16 [B, H_q, D]; kv_cmp bf16 [B, N, D]; idx int32 [B, k] with values in

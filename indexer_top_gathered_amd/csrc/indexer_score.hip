@@ -1,7 +1,8 @@
 // Lightning-indexer scoring on gfx950 ("feat: Add DeepSeek-V4 CSA attention
-// kernels", section "How the algorithm works", step 2: a multi-query product
-// of the indexer query with every compressed key, a ReLU and a per-head
-// weight, summed over heads).
+// kernels", section "How the algorithm works", step 2). Every indexer head's
+// query is dotted with each compressed key; negative dot products are
+// clipped to zero, each head's result is scaled by that head's weight, and
+// the heads are added up.
 //
 //   s[b,j] = sum_h w[b,h] * max(0, q[b,h,:] . k[b,j,:]),   D_I = 128
 //

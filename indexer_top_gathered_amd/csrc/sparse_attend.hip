@@ -1,8 +1,8 @@
 // Sparse multi-query decode attention on gfx950 ("feat: Add DeepSeek-V4 CSA
-// attention kernels", "How the algorithm works", step 4: gather the
-// selected KV rows, add the sliding window, run multi-query attention; "The
-// top-k on the GPSIMD engine": K and V are one embedding, read once and
-// transposed on chip).
+// attention kernels", "How the algorithm works", step 4; "The top-k on the
+// GPSIMD engine"). Each batch row attends over the compressed rows its top-k
+// picked plus its recent raw rows; one tensor serves as both keys and
+// values, so a row is fetched from HBM once and used for both products.
 //
 //   R_b = kv_cmp[b, idx[b, :]] ++ kv_win[b, :]          (k + W rows of D)
 //   out[b,h,:] = softmax_r(scale * q[b,h,:] . R_b[r,:]) @ R_b

@@ -113,6 +113,10 @@ def _configure(lib):
     lib.oracle_step_mt.restype = I
     lib.oracle_qproj.argtypes = [P, P, P, I, I, I]
     lib.oracle_qproj.restype = None
+    lib.oracle_attend_sink.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_double]
+    lib.oracle_attend_sink.restype = I
+    lib.oracle_compress.argtypes = [P, P, P, I, I, I]
+    lib.oracle_compress.restype = None
     lib.oracle_set_threads.argtypes = [I]
     lib.oracle_set_threads.restype = None
     lib.oracle_max_threads.argtypes = []
@@ -204,10 +208,12 @@ def topk_ragged(scores: np.ndarray, lengths: np.ndarray, k: int,
 
 
 def attend(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win: np.ndarray | None,
-           scale: float) -> np.ndarray:
+           scale: float, sink: np.ndarray | None = None) -> np.ndarray:
     """Sparse attention. q uint16 [B,Hq,D], kv uint16 [B,N,D], idx int32 [B,k]
     (-1: an empty slot, no row), win uint16 [B,W,D] or None -> float64
-    [B,Hq,D]; a batch row with no rows at all gets zeros."""
+    [B,Hq,D]; a batch row with no rows at all gets zeros. sink: float64
+    [Hq] (finite or -inf), one logit per query head that joins the softmax
+    normalisation with no value vector, or None for none."""
     q = _c(q, np.uint16)
     kv = _c(kv, np.uint16)
     idx = _c(idx, np.int32)
@@ -222,8 +228,14 @@ def attend(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, win: np.ndarray | Non
         W = win.shape[1]
         assert win.shape == (B, W, D)
     out = np.empty((B, Hq, D), np.float64)
-    rc = _load().oracle_attend(_ptr(q), _ptr(kv), _ptr(idx), _ptr(win), _ptr(out),
-                               B, N, k, W, Hq, D, float(scale))
+    if sink is None:
+        rc = _load().oracle_attend(_ptr(q), _ptr(kv), _ptr(idx), _ptr(win), _ptr(out),
+                                   B, N, k, W, Hq, D, float(scale))
+    else:
+        sink = _c(sink, np.float64)
+        assert sink.shape == (Hq,)
+        rc = _load().oracle_attend_sink(_ptr(q), _ptr(kv), _ptr(idx), _ptr(win), _ptr(sink),
+                                        _ptr(out), B, N, k, W, Hq, D, float(scale))
     if rc != 0:
         raise ValueError("oracle_attend: index out of range or empty row set")
     return out
@@ -372,4 +384,20 @@ def qproj(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     assert w.shape == (O, d_in)
     out = np.empty((B, O), np.float64)
     _load().oracle_qproj(_ptr(x), _ptr(w), _ptr(out), B, d_in, O)
+    return out
+
+
+def compress(x: np.ndarray, wg: np.ndarray) -> np.ndarray:
+    """Compressor: each group of 4 consecutive raw rows becomes one row,
+    weighted by the softmax of the rows' gate scores wg . x_i. x uint16
+    (bf16) [B, 4G, D], wg float32 [D] -> float64 [B, G, D]."""
+    x = _c(x, np.uint16)
+    wg = _c(wg, np.float32)
+    B, R, D = x.shape
+    if R % 4 != 0:
+        raise ValueError("the raw rows must come in groups of 4")
+    assert wg.shape == (D,)
+    G = R // 4
+    out = np.empty((B, G, D), np.float64)
+    _load().oracle_compress(_ptr(x), _ptr(wg), _ptr(out), B, G, D)
     return out

@@ -11,7 +11,7 @@
  *  [CSA]  "feat: Add DeepSeek-V4 CSA attention kernels" (aws-neuron
  *         nki-library pull request 13), section "How the algorithm works",
  *         the step table (steps 2, 3, 4), and the paragraph after the GpSimd
- *         bullet list (K and V are the same embedding).
+ *         bullet list (keys and values are one tensor).
  *  [DS]   "DeepSelect" project page (deepseek-ai/DeepSelect), the algorithm
  *         and scenario paragraphs (top-k by score, sorted_index and
  *         return_value options).
@@ -34,6 +34,12 @@
  *    rows share one row of keys (indexer keys and compressed KV); each has
  *    its own queries, weights, window, length and selection, and is in
  *    every other respect an independent decode row.
+ *  - attention sink: one logit per query head, in the units of the scaled
+ *    q.k logits, that takes part in the softmax normalisation like a row
+ *    whose value vector is zero (so it adds to the denominator only).
+ *  - compressor: each group of 4 consecutive raw KV rows becomes one
+ *    compressed row, the softmax (over the 4 rows) of a linear gate score
+ *    of each row weighting the rows' sum.
  *
  * Every floating-point step runs in double. bf16 inputs are decoded exactly.
  * OpenMP, when enabled, only splits independent batch rows; the result does
@@ -235,8 +241,8 @@ int oracle_topk_ragged(const void* scores, int dtype, int B, int N, const int32_
  * Returns 0, or -1 if an index is out of range.
  */
 static int attend_rows(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                       const uint16_t* win, double* out, int B, int T, int N, int k,
-                       int W, int Hq, int D, double scale) {
+                       const uint16_t* win, const double* sink, double* out, int B, int T,
+                       int N, int k, int W, int Hq, int D, double scale) {
   /* query row b gathers from the compressed rows of batch row b / T */
   for (int64_t t = 0; t < (int64_t)B * T * k; ++t)
     if (idx[t] < -1 || idx[t] >= N) return -1;
@@ -266,14 +272,16 @@ static int attend_rows(const uint16_t* q, const uint16_t* kv, const int32_t* idx
           for (int d = 0; d < D; ++d) o[d] = 0.0;
           continue;
         }
-        double m = -INFINITY;
+        /* The sink (when given) competes for the maximum and adds exp(sink - m)
+         * to the denominator; it brings no value vector. */
+        double m = sink ? sink[h] : -INFINITY;
         for (int r = 0; r < nr; ++r) {
           double dot = 0.0;
           for (int d = 0; d < D; ++d) dot += qd[d] * rows[(int64_t)r * D + d];
           z[r] = scale * dot;
           if (z[r] > m) m = z[r];
         }
-        double l = 0.0;
+        double l = sink ? exp(sink[h] - m) : 0.0;
         for (int r = 0; r < nr; ++r) {
           z[r] = exp(z[r] - m);
           l += z[r];
@@ -295,7 +303,24 @@ static int attend_rows(const uint16_t* q, const uint16_t* kv, const int32_t* idx
 int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                   const uint16_t* win, double* out, int B, int N, int k, int W,
                   int Hq, int D, double scale) {
-  return attend_rows(q, kv, idx, win, out, B, 1, N, k, W, Hq, D, scale);
+  return attend_rows(q, kv, idx, win, NULL, out, B, 1, N, k, W, Hq, D, scale);
+}
+
+/*
+ * Attention with a sink [CSA, "DMA Traffic Shaping", priority table, where
+ * the attention sink is one of the transfers of the attention kernel; the
+ * pages give no formula, so this is a reading]: sink[h] (double [Hq], finite
+ * or -inf) is a logit of head h, in the units of z, that joins the softmax
+ * normalisation and brings no value vector:
+ *   m = max(sink[h], max_r z[h,r])
+ *   out[b,h,:] = sum_r exp(z[h,r] - m) R_b[r,:] / (exp(sink[h] - m) + sum_r exp(z[h,r] - m))
+ * sink[h] = -inf gives plain attention. A batch row with no rows at all
+ * still gets a zero output.
+ */
+int oracle_attend_sink(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
+                       const uint16_t* win, const double* sink, double* out, int B, int N,
+                       int k, int W, int Hq, int D, double scale) {
+  return attend_rows(q, kv, idx, win, sink, out, B, 1, N, k, W, Hq, D, scale);
 }
 
 /* T query tokens per batch row: q [B*T,Hq,D], idx [B*T,k], win [B*T,W,D],
@@ -303,7 +328,7 @@ int oracle_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
 int oracle_attend_mt(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                      const uint16_t* win, double* out, int B, int T, int N, int k,
                      int W, int Hq, int D, double scale) {
-  return attend_rows(q, kv, idx, win, out, B, T, N, k, W, Hq, D, scale);
+  return attend_rows(q, kv, idx, win, NULL, out, B, T, N, k, W, Hq, D, scale);
 }
 
 /*
@@ -366,6 +391,44 @@ void oracle_qproj(const uint16_t* x, const uint16_t* w, double* out, int B, int 
       double acc = 0.0;
       for (int i = 0; i < d_in; ++i) acc += bf16_value(xrow[i]) * bf16_value(wrow[i]);
       out[(int64_t)b * O + o] = acc;
+    }
+  }
+}
+
+/*
+ * Compressor [CSA, "How the algorithm works", step table, step 1: every 4
+ * raw tokens are folded into one compressed entry by a gated weighted sum].
+ * The pages give no formula; reading: each raw KV row x_i (i < 4 of one
+ * group) gets a gate score z_i = sum_d wg[d] * x_i[d] (one learned gate
+ * vector wg), the weights are the softmax of the 4 scores, and the
+ * compressed row is the weighted sum:
+ *   a_i = exp(z_i - max_j z_j) / sum_j exp(z_j - max_j z_j)
+ *   out[b, g, d] = sum_i a_i * x[b, 4g + i, d]
+ * x bf16 [B, 4G, D] (raw rows, group g = rows 4g .. 4g+3), wg float [D], out
+ * double [B, G, D]. Every step runs in double.
+ */
+void oracle_compress(const uint16_t* x, const float* wg, double* out, int B, int G, int D) {
+#pragma omp parallel for schedule(static)
+  for (int bg = 0; bg < B * G; ++bg) {
+    const uint16_t* rows = x + (int64_t)bg * 4 * D;  /* group bg's 4 rows are consecutive */
+    double z[4], a[4];
+    double zmax = -INFINITY;
+    for (int i = 0; i < 4; ++i) {
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d) dot += (double)wg[d] * bf16_value(rows[(int64_t)i * D + d]);
+      z[i] = dot;
+      if (dot > zmax) zmax = dot;
+    }
+    double l = 0.0;
+    for (int i = 0; i < 4; ++i) {
+      a[i] = exp(z[i] - zmax);
+      l += a[i];
+    }
+    double* o = out + (int64_t)bg * D;
+    for (int d = 0; d < D; ++d) {
+      double acc = 0.0;
+      for (int i = 0; i < 4; ++i) acc += (a[i] / l) * bf16_value(rows[(int64_t)i * D + d]);
+      o[d] = acc;
     }
   }
 }

@@ -61,6 +61,18 @@ MUTANTS = [
      "r < k ? kv + ((int64_t)(b / T) * N + idx[(int64_t)b * k + r]) * D",
      "r < k ? kv + ((int64_t)(b % B) * N + idx[(int64_t)b * k + r]) * D",
      [pins.test_attend_mt_equals_sdpa_per_token]),
+    ("attention: the sink left out of the denominator",
+     "double l = sink ? exp(sink[h] - m) : 0.0;",
+     "double l = 0.0;",
+     [pins.test_attend_sink_equals_sdpa_with_a_zero_value_row, pins.test_attend_sink_closed_forms]),
+    ("compressor: weights not normalised",
+     "acc += (a[i] / l) * bf16_value(rows[(int64_t)i * D + d]);",
+     "acc += a[i] * bf16_value(rows[(int64_t)i * D + d]);",
+     [pins.test_compress_closed_forms, pins.test_compress_equals_torch_softmax_gate]),
+    ("compressor: every gate score taken from the group's first row",
+     "dot += (double)wg[d] * bf16_value(rows[(int64_t)i * D + d]);",
+     "dot += (double)wg[d] * bf16_value(rows[d]);",
+     [pins.test_compress_equals_torch_softmax_gate, pins.test_compress_closed_forms]),
     ("query projection: weight read transposed",
      "acc += bf16_value(xrow[i]) * bf16_value(wrow[i]);",
      "acc += bf16_value(xrow[i]) * bf16_value(w[(int64_t)i * O + o]);",

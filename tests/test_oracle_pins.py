@@ -538,3 +538,148 @@ def test_qproj_one_hot_and_scaling_are_exact():
     a = oracle.qproj(bf16_bits(xs), bf16_bits(w))
     b2 = oracle.qproj(bf16_bits((xs.float() * 2).to(torch.bfloat16)), bf16_bits(w))
     assert np.array_equal(b2, 2 * a)  # exact: powers of two scale every product exactly
+
+
+# ---------------------------------------------------------------- attention sink
+
+def _sink_inputs(seed, B=2, N=60, k=12, W=5, Hq=16, D=128):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(B, N, D, generator=g).to(torch.bfloat16)
+    win = torch.randn(B, W, D, generator=g).to(torch.bfloat16)
+    idx = torch.stack([torch.randperm(N, generator=g)[:k] for _ in range(B)]).int()
+    return q, kv, win, idx
+
+
+def test_attend_sink_of_minus_infinity_is_plain_attention():
+    q, kv, win, idx = _sink_inputs(41)
+    Hq = q.shape[1]
+    a = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), 0.09)
+    b = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), 0.09,
+                      sink=np.full(Hq, -np.inf))
+    assert np.array_equal(a, b)
+
+
+def test_attend_sink_equals_sdpa_with_a_zero_value_row():
+    """A sink is a row whose value vector is zero and whose logit is the sink:
+    torch's scaled_dot_product_attention over the gathered rows plus one zero
+    key/value row, with the sink added to that row's logit as a float mask,
+    per head."""
+    q, kv, win, idx = _sink_inputs(42)
+    B, Hq, D = q.shape
+    sink = np.linspace(-3.0, 4.0, Hq)
+    scale = 0.08
+    got = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), scale,
+                        sink=sink)
+    rows = torch.cat([torch.stack([kv[b, idx[b].long()] for b in range(B)]), win], dim=1).double()
+    rows = torch.cat([rows, torch.zeros(B, 1, D, dtype=torch.float64)], dim=1)   # zero row
+    R = rows.shape[1]
+    mask = torch.zeros(B, Hq, 1, R, dtype=torch.float64)
+    mask[:, :, 0, R - 1] = torch.from_numpy(sink)
+    kk = rows.unsqueeze(1).expand(B, Hq, R, D)
+    ref = torch.nn.functional.scaled_dot_product_attention(q.double().unsqueeze(2), kk, kk,
+                                                           attn_mask=mask, scale=scale)
+    assert np.max(np.abs(got - ref[:, :, 0, :].numpy())) < 1e-12
+    # the sink changes the result (it is not ignored)
+    plain = oracle.attend(bf16_bits(q), bf16_bits(kv), idx.numpy(), bf16_bits(win), scale)
+    assert np.max(np.abs(got - plain)) > 1e-3
+
+
+def test_attend_sink_closed_forms():
+    g = torch.Generator().manual_seed(43)
+    Hq, D = 16, 128
+    q = torch.randn(1, Hq, D, generator=g).to(torch.bfloat16)
+    kv = torch.randn(1, 8, D, generator=g).to(torch.bfloat16)
+    kvd = kv.double().numpy()[0]
+    qd = q.double().numpy()[0]
+    sink = np.linspace(-2.0, 2.0, Hq)
+    scale = 0.1
+    # one row: out = sigma(z - sink) * row
+    out = oracle.attend(bf16_bits(q), bf16_bits(kv), np.array([[3]], np.int32), None, scale,
+                        sink=sink)[0]
+    for h in range(Hq):
+        z = scale * float(np.dot(qd[h], kvd[3]))
+        a, _ = brute.softmax_weights_two_rows(z, sink[h])
+        assert np.max(np.abs(out[h] - a * kvd[3])) < 1e-13
+    # a batch row with no rows at all still outputs zeros
+    out = oracle.attend(bf16_bits(q), bf16_bits(kv), np.array([[-1, -1]], np.int32), None,
+                        scale, sink=sink)
+    assert np.array_equal(out, np.zeros_like(out))
+
+
+# ---------------------------------------------------------------- compressor
+
+def _compress_ref(x_bits: np.ndarray, wg: np.ndarray) -> np.ndarray:
+    """The compressor written with torch in fp64: gate scores, softmax over
+    each group's 4 rows, weighted sum."""
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).double()
+    B, R, D = x.shape
+    xg = x.view(B, R // 4, 4, D)
+    z = torch.matmul(xg, torch.from_numpy(wg.astype(np.float64)))          # [B, G, 4]
+    a = torch.softmax(z, dim=-1)
+    return (a.unsqueeze(-1) * xg).sum(2).numpy()
+
+
+def test_compress_equals_torch_softmax_gate():
+    g = torch.Generator().manual_seed(51)
+    B, G, D = 3, 5, 128
+    x = torch.randn(B, 4 * G, D, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(D, generator=g) / math.sqrt(D)).float().numpy()
+    got = oracle.compress(bf16_bits(x), wg)
+    ref = _compress_ref(bf16_bits(x), wg)
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # the weights differ from uniform: the result is not the plain mean
+    mean = x.double().view(B, G, 4, D).mean(2).numpy()
+    assert np.max(np.abs(got - mean)) > 1e-2
+
+
+def test_compress_closed_forms():
+    g = torch.Generator().manual_seed(52)
+    B, G, D = 2, 3, 64
+    x = torch.randn(B, 4 * G, D, generator=g).to(torch.bfloat16)
+    xd = x.double().view(B, G, 4, D).numpy()
+    # zero gate: equal weights, the mean of each group's rows
+    got = oracle.compress(bf16_bits(x), np.zeros(D, np.float32))
+    assert np.max(np.abs(got - xd.mean(2))) < 1e-15
+    # a gate that only row 1 of every group passes strongly: that row exactly
+    y = x.clone().view(B, G, 4, D)
+    y[:, :, :, 0] = 0.0
+    y[:, :, 1, 0] = 1000.0                       # exact in bf16
+    wg = np.zeros(D, np.float32)
+    wg[0] = 1.0
+    got = oracle.compress(bf16_bits(y.view(B, 4 * G, D)), wg)
+    assert np.array_equal(got, y.double()[:, :, 1, :].numpy())
+    # two rows left in the race: logistic weights of their gate gap
+    y = x.clone().view(B, G, 4, D)
+    y[:, :, 2:, 0] = -1000.0                     # rows 2 and 3 get weight exp(-1000 - ...) = 0
+    y[:, :, :2, 0] = torch.tensor([0.5, -0.25], dtype=torch.bfloat16)
+    wg = np.zeros(D, np.float32)
+    wg[0] = 1.0
+    got = oracle.compress(bf16_bits(y.view(B, 4 * G, D)), wg)
+    yd = y.double().numpy()
+    a, b = brute.softmax_weights_two_rows(0.5, -0.25)
+    ref = a * yd[:, :, 0, :] + b * yd[:, :, 1, :]
+    assert np.max(np.abs(got - ref)) < 1e-15
+
+
+def test_compress_row_order_and_group_locality():
+    g = torch.Generator().manual_seed(53)
+    B, G, D = 2, 4, 128
+    x = torch.randn(B, 4 * G, D, generator=g).to(torch.bfloat16)
+    wg = torch.randn(D, generator=g).float().numpy() / 8
+    base = oracle.compress(bf16_bits(x), wg)
+    # the rows of a group may come in any order
+    perm = torch.tensor([2, 0, 3, 1])
+    xp = x.view(B, G, 4, D)[:, :, perm, :].reshape(B, 4 * G, D)
+    assert np.max(np.abs(oracle.compress(bf16_bits(xp), wg) - base)) < 1e-14
+    # changing group 2 leaves the other groups alone
+    y = x.clone()
+    y[:, 8:12] = torch.randn(B, 4, D, generator=g).to(torch.bfloat16)
+    got = oracle.compress(bf16_bits(y), wg)
+    assert np.array_equal(got[:, [0, 1, 3]], base[:, [0, 1, 3]])
+    assert np.max(np.abs(got[:, 2] - base[:, 2])) > 1e-3
+
+
+def test_compress_rejects_an_incomplete_group():
+    with pytest.raises(ValueError):
+        oracle.compress(np.zeros((1, 6, 16), np.uint16), np.zeros(16, np.float32))

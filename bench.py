@@ -67,7 +67,7 @@ def parse():
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
                    choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step",
-                            "ragged-step", "mtp-step", "qproj", "context-sweep"])
+                            "ragged-step", "mtp-step", "qproj", "context-sweep", "compress"])
     return p.parse_args()
 
 
@@ -327,6 +327,36 @@ def other_workload(args):
                      "compulsory_bytes": nbytes, "rotating_input_copies": R,
                      "config": {"B": B, "d_in": d_in, "H_I": H, "D_I": 128,
                                 "weights": "synthetic, N(0, 1/d_in)"}})
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "compress":
+        # The compressor on the production KV width (D = 512): a decode step's
+        # fold of 4 raw rows per batch row (G = 1), and a 4096-token prompt
+        # chunk per batch row (G = 1024).
+        import math
+        B, D = 16, 512
+        results = []
+        for G in (1, 1024):
+            nbytes = B * 4 * G * D * 2 + D * 4 + B * G * D * 2
+            R = max(1, min(256, -(-(1 << 30) // nbytes)))
+            gen = torch.Generator(device=dev).manual_seed(8500 + G)
+            xs = [torch.randn(B, 4 * G, D, generator=gen, device=dev).to(torch.bfloat16)
+                  for _ in range(R)]
+            wg = (torch.randn(D, generator=gen, device=dev) / math.sqrt(D)).float()
+            outc = torch.empty((B, G, D), dtype=torch.bfloat16, device=dev)
+
+            def call(i, xs=xs, wg=wg, outc=outc):
+                dsa.dsa_compress(xs[i % R], wg, out=outc, stream=stream)
+            us = time_calls(call, args.warmup, args.steps, stream)
+            gbps = nbytes / (us * 1e-6) / 1e9
+            results.append({"groups_per_row": G, "us": round(us, 2),
+                            "effective_GBps": round(gbps, 1),
+                            "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                            "compulsory_bytes": nbytes, "rotating_input_copies": R})
+            del xs
+        line.update({"value": results[-1]["effective_GBps"], "results": results,
+                     "config": {"B": B, "D": D, "groups": [1, 1024],
+                                "gate": "synthetic, N(0, 1/D)"}})
         print(json.dumps(line), flush=True)
         return
     if args.workload == "mtp-step":

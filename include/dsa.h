@@ -227,6 +227,45 @@ DSA_EXPORT dsa_status_t dsa_decode_step_mt(const void* q_idx, const void* k_idx,
                                 size_t ws_bytes, void* stream);
 
 /*
+ * Attention sink (CSA pull request, "DMA Traffic Shaping", priority table:
+ * the attention sink is one of the attention kernel's inputs; the pages give
+ * no formula). Reading: sink float [H_q] holds one logit per query head, in
+ * the units of scale * q.k, that takes part in the softmax normalisation
+ * and brings no value vector:
+ *   M = max(sink[h], max_r z[h,r]),  z[h,r] = scale * q[b,h] . R_b[r]
+ *   out[b,h] = sum_r e^(z[h,r] - M) R_b[r] / (e^(sink[h] - M) + sum_r e^(z[h,r] - M))
+ * A sink of -inf gives dsa_sparse_attend's result; a batch row with no rows
+ * at all still gets zeros. sink must be non-NULL, 4-byte aligned, finite or
+ * -inf. Everything else, workspaces included, as dsa_sparse_attend and
+ * dsa_decode_step.
+ */
+DSA_EXPORT dsa_status_t dsa_sparse_attend_sink(const void* q, const void* kv_cmp,
+                                    const int32_t* idx, const void* kv_win, const float* sink,
+                                    void* out, const dsa_dims_t* dims, void* ws,
+                                    size_t ws_bytes, void* stream);
+DSA_EXPORT dsa_status_t dsa_decode_step_sink(const void* q_idx, const void* k_idx,
+                                  const float* w, const void* q, const void* kv_cmp,
+                                  const void* kv_win, const float* sink, void* out,
+                                  int32_t* out_idx, const dsa_dims_t* dims, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/*
+ * Compressor (CSA pull request, "How the algorithm works", step table, step
+ * 1: every 4 raw tokens are folded into one compressed entry by a gated
+ * weighted sum; the pages give no formula). Reading: the 4 raw KV rows x_i
+ * of a group each get a gate score z_i = sum_d w_gate[d] * x_i[d], and
+ *   out[b, g, :] = sum_i softmax(z)_i * x[b, 4g + i, :]
+ * x bf16 [B, 4G, D] (group g of batch row b = its raw rows 4g .. 4g+3);
+ * w_gate float [D] (the learned gate vector); out bf16 [B, G, D], rounded to
+ * nearest even (row g of out is the compressed row the caller appends to
+ * kv_cmp). Sums and the softmax run in float32 in a fixed order. D must be a
+ * multiple of 8 and at most 1024. No workspace. A decode step calls it with
+ * G = 1 every 4 tokens; a prompt with G = its length / 4.
+ */
+DSA_EXPORT dsa_status_t dsa_compress(const void* x, const float* w_gate, void* out, int B, int G,
+                          int D, void* stream);
+
+/*
  * For callers that cannot allocate device memory: code being captured into a
  * HIP graph, tight serving loops, or harnesses that forbid hipMalloc. The
  * same step as dsa_decode_step (same kernels, same results bit for bit), but

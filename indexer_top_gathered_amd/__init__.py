@@ -11,7 +11,9 @@ from .binding import (  # noqa: F401
     dsa_decode_step_mt,
     dsa_decode_step_mt_workspace_bytes,
     NOALLOC_SCRATCH_BYTES,
+    dsa_compress,
     dsa_decode_step_noalloc,
+    dsa_decode_step_sink,
     dsa_decode_step_ragged,
     dsa_decode_step_workspace_bytes,
     dsa_indexer_qproj,
@@ -19,6 +21,7 @@ from .binding import (  # noqa: F401
     dsa_indexer_score_mt,
     dsa_sparse_attend,
     dsa_sparse_attend_mt,
+    dsa_sparse_attend_sink,
     dsa_sparse_attend_workspace_bytes,
     dsa_topk,
     dsa_topk_ragged,

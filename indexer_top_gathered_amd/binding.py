@@ -38,6 +38,9 @@ EXPORTED = (
     "dsa_decode_step_mt",
     "dsa_indexer_qproj",
     "dsa_decode_step_noalloc",
+    "dsa_sparse_attend_sink",
+    "dsa_decode_step_sink",
+    "dsa_compress",
     "dsa_status_string",
 )
 
@@ -108,6 +111,12 @@ def _load() -> ctypes.CDLL:
     lib.dsa_indexer_qproj.restype = I
     lib.dsa_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, D, P]
     lib.dsa_decode_step_noalloc.restype = I
+    lib.dsa_sparse_attend_sink.argtypes = [P, P, P, P, P, P, D, P, S, P]
+    lib.dsa_sparse_attend_sink.restype = I
+    lib.dsa_decode_step_sink.argtypes = [P, P, P, P, P, P, P, P, P, D, P, S, P]
+    lib.dsa_decode_step_sink.restype = I
+    lib.dsa_compress.argtypes = [P, P, P, I, I, I, P]
+    lib.dsa_compress.restype = I
     lib.dsa_status_string.argtypes = [I]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -297,6 +306,19 @@ def dsa_sparse_attend_workspace_bytes(dims: DsaDims) -> int:
 @_on_stream
 def dsa_sparse_attend(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, stream=None):
     """bf16 [B,H_q,D] = softmax(scale * q R^T) R over R = kv_cmp[idx] ++ kv_win."""
+    return _attend(q, kv_cmp, idx, kv_win, None, scale, out, ws, stream)
+
+
+@_on_stream
+def dsa_sparse_attend_sink(q, kv_cmp, idx, kv_win, sink, scale: float, out=None, ws=None,
+                           stream=None):
+    """dsa_sparse_attend with an attention sink: sink float32 [H_q], one
+    logit per query head that joins the softmax normalisation with no value
+    vector (-inf: no effect)."""
+    return _attend(q, kv_cmp, idx, kv_win, sink, scale, out, ws, stream)
+
+
+def _attend(q, kv_cmp, idx, kv_win, sink, scale, out, ws, stream):
     B, Hq, D = q.shape
     N = kv_cmp.shape[1]
     k = idx.shape[1]
@@ -311,9 +333,16 @@ def dsa_sparse_attend(q, kv_cmp, idx, kv_win, scale: float, out=None, ws=None, s
     _need(out, "out", torch.bfloat16, (B, Hq, D))
     dims = make_dims(B, N, 1, 128, k, W, Hq, D, scale)
     ws = _workspace(LIB.dsa_sparse_attend_workspace_bytes(ctypes.byref(dims)), q.device, ws)
-    _check(LIB.dsa_sparse_attend(_ptr(q), _ptr(kv_cmp), _ptr(idx), _ptr(kv_win if W else None),
-                                 _ptr(out), ctypes.byref(dims), _ptr(ws), ws.numel(),
-                                 _stream(stream)), "dsa_sparse_attend")
+    if sink is None:
+        _check(LIB.dsa_sparse_attend(_ptr(q), _ptr(kv_cmp), _ptr(idx),
+                                     _ptr(kv_win if W else None), _ptr(out), ctypes.byref(dims),
+                                     _ptr(ws), ws.numel(), _stream(stream)), "dsa_sparse_attend")
+    else:
+        _need(sink, "sink", torch.float32, (Hq,))
+        _check(LIB.dsa_sparse_attend_sink(_ptr(q), _ptr(kv_cmp), _ptr(idx),
+                                          _ptr(kv_win if W else None), _ptr(sink), _ptr(out),
+                                          ctypes.byref(dims), _ptr(ws), ws.numel(),
+                                          _stream(stream)), "dsa_sparse_attend_sink")
     return out
 
 
@@ -357,6 +386,14 @@ def dsa_decode_step(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: float, ou
 
 
 @_on_stream
+def dsa_decode_step_sink(q_idx, k_idx, w, q, kv_cmp, kv_win, sink, k: int, scale: float,
+                         out=None, out_idx=None, ws=None, stream=None, return_idx: bool = False):
+    """dsa_decode_step whose attention has a sink (float32 [H_q] logits)."""
+    return _step(q_idx, k_idx, w, q, kv_cmp, kv_win, None, k, scale, out, out_idx, ws, stream,
+                 return_idx, sink=sink)
+
+
+@_on_stream
 def dsa_decode_step_ragged(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k: int, scale: float,
                            out=None, out_idx=None, ws=None, stream=None,
                            return_idx: bool = False):
@@ -366,7 +403,7 @@ def dsa_decode_step_ragged(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k: int, 
 
 
 def _step(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k, scale, out, out_idx, ws, stream,
-          return_idx):
+          return_idx, sink=None):
     B, H, DI = q_idx.shape
     N = k_idx.shape[1]
     Hq, D = q.shape[1], q.shape[2]
@@ -387,7 +424,13 @@ def _step(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, k, scale, out, out_idx, w
         _need(out_idx, "out_idx", torch.int32, (B, k))
     dims = make_dims(B, N, H, DI, k, W, Hq, D, scale)
     ws = _workspace(LIB.dsa_decode_step_workspace_bytes(ctypes.byref(dims)), q.device, ws)
-    if lengths is None:
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (Hq,))
+        _check(LIB.dsa_decode_step_sink(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
+                                        _ptr(kv_win if W else None), _ptr(sink), _ptr(out),
+                                        _ptr(out_idx), ctypes.byref(dims), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "dsa_decode_step_sink")
+    elif lengths is None:
         _check(LIB.dsa_decode_step(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q), _ptr(kv_cmp),
                                    _ptr(kv_win if W else None), _ptr(out), _ptr(out_idx),
                                    ctypes.byref(dims), _ptr(ws), ws.numel(), _stream(stream)),
@@ -469,3 +512,22 @@ def dsa_decode_step_noalloc(q_idx, k_idx, w, q, kv_cmp, kv_win, k: int, scale: f
                                        ctypes.byref(dims), _stream(stream)),
            "dsa_decode_step_noalloc")
     return (out, out_idx) if out_idx is not None else out
+
+
+@_on_stream
+def dsa_compress(x, w_gate, out=None, stream=None):
+    """Compressor: x bf16 [B, 4G, D] (raw KV rows, 4 per group), w_gate
+    float32 [D] -> bf16 [B, G, D], each group's rows weighted by the softmax
+    of their gate scores w_gate . x_i."""
+    B, R, D = x.shape
+    _need(x, "x", torch.bfloat16)
+    if R % 4 != 0:
+        raise ValueError("x must hold whole groups of 4 raw rows")
+    G = R // 4
+    _need(w_gate, "w_gate", torch.float32, (D,))
+    if out is None:
+        out = torch.empty((B, G, D), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (B, G, D))
+    _check(LIB.dsa_compress(_ptr(x), _ptr(w_gate), _ptr(out), B, G, D, _stream(stream)),
+           "dsa_compress")
+    return out

@@ -18,7 +18,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["topk.hip", "sparse_attend.hip", "indexer_score.hip", "dsa_api.hip", "qproj.hip"]
+SOURCES = ["topk.hip", "sparse_attend.hip", "indexer_score.hip", "dsa_api.hip", "qproj.hip",
+           "compress.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -231,15 +231,14 @@ size_t dsa_sparse_attend_mt_workspace_bytes(const dsa_dims_t* dims, int T) {
   return b ? b : 256;
 }
 
-dsa_status_t dsa_sparse_attend(const void* q, const void* kv_cmp, const int32_t* idx,
-                               const void* kv_win, void* out, const dsa_dims_t* dims, void* ws,
-                               size_t ws_bytes, void* stream) {
-  return dsa_sparse_attend_mt(q, kv_cmp, idx, kv_win, out, dims, 1, ws, ws_bytes, stream);
-}
+}  // extern "C"
 
-dsa_status_t dsa_sparse_attend_mt(const void* q, const void* kv_cmp, const int32_t* idx,
-                                  const void* kv_win, void* out, const dsa_dims_t* dims, int T,
-                                  void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+dsa_status_t attend_impl(const void* q, const void* kv_cmp, const int32_t* idx,
+                         const void* kv_win, const float* sink, void* out,
+                         const dsa_dims_t* dims, int T, void* ws, size_t ws_bytes,
+                         void* stream) {
   if (!dims || T < 1) return DSA_ERROR_INVALID_VALUE;
   if (T > kMaxTokens) return DSA_ERROR_NOT_SUPPORTED;
   const dsa_dims_t dq = query_rows(*dims, T);
@@ -248,7 +247,8 @@ dsa_status_t dsa_sparse_attend_mt(const void* q, const void* kv_cmp, const int32
   if (!q || !kv_cmp || !idx || !out || !ws || (dims->window > 0 && !kv_win))
     return DSA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(kv_cmp) || !aligned16(out) || !aligned16(ws) ||
-      (kv_win && !aligned16(kv_win)) || (reinterpret_cast<uintptr_t>(idx) & 3u))
+      (kv_win && !aligned16(kv_win)) || (reinterpret_cast<uintptr_t>(idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u))
     return DSA_ERROR_INVALID_VALUE;
   const AttendPlan plan = plan_attend(dq);
   if (ws_bytes < (plan.bytes ? plan.bytes : 256)) return DSA_ERROR_WORKSPACE_TOO_SMALL;
@@ -256,7 +256,31 @@ dsa_status_t dsa_sparse_attend_mt(const void* q, const void* kv_cmp, const int32
   if (s != DSA_SUCCESS) return s;
   return to_status(launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp),
                                  idx, static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out),
-                                 dq, plan, T, ws, static_cast<hipStream_t>(stream)));
+                                 sink, dq, plan, T, ws, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status_t dsa_sparse_attend(const void* q, const void* kv_cmp, const int32_t* idx,
+                               const void* kv_win, void* out, const dsa_dims_t* dims, void* ws,
+                               size_t ws_bytes, void* stream) {
+  return attend_impl(q, kv_cmp, idx, kv_win, nullptr, out, dims, 1, ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_sparse_attend_sink(const void* q, const void* kv_cmp, const int32_t* idx,
+                                    const void* kv_win, const float* sink, void* out,
+                                    const dsa_dims_t* dims, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  if (!sink) return DSA_ERROR_INVALID_VALUE;
+  return attend_impl(q, kv_cmp, idx, kv_win, sink, out, dims, 1, ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_sparse_attend_mt(const void* q, const void* kv_cmp, const int32_t* idx,
+                                  const void* kv_win, void* out, const dsa_dims_t* dims, int T,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  return attend_impl(q, kv_cmp, idx, kv_win, nullptr, out, dims, T, ws, ws_bytes, stream);
 }
 
 size_t dsa_decode_step_workspace_bytes(const dsa_dims_t* dims) {
@@ -294,7 +318,7 @@ dsa_status_t check_step_pointers(const void* q_idx, const void* k_idx, const flo
 dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, const void* q,
                        const void* kv_cmp, const void* kv_win, const int32_t* lengths, void* out,
                        int32_t* out_idx, const dsa_dims_t* dims, int T, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, const float* sink = nullptr) {
   if (!dims || T < 1) return DSA_ERROR_INVALID_VALUE;
   if (T > kMaxTokens) return DSA_ERROR_NOT_SUPPORTED;
   const dsa_dims_t dq = query_rows(*dims, T);
@@ -304,7 +328,8 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
   if (s != DSA_SUCCESS) return s;
   s = check_step_pointers(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims->window);
   if (s != DSA_SUCCESS) return s;
-  if (!ws || !aligned16(ws)) return DSA_ERROR_INVALID_VALUE;
+  if (!ws || !aligned16(ws) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return DSA_ERROR_INVALID_VALUE;
   const StepLayout L = step_layout(*dims, T);
   if (ws_bytes < L.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();
@@ -322,8 +347,8 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
                   base + L.topk_off, st);
   if (e != hipSuccess) return DSA_ERROR_LAUNCH;
   e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp), sel,
-                    static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), dq, L.at, T,
-                    base + L.attend_off, st);
+                    static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), sink, dq,
+                    L.at, T, base + L.attend_off, st);
   return to_status(e);
 }
 
@@ -346,6 +371,30 @@ dsa_status_t dsa_decode_step_ragged(const void* q_idx, const void* k_idx, const 
   if (!lengths) return DSA_ERROR_INVALID_VALUE;
   return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, lengths, out, out_idx, dims, 1, ws,
                    ws_bytes, stream);
+}
+
+dsa_status_t dsa_decode_step_sink(const void* q_idx, const void* k_idx, const float* w,
+                                  const void* q, const void* kv_cmp, const void* kv_win,
+                                  const float* sink, void* out, int32_t* out_idx,
+                                  const dsa_dims_t* dims, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (!sink) return DSA_ERROR_INVALID_VALUE;
+  return step_impl(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx, dims, 1, ws,
+                   ws_bytes, stream, sink);
+}
+
+dsa_status_t dsa_compress(const void* x, const float* w_gate, void* out, int B, int G, int D,
+                          void* stream) {
+  if (!x || !w_gate || !out) return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(out)) return DSA_ERROR_INVALID_VALUE;
+  if (B < 1 || G < 1 || D < 1) return DSA_ERROR_INVALID_VALUE;
+  if (D % 8 != 0 || D > 1024) return DSA_ERROR_NOT_SUPPORTED;
+  if ((long long)B * G * 4 * D > 0x7FFFFFFFLL) return DSA_ERROR_NOT_SUPPORTED;
+  dsa_status_t s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  return to_status(launch_compress(static_cast<const uint16_t*>(x), w_gate,
+                                   static_cast<uint16_t*>(out), B * G, D,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 dsa_status_t dsa_decode_step_mt(const void* q_idx, const void* k_idx, const float* w,

@@ -221,8 +221,16 @@ struct AttendPlan {
 AttendPlan plan_attend(const dsa_dims_t& d);
 // d.batch counts query rows; tokens consecutive query rows share one row of
 // kv (kv holds d.batch / tokens rows).
+// sink: float [q_heads] (one logit per query head, joining the softmax
+// normalisation with no value vector), or NULL for none.
 hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                         const uint16_t* win, uint16_t* out, const dsa_dims_t& d,
-                         const AttendPlan& plan, int tokens, void* ws, hipStream_t st);
+                         const uint16_t* win, uint16_t* out, const float* sink,
+                         const dsa_dims_t& d, const AttendPlan& plan, int tokens, void* ws,
+                         hipStream_t st);
+
+// Compressor: out bf16 [groups, D] from x bf16 [groups, 4, D] and the gate
+// vector wg float [D]; D a multiple of 8, at most 1024.
+hipError_t launch_compress(const uint16_t* x, const float* wg, uint16_t* out, int groups, int D,
+                           hipStream_t st);
 
 }  // namespace dsa

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
     uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
-    int N, int k, int W, int Hq, float scale, int rows_per_split, int splits, int nitems,
-    int hgroups, int tokens) {
+    const float* __restrict__ sink, int N, int k, int W, int Hq, float scale,
+    int rows_per_split, int splits, int nitems, int hgroups, int tokens) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int THREADS = WAVES * kWave;
   constexpr int HW = HG * 16;           // query heads per workgroup
@@ -358,7 +358,18 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   l += lane_xor32(l);
   // Lane (m, g) holds O[h][dbase + 16*dt + 4g + i].
   if (splits == 1) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // no row at all: zeros
+    // A sink (one logit of head h, no value vector) joins the normalisation:
+    // with M = max(running max, sink), the sum becomes l 2^(mrun - M) +
+    // 2^(sink - M) and O is scaled by 2^(mrun - M). A sink of -inf changes
+    // nothing; a batch row with no rows keeps O = 0.
+    float oscale = 1.0f;
+    if (sink) {
+      const float s2 = sink[h] * kLog2e;
+      const float M = fmaxf(mrun, s2);
+      oscale = __builtin_amdgcn_exp2f(mrun - M);
+      l = l * oscale + __builtin_amdgcn_exp2f(s2 - M);
+    }
+    const float inv = l > 0.0f ? oscale / l : 0.0f;  // no row at all: zeros
     uint16_t* orow = out + ((size_t)b * Hq + h) * D + dbase;
 #pragma unroll
     for (int dt = 0; dt < DTW; ++dt) {
@@ -407,7 +418,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void attend_combine_kernel(
     const uint16_t* __restrict__ part_o, const float4* __restrict__ part_ml,
-    uint16_t* __restrict__ out, int Hq, int splits, int nitems) {
+    const float* __restrict__ sink, uint16_t* __restrict__ out, int Hq, int splits, int nitems) {
   constexpr int TPH = D / 8;      // threads per head
   constexpr int HPW = 256 / TPH;  // heads per workgroup (divides Hq, a multiple of 16)
   constexpr int SC = 8;
@@ -458,6 +469,13 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(
     }
     M = Mc;
   }
+  if (sink) {  // the sink's term of the normalisation (natural-log units, as M)
+    const float Ms = fmaxf(M, sink[h]);
+    const float r = __expf(M - Ms);
+    L = L * r + __expf(sink[h] - Ms);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= r;
+  }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // no row at all: zeros
   u32x4 o;
 #pragma unroll
@@ -470,7 +488,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 template <int D, int HG, int DSPLIT>
 hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                            const uint16_t* win, uint16_t* out, uint16_t* po, float* pml,
-                           const dsa_dims_t& d, const AttendPlan& p, int tokens, hipStream_t st) {
+                           const float* sink, const dsa_dims_t& d, const AttendPlan& p,
+                           int tokens, hipStream_t st) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int ROW_WORDS = D / 2 + 4;
   constexpr int XWORDS = DSPLIT > 1 ? 2 * WAVES * kWave * 8 : 0;
@@ -484,8 +503,8 @@ hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t*
   const int nitems = d.batch * p.splits * hgroups;
   const int grid = (nitems + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
-                     pml, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split, p.splits,
-                     nitems, hgroups, tokens);
+                     pml, sink, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split,
+                     p.splits, nitems, hgroups, tokens);
   return hipGetLastError();
 }
 
@@ -517,20 +536,21 @@ AttendPlan plan_attend(const dsa_dims_t& d) {
 }
 
 hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
-                         const uint16_t* win, uint16_t* out, const dsa_dims_t& d,
-                         const AttendPlan& p, int tokens, void* ws, hipStream_t st) {
+                         const uint16_t* win, uint16_t* out, const float* sink,
+                         const dsa_dims_t& d, const AttendPlan& p, int tokens, void* ws,
+                         hipStream_t st) {
   uint16_t* po = p.splits > 1 ? reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
   float* pml = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
   const int hgw = p.heads_per_wg / 16;  // 16-head groups per workgroup
   hipError_t e;
   if (d.head_dim == 512) {
-    if (hgw == 4) e = launch_attend_t<512, 4, 2>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
-    else if (hgw == 2) e = launch_attend_t<512, 2, 2>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
-    else e = launch_attend_t<512, 1, 2>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
+    if (hgw == 4) e = launch_attend_t<512, 4, 2>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
+    else if (hgw == 2) e = launch_attend_t<512, 2, 2>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
+    else e = launch_attend_t<512, 1, 2>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
   } else {
-    if (hgw == 4) e = launch_attend_t<128, 4, 1>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
-    else if (hgw == 2) e = launch_attend_t<128, 2, 1>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
-    else e = launch_attend_t<128, 1, 1>(q, kv, idx, win, out, po, pml, d, p, tokens, st);
+    if (hgw == 4) e = launch_attend_t<128, 4, 1>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
+    else if (hgw == 2) e = launch_attend_t<128, 2, 1>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
+    else e = launch_attend_t<128, 1, 1>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
   }
   if (e != hipSuccess || p.splits == 1) return e;
   const int Hq = d.q_heads;
@@ -539,10 +559,10 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
   const int grid = (nitems + 7) / 8 * 8;
   if (d.head_dim == 512)
     hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(grid), dim3(256), 0, st, po,
-                       reinterpret_cast<const float4*>(pml), out, Hq, p.splits, nitems);
+                       reinterpret_cast<const float4*>(pml), sink, out, Hq, p.splits, nitems);
   else
     hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(grid), dim3(256), 0, st, po,
-                       reinterpret_cast<const float4*>(pml), out, Hq, p.splits, nitems);
+                       reinterpret_cast<const float4*>(pml), sink, out, Hq, p.splits, nitems);
   return hipGetLastError();
 }
 

@@ -140,6 +140,32 @@ def test_noalloc_argument_errors(lib):
     assert "DSA_NOALLOC_SCRATCH_BYTES (64u << 20)" in open(HEADER).read()
 
 
+def test_sink_and_compress_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    ok = _dims(lib)
+    # no sink, or a misaligned one
+    assert L.dsa_sparse_attend_sink(v(P), v(P), v(P), v(P), None, v(P), ctypes.byref(ok), v(P),
+                                    1 << 30, None) == INVALID
+    assert L.dsa_sparse_attend_sink(v(P), v(P), v(P), v(P), v(P + 2), v(P), ctypes.byref(ok),
+                                    v(P), 1 << 30, None) == INVALID
+    assert L.dsa_decode_step_sink(v(P), v(P), v(P), v(P), v(P), v(P), None, v(P), None,
+                                  ctypes.byref(ok), v(P), 1 << 30, None) == INVALID
+    need = lib.dsa_decode_step_workspace_bytes(ok)
+    assert L.dsa_decode_step_sink(v(P), v(P), v(P), v(P), v(P), v(P), v(P), v(P), None,
+                                  ctypes.byref(ok), v(P), need - 1, None) == WS_SMALL
+    bad = _dims(lib, D=64)
+    assert L.dsa_sparse_attend_sink(v(P), v(P), v(P), v(P), v(P), v(P), ctypes.byref(bad), v(P),
+                                    1 << 30, None) == NOT_SUPPORTED
+    # compressor
+    assert L.dsa_compress(None, v(P), v(P), 1, 1, 512, None) == INVALID
+    assert L.dsa_compress(v(P), v(P), v(P + 8), 1, 1, 512, None) == INVALID
+    assert L.dsa_compress(v(P), v(P), v(P), 0, 1, 512, None) == INVALID
+    assert L.dsa_compress(v(P), v(P), v(P), 1, 0, 512, None) == INVALID
+    assert L.dsa_compress(v(P), v(P), v(P), 1, 1, 100, None) == NOT_SUPPORTED
+    assert L.dsa_compress(v(P), v(P), v(P), 1, 1, 2048, None) == NOT_SUPPORTED
+
+
 def test_valid_call_without_device_reports_device_error(lib):
     import torch
     if torch.cuda.is_available():
@@ -149,6 +175,7 @@ def test_valid_call_without_device_reports_device_error(lib):
     assert L.dsa_indexer_score(v(P), v(P), v(P), v(P), 1, 10, 8, 128, None) == DEVICE
     assert L.dsa_decode_step_noalloc(*([v(P)] * 7), None, ctypes.byref(_dims(lib)),
                                      None) == DEVICE
+    assert L.dsa_compress(v(P), v(P), v(P), 2, 3, 512, None) == DEVICE
 
 
 def test_ragged_and_multi_token_argument_errors(lib):

@@ -698,8 +698,8 @@ def main():
 
     scores = torch.empty((s.B, s.N), dtype=torch.float32, device=dev)
     sel = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
-    tws = torch.empty(dsa.dsa_topk_workspace_bytes(s.B, s.N, s.k, torch.float32),
-                      dtype=torch.uint8, device=dev)
+    itws = torch.empty(dsa.dsa_indexer_topk_workspace_bytes(s.B, s.N, s.H_I, s.k, False),
+                       dtype=torch.uint8, device=dev)
     aws = torch.empty(max(256, dsa.dsa_sparse_attend_workspace_bytes(dims)), dtype=torch.uint8,
                       device=dev)
 
@@ -707,27 +707,30 @@ def main():
         c = copies[i % R]
         dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"], scores=scores, stream=stream)
     is_us = time_calls(is_call, args.warmup, args.steps, stream)
-    # Score rows of every copy for the top-k and attention legs.
-    all_scores = [dsa.dsa_indexer_score(c["q_idx"], c["k_idx"], c["w"]) for c in copies]
-    all_idx = [dsa.dsa_topk(sc, s.k) for sc in all_scores]
 
-    def tk_call(i):
-        dsa.dsa_topk(all_scores[i % R], s.k, out_idx=sel, ws=tws, stream=stream)
-    tk_us = time_calls(tk_call, args.warmup, args.steps, stream)
+    def itk_call(i):
+        c = copies[i % R]
+        dsa.dsa_indexer_topk(c["q_idx"], c["k_idx"], c["w"], s.k, out_idx=sel, scores=scores,
+                             ws=itws, stream=stream)
+    itk_us = time_calls(itk_call, args.warmup, args.steps, stream)
+    # Selections of every copy for the attention leg.
+    all_idx = [dsa.dsa_indexer_topk(c["q_idx"], c["k_idx"], c["w"], s.k) for c in copies]
 
     def sa_call(i):
         c = copies[i % R]
         dsa.dsa_sparse_attend(c["q"], c["kv_cmp"], all_idx[i % R], c["kv_win"], s.scale,
                               out=out, ws=aws, stream=stream)
     sa_us = time_calls(sa_call, args.warmup, args.steps, stream)
-    del all_scores, all_idx
+    del all_idx
 
     kernels = {
         "indexer": stage("indexer", "indexer_score_kernel<4>", indexer_bytes(s), is_us,
                          flops=2 * s.B * s.N * s.H_I * s.D_I,
                          traffic=tsum("indexer_score_kernel<4>")),
-        "topk": stage("topk", "topk_segment_kernel + topk_merge_kernel (float32 rows)",
-                      topk_stage_bytes(s.B, s.N, s.k, 4), tk_us),
+        "indexer_topk": stage("indexer_topk",
+                              "indexer_score_cut_kernel<4> + topk_merge_kernel<false, 8, true>",
+                              indexer_bytes(s) + s.B * s.k * 4, itk_us,
+                              flops=2 * s.B * s.N * s.H_I * s.D_I),
         "attention": stage("attention", "sparse_attend_kernel<512, 4, 2> + attend_combine_kernel<512>",
                            attend_bytes(s), sa_us, flops=attend_flops(s)),
     }
@@ -760,7 +763,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline,
     }
-    del scores, sel, tws, aws
+    del scores, sel, itws, aws
 
     line["graph"] = graph_replay_us(s, copies, out, ws, args.steps)
     if args.latency_calls > 0:

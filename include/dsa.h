@@ -124,6 +124,40 @@ DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, i
                       size_t ws_bytes, void* stream);
 
 /*
+ * Indexer scores and top-k in one pass (CSA pull request, "Highlights":
+ * indexer and top-k fused in one launch; "The top-k on the GPSIMD engine":
+ * the scores are selected chunk by chunk as they are computed, and a final
+ * top-k merges the chunks' results). The result is exactly
+ * dsa_topk(dsa_indexer_score(...), k) as a set: the k positions with the
+ * largest float32 score (the indexer's arithmetic, bit for bit), ties to the
+ * lower index. Each row is scored in C interleaved chunks (every C-th group
+ * of 32 positions); each chunk keeps its exact top few and the smallest
+ * score it kept, and a merge selects the row's k-th kept candidate T*. When
+ * no chunk dropped a candidate at or above T*, the merge's answer is exact;
+ * a row where some chunk did (only rows that pile their top scores into few
+ * chunks) is selected again, exactly, from its score row.
+ *   q_idx bf16 [B, H_I, D_I]; k_idx bf16 [B, N, D_I]; w float [B, H_I] (as
+ *   dsa_indexer_score); out_idx int32 [B, k] (output, in an unspecified but
+ *   deterministic order); scores float [B, N] (output, as
+ *   dsa_indexer_score writes them) or NULL to keep them in the workspace.
+ * Requires the shapes of dsa_indexer_score and 1 <= k <= min(N, 4096).
+ * ws: dsa_indexer_topk_workspace_bytes(B, N, H_I, k, scores == NULL) bytes;
+ * its contents on entry do not matter. Shapes whose chunks would not fit
+ * (dsa_indexer_topk_chunks returns 0) run the indexer and dsa_topk's
+ * kernels instead, with the same result.
+ */
+DSA_EXPORT size_t dsa_indexer_topk_workspace_bytes(int B, int N, int H_I, int k,
+                                                   int own_scores);
+DSA_EXPORT dsa_status_t dsa_indexer_topk(const void* q_idx, const void* k_idx, const float* w,
+                                         int B, int N, int H_I, int D_I, int k,
+                                         int32_t* out_idx, float* scores, void* ws,
+                                         size_t ws_bytes, void* stream);
+/* The number C of interleaved chunks dsa_indexer_topk splits each row into
+ * (row position j belongs to chunk (j / 32) mod C), or 0 when the shape
+ * takes the unfused kernels or is invalid. */
+DSA_EXPORT int dsa_indexer_topk_chunks(int B, int N, int k);
+
+/*
  * Sparse multi-query attention (CSA pull request, step 4, and "The top-k on
  * the GPSIMD engine"): every query head of a batch row attends over the
  * compressed rows the top-k picked followed by the window of recent raw
@@ -148,10 +182,11 @@ DSA_EXPORT dsa_status_t dsa_sparse_attend(const void* q, const void* kv_cmp, con
  * The whole decode step: indexer scores -> top-k -> sparse attention, all on
  * `stream` with no host synchronisation; the score rows and the selected
  * indices stay in the workspace (as in the CSA pull request's Summary, where
- * neither returns to the host). Arguments as in the three calls above.
- * out_idx int32 [B, k] or NULL: when given, receives the selected positions
- * in the order dsa_topk gives with sorted_index == 0. Workspace:
- * dsa_decode_step_workspace_bytes(dims).
+ * neither returns to the host). Indexer and top-k run as dsa_indexer_topk.
+ * Arguments as in the calls above. out_idx int32 [B, k] or NULL: when
+ * given, receives the selected positions in the order dsa_indexer_topk
+ * gives them. Workspace: dsa_decode_step_workspace_bytes(dims) (enough for
+ * the ragged and several-token calls on the same dims too).
  */
 DSA_EXPORT size_t dsa_decode_step_workspace_bytes(const dsa_dims_t* dims);
 DSA_EXPORT dsa_status_t dsa_decode_step(const void* q_idx, const void* k_idx, const float* w,

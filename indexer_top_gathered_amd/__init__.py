@@ -19,6 +19,9 @@ from .binding import (  # noqa: F401
     dsa_indexer_qproj,
     dsa_indexer_score,
     dsa_indexer_score_mt,
+    dsa_indexer_topk,
+    dsa_indexer_topk_chunks,
+    dsa_indexer_topk_workspace_bytes,
     dsa_sparse_attend,
     dsa_sparse_attend_mt,
     dsa_sparse_attend_sink,

@@ -41,6 +41,9 @@ EXPORTED = (
     "dsa_sparse_attend_sink",
     "dsa_decode_step_sink",
     "dsa_compress",
+    "dsa_indexer_topk_workspace_bytes",
+    "dsa_indexer_topk",
+    "dsa_indexer_topk_chunks",
     "dsa_status_string",
 )
 
@@ -117,6 +120,12 @@ def _load() -> ctypes.CDLL:
     lib.dsa_decode_step_sink.restype = I
     lib.dsa_compress.argtypes = [P, P, P, I, I, I, P]
     lib.dsa_compress.restype = I
+    lib.dsa_indexer_topk_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.dsa_indexer_topk_workspace_bytes.restype = S
+    lib.dsa_indexer_topk.argtypes = [P, P, P, I, I, I, I, I, P, P, P, S, P]
+    lib.dsa_indexer_topk.restype = I
+    lib.dsa_indexer_topk_chunks.argtypes = [I, I, I]
+    lib.dsa_indexer_topk_chunks.restype = I
     lib.dsa_status_string.argtypes = [I]
     lib.dsa_status_string.restype = ctypes.c_char_p
     return lib
@@ -244,6 +253,43 @@ def dsa_indexer_score_mt(q_idx, k_idx, w, scores=None, stream=None):
     _check(LIB.dsa_indexer_score_mt(_ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores), B, T, N, H,
                                     DI, _stream(stream)), "dsa_indexer_score_mt")
     return scores
+
+
+def dsa_indexer_topk_workspace_bytes(B: int, N: int, H_I: int, k: int,
+                                     own_scores: bool = True) -> int:
+    return int(LIB.dsa_indexer_topk_workspace_bytes(int(B), int(N), int(H_I), int(k),
+                                                    int(bool(own_scores))))
+
+
+def dsa_indexer_topk_chunks(B: int, N: int, k: int) -> int:
+    """Interleaved chunks per row of dsa_indexer_topk (0: unfused kernels)."""
+    return int(LIB.dsa_indexer_topk_chunks(int(B), int(N), int(k)))
+
+
+@_on_stream
+def dsa_indexer_topk(q_idx, k_idx, w, k: int, out_idx=None, scores=None, ws=None, stream=None,
+                     return_scores: bool = False):
+    """Indexer scores and their top-k in one pass: int32 [B, k], the set
+    dsa_topk(dsa_indexer_score(q_idx, k_idx, w), k) gives (order unspecified,
+    deterministic); with return_scores, also the float32 [B, N] scores."""
+    B, H, DI = q_idx.shape
+    N = k_idx.shape[1]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(k_idx, "k_idx", torch.bfloat16, (B, N, DI))
+    _need(w, "w", torch.float32, (B, H))
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q_idx.device)
+    _need(out_idx, "out_idx", torch.int32, (B, k))
+    if return_scores and scores is None:
+        scores = torch.empty((B, N), dtype=torch.float32, device=q_idx.device)
+    if scores is not None:
+        _need(scores, "scores", torch.float32, (B, N))
+    nbytes = LIB.dsa_indexer_topk_workspace_bytes(B, N, H, int(k), int(scores is None))
+    ws = _workspace(nbytes, q_idx.device, ws)
+    _check(LIB.dsa_indexer_topk(_ptr(q_idx), _ptr(k_idx), _ptr(w), B, N, H, DI, int(k),
+                                _ptr(out_idx), _ptr(scores), _ptr(ws), ws.numel(),
+                                _stream(stream)), "dsa_indexer_topk")
+    return (out_idx, scores) if scores is not None else out_idx
 
 
 # ------------------------------------------------------------------ top-k

@@ -80,25 +80,85 @@ dsa_dims_t query_rows(const dsa_dims_t& d, int T) {
   return r;
 }
 
-// Workspace layout of the fused step (T query tokens per batch row).
+// Workspace of dsa_indexer_topk: the score rows (unless the caller takes
+// them), then either the chunk cut's candidates or the two-stage top-k's.
+struct IndexerTopkLayout {
+  size_t scores_off, cand_off, cnt_off, tcut_off, topk_off, bytes;
+  CutPlan cut;
+  TopkPlan tk;
+};
+
+IndexerTopkLayout indexer_topk_layout(int B, int N, int k, bool own_scores) {
+  IndexerTopkLayout L{};
+  L.cut = plan_cut(B, N, k);
+  L.tk = plan_topk(B, N, k, DSA_F32);
+  size_t off = 0;
+  L.scores_off = off;
+  if (own_scores) off = align_up(off + (size_t)B * N * sizeof(float), 256);
+  if (L.cut.ok) {
+    const size_t rows = (size_t)B * L.cut.chunks;
+    L.cand_off = off;
+    off = align_up(off + rows * L.cut.keep * sizeof(uint64_t), 256);
+    L.cnt_off = off;
+    off = align_up(off + rows * sizeof(uint32_t), 256);
+    L.tcut_off = off;
+    off = align_up(off + rows * sizeof(uint64_t), 256);
+  } else {
+    L.topk_off = off;
+    off = align_up(off + L.tk.bytes, 256);
+  }
+  L.bytes = off ? off : 256;
+  return L;
+}
+
+// The launches of dsa_indexer_topk (arguments already checked): the
+// indexer with the chunk cut and the cut merge when the shape fits, else the
+// indexer and the two-stage top-k.
+hipError_t launch_indexer_topk(const void* q_idx, const void* k_idx, const float* w, float* scores,
+                               int B, int N, int H, int k, int32_t* out_idx,
+                               const IndexerTopkLayout& L, char* base, hipStream_t st) {
+  hipError_t e;
+  if (L.cut.ok) {
+    uint64_t* cand = reinterpret_cast<uint64_t*>(base + L.cand_off);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(base + L.cnt_off);
+    uint64_t* tcut = reinterpret_cast<uint64_t*>(base + L.tcut_off);
+    e = launch_indexer_cut(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                           w, scores, B, N, H, L.cut, cand, cnt, tcut, st);
+    if (e != hipSuccess) return e;
+    return launch_topk_cut_merge(scores, B, N, k, L.cut, cand, cnt, tcut, out_idx, st);
+  }
+  e = launch_indexer_score(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                           w, scores, B, N, H, 1, nullptr, st);
+  if (e != hipSuccess) return e;
+  return launch_topk(scores, DSA_F32, B, N, k, out_idx, nullptr, 0, nullptr, L.tk,
+                     base + L.topk_off, st);
+}
+
+// Workspace layout of the fused step (T query tokens per batch row). A
+// plain one-token step takes dsa_indexer_topk's launches; ragged rows and
+// several tokens take the indexer and the two-stage top-k.
 struct StepLayout {
   size_t scores_off, idx_off, topk_off, attend_off, bytes;
+  bool plain;             // no lengths, one token: dsa_indexer_topk's path
+  IndexerTopkLayout itk;  // its buffers, at topk_off (the score rows at scores_off)
   TopkPlan tk;
   AttendPlan at;
 };
 
-StepLayout step_layout(const dsa_dims_t& d, int T) {
+StepLayout step_layout(const dsa_dims_t& d, int T, bool ragged) {
   StepLayout L{};
   const dsa_dims_t dq = query_rows(d, T);
   L.tk = plan_topk(dq.batch, d.n, d.topk, DSA_F32);
   L.at = plan_attend(dq);
+  L.plain = T == 1 && !ragged;
+  if (L.plain) L.itk = indexer_topk_layout(d.batch, d.n, d.topk, false);
   size_t off = 0;
   L.scores_off = off;
   off = align_up(off + (size_t)dq.batch * d.n * sizeof(float), 256);
   L.idx_off = off;
   off = align_up(off + (size_t)dq.batch * d.topk * sizeof(int32_t), 256);
   L.topk_off = off;
-  off = align_up(off + L.tk.bytes, 256);
+  off = align_up(off + (L.plain ? L.itk.bytes : L.tk.bytes), 256);
   L.attend_off = off;
   off = align_up(off + L.at.bytes, 256);
   L.bytes = off;
@@ -173,6 +233,40 @@ dsa_status_t dsa_indexer_qproj(const void* x, const void* w_q, void* q_idx, int 
 size_t dsa_topk_workspace_bytes(int B, int N, int k, dsa_dtype_t dtype) {
   if (check_topk_shape(B, N, k, dtype) != DSA_SUCCESS) return 0;
   return plan_topk(B, N, k, dtype).bytes;
+}
+
+int dsa_indexer_topk_chunks(int B, int N, int k) {
+  if (check_topk_shape(B, N, k, DSA_F32) != DSA_SUCCESS) return 0;
+  const CutPlan p = plan_cut(B, N, k);
+  return p.ok ? p.chunks : 0;
+}
+
+size_t dsa_indexer_topk_workspace_bytes(int B, int N, int H_I, int k, int own_scores) {
+  if (check_indexer_shape(B, N, H_I, 128) != DSA_SUCCESS) return 0;
+  if (check_topk_shape(B, N, k, DSA_F32) != DSA_SUCCESS) return 0;
+  return indexer_topk_layout(B, N, k, own_scores != 0).bytes;
+}
+
+dsa_status_t dsa_indexer_topk(const void* q_idx, const void* k_idx, const float* w, int B, int N,
+                              int H_I, int D_I, int k, int32_t* out_idx, float* scores, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!q_idx || !k_idx || !w || !out_idx || !ws) return DSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(ws) ||
+      (reinterpret_cast<uintptr_t>(w) & 3u) || (reinterpret_cast<uintptr_t>(out_idx) & 3u) ||
+      (scores && !aligned16(scores)))
+    return DSA_ERROR_INVALID_VALUE;
+  dsa_status_t s = check_indexer_shape(B, N, H_I, D_I);
+  if (s != DSA_SUCCESS) return s;
+  s = check_topk_shape(B, N, k, DSA_F32);
+  if (s != DSA_SUCCESS) return s;
+  const IndexerTopkLayout L = indexer_topk_layout(B, N, k, scores == nullptr);
+  if (ws_bytes < L.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
+  s = check_device();
+  if (s != DSA_SUCCESS) return s;
+  char* base = static_cast<char*>(ws);
+  float* sc = scores ? scores : reinterpret_cast<float*>(base + L.scores_off);
+  return to_status(launch_indexer_topk(q_idx, k_idx, w, sc, B, N, H_I, k, out_idx, L, base,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -293,7 +387,10 @@ size_t dsa_decode_step_mt_workspace_bytes(const dsa_dims_t* dims, int T) {
   if (check_attend_dims(&dq) != DSA_SUCCESS) return 0;
   if (check_indexer_shape(dims->batch, dims->n, dims->idx_heads, dims->idx_dim, T) != DSA_SUCCESS)
     return 0;
-  return step_layout(*dims, T).bytes;
+  // The larger of the two layouts, so one size serves the plain, ragged and
+  // several-token calls alike.
+  const size_t a = step_layout(*dims, T, false).bytes, b = step_layout(*dims, T, true).bytes;
+  return a > b ? a : b;
 }
 
 }  // extern "C"
@@ -330,7 +427,7 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
   if (s != DSA_SUCCESS) return s;
   if (!ws || !aligned16(ws) || (reinterpret_cast<uintptr_t>(sink) & 3u))
     return DSA_ERROR_INVALID_VALUE;
-  const StepLayout L = step_layout(*dims, T);
+  const StepLayout L = step_layout(*dims, T, lengths != nullptr);
   if (ws_bytes < L.bytes) return DSA_ERROR_WORKSPACE_TOO_SMALL;
   s = check_device();
   if (s != DSA_SUCCESS) return s;
@@ -339,13 +436,20 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
   float* scores = reinterpret_cast<float*>(base + L.scores_off);
   int32_t* sel = out_idx ? out_idx : reinterpret_cast<int32_t*>(base + L.idx_off);
   const dsa_dims_t& d = *dims;
-  hipError_t e = launch_indexer_score(static_cast<const uint16_t*>(q_idx),
-                                      static_cast<const uint16_t*>(k_idx), w, scores, d.batch, d.n,
-                                      d.idx_heads, T, lengths, st);
-  if (e != hipSuccess) return DSA_ERROR_LAUNCH;
-  e = launch_topk(scores, DSA_F32, dq.batch, d.n, d.topk, sel, nullptr, 0, lengths, L.tk,
-                  base + L.topk_off, st);
-  if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+  hipError_t e;
+  if (L.plain) {
+    e = launch_indexer_topk(q_idx, k_idx, w, scores, d.batch, d.n, d.idx_heads, d.topk, sel,
+                            L.itk, base + L.topk_off, st);
+    if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+  } else {
+    e = launch_indexer_score(static_cast<const uint16_t*>(q_idx),
+                             static_cast<const uint16_t*>(k_idx), w, scores, d.batch, d.n,
+                             d.idx_heads, T, lengths, st);
+    if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+    e = launch_topk(scores, DSA_F32, dq.batch, d.n, d.topk, sel, nullptr, 0, lengths, L.tk,
+                    base + L.topk_off, st);
+    if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+  }
   e = launch_attend(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp), sel,
                     static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), sink, dq,
                     L.at, T, base + L.attend_off, st);
@@ -459,7 +563,7 @@ dsa_status_t dsa_decode_step_noalloc(const void* q_idx, const void* k_idx, const
   s = check_step_pointers(q_idx, k_idx, w, q, kv_cmp, kv_win, nullptr, out, out_idx,
                           dims->window);
   if (s != DSA_SUCCESS) return s;
-  const size_t need = step_layout(*dims, 1).bytes;
+  const size_t need = step_layout(*dims, 1, false).bytes;
   if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERROR_SCRATCH_LIMIT;
   s = check_device();
   if (s != DSA_SUCCESS) return s;

@@ -188,6 +188,32 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
                                 float* s, int B, int N, int H, int tokens,
                                 const int32_t* lengths, hipStream_t st);
 
+// The indexer fused with a per-chunk cut of the top-k: chunk c of C
+// interleaved chunks of row b (one group of 32 keys out of every C) keeps
+// its top scores, between `target` and `keep` of them, as composites in cand
+// [B, C, keep], their number in cnt [B, C], and in tcut [B, C] a composite
+// that every kept one reaches and every dropped one lies below (0: the
+// chunk kept all its scores). The scores are written to s as launch_indexer_score
+// writes them.
+struct CutPlan {
+  bool ok;     // the shape fits the fused path
+  int chunks;  // C
+  int target;  // a chunk keeps at least this many of its top scores
+  int keep;    // and at most this many (its candidate slots)
+  int mcap;    // keys of the largest chunk
+};
+CutPlan plan_cut(int B, int N, int k);
+hipError_t launch_indexer_cut(const uint16_t* q, const uint16_t* k, const float* w, float* s,
+                              int B, int N, int H, const CutPlan& p, uint64_t* cand,
+                              uint32_t* cnt, uint64_t* tcut, hipStream_t st);
+// The row merge of the chunk cut: the k largest composites of each row's
+// kept candidates, written to out_idx [B, k] when every chunk's cut lies at
+// or below the row's k-th kept composite (then the answer is exact); other
+// rows are selected again, exactly, from the float32 score rows.
+hipError_t launch_topk_cut_merge(const float* scores, int B, int N, int k, const CutPlan& p,
+                                 const uint64_t* cand, const uint32_t* cnt, const uint64_t* tcut,
+                                 int32_t* out_idx, hipStream_t st);
+
 // Indexer query projection: out bf16 [B, O] = x bf16 [B, d_in] @ w^T, w
 // bf16 [O, d_in]; d_in a multiple of 256, O of 32.
 hipError_t launch_qproj(const uint16_t* x, const uint16_t* w, uint16_t* out, int B, int d_in,

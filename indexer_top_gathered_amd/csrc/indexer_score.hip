@@ -20,6 +20,8 @@
 // in registers for the whole sweep. Each lane ends with four heads of one
 // key; the head sum finishes with two cross-lane steps. Summation order is
 // fixed, so results are deterministic.
+#include <cmath>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -32,14 +34,34 @@ constexpr int kIsKeysPerStep = 16 * kIsTiles;     // keys per wave per step
 constexpr int kIsKeysPerRound = kIsWaves * kIsKeysPerStep;  // 256 per workgroup round
 constexpr int kDI = 128;
 
+// Interleaved chunks of a row: its groups of 32 keys are taken C at a time
+// (super-group L holds groups L*C .. L*C + C-1) and chunk c gets group
+// L*C + (c + L) mod C of each, so every chunk samples the whole row evenly
+// (a rising row gives every chunk the same share of its top k), and one
+// chunk's consecutive groups are never a power-of-two stride apart (which
+// measured 1.5 us slower on the production shape: the loads of a workgroup
+// then pile onto few memory channels).
+__device__ __forceinline__ int chunk_group(int c, int C, int L) { return L * C + (c + L) % C; }
+__device__ __forceinline__ int chunk_group_count(int c, int C, int groups) {
+  const int full = groups / C, rem = groups % C;
+  return full + ((c + full) % C < rem ? 1 : 0);
+}
+
 // One workgroup's sweep over keys [start, end) of batch row b: start is a
 // multiple of 256 keys, end at most the row's valid length. st: this wave's
 // 8 KB LDS staging area.
-template <int MT>  // MT = number of 16-head tiles (1..4)
+//
+// CUT sweeps take chunk c of C interleaved chunks of the row instead (one
+// group of 32 keys per wave step; start is unused, end is N). Each score's
+// order key also goes to keep[local index] in LDS (local index = 32 * (the
+// group's rank in the chunk) + offset; 0 for a position past N), for the
+// cut that follows the sweep.
+template <int MT, bool CUT = false>  // MT = number of 16-head tiles (1..4)
 __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k,
                                           const float* __restrict__ w, float* __restrict__ s,
-                                          int b, int N, int H, int start, int end, u32x4* st) {
+                                          int b, int N, int H, int start, int end, u32x4* st,
+                                          int c = 0, int C = 1, uint32_t* keep = nullptr) {
   // The thread index passes through an empty asm statement, so that the
   // values derived from it are formed per call: a caller that sweeps
   // several rows in a loop does not keep them live across its iterations.
@@ -88,7 +110,7 @@ __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
       r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(krow + (size_t)key * kDI) + (lane & 15));
     }
   };
-  auto score_step = [&](const u32x4 (&r)[8], int key0) {
+  auto score_step = [&](const u32x4 (&r)[8], int key0, int local0) {
     // stage: key q = 4j + lane/16, chunk c = lane%16 -> slot q*16 + (c ^ (q & 15))
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -131,24 +153,36 @@ __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
     if (g < 2) {
       const int key = key0 + g * 16 + m;
       if (key < end) srow[key] = mine;
+      if constexpr (CUT) keep[local0 + g * 16 + m] = key < end ? f32_key(__float_as_uint(mine)) : 0u;
     }
   };
   // Three register buffers in turn: two steps of loads in flight while one
   // step is staged and computed.
   u32x4 ra[8], rb[8], rc[8];
   int key0 = start + wave * kIsKeysPerStep;
-  const int nsteps = key0 < end ? (end - key0 + kIsKeysPerRound - 1) / kIsKeysPerRound : 0;
-  if (nsteps > 0) load_step(ra, key0);
-  if (nsteps > 1) load_step(rb, key0 + kIsKeysPerRound);
+  int nsteps = key0 < end ? (end - key0 + kIsKeysPerRound - 1) / kIsKeysPerRound : 0;
+  if constexpr (CUT) {
+    // Step i of this wave takes the chunk's group 8i + wave.
+    const int groups = (N + kIsKeysPerStep - 1) / kIsKeysPerStep;
+    const int mine_groups = chunk_group_count(c, C, groups);
+    nsteps = wave < mine_groups ? (mine_groups - wave + kIsWaves - 1) / kIsWaves : 0;
+  }
+  auto key_at = [&](int i) {
+    if constexpr (CUT) return chunk_group(c, C, i * kIsWaves + wave) * kIsKeysPerStep;
+    return key0 + i * kIsKeysPerRound;
+  };
+  auto local_at = [&](int i) { return (i * kIsWaves + wave) * kIsKeysPerStep; };
+  if (nsteps > 0) load_step(ra, key_at(0));
+  if (nsteps > 1) load_step(rb, key_at(1));
   for (int i = 0; i < nsteps; i += 3) {
-    if (i + 2 < nsteps) load_step(rc, key0 + (i + 2) * kIsKeysPerRound);
-    score_step(ra, key0 + i * kIsKeysPerRound);
+    if (i + 2 < nsteps) load_step(rc, key_at(i + 2));
+    score_step(ra, key_at(i), local_at(i));
     if (i + 1 >= nsteps) break;
-    if (i + 3 < nsteps) load_step(ra, key0 + (i + 3) * kIsKeysPerRound);
-    score_step(rb, key0 + (i + 1) * kIsKeysPerRound);
+    if (i + 3 < nsteps) load_step(ra, key_at(i + 3));
+    score_step(rb, key_at(i + 1), local_at(i + 1));
     if (i + 2 >= nsteps) break;
-    if (i + 4 < nsteps) load_step(rb, key0 + (i + 4) * kIsKeysPerRound);
-    score_step(rc, key0 + (i + 2) * kIsKeysPerRound);
+    if (i + 4 < nsteps) load_step(rb, key_at(i + 4));
+    score_step(rc, key_at(i + 2), local_at(i + 2));
   }
 }
 
@@ -161,6 +195,283 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_kernel(
   const int start = blockIdx.x * keys_per_wg;
   const int end = min(N, start + keys_per_wg);
   sweep_row<MT>(q, k, w, s, b, N, H, start, end, stage_lds[threadIdx.x / kWave]);
+}
+
+// ---------------------------------------------------------------- chunk cut
+// The indexer fused with the first half of the top-k ("feat: Add DeepSeek-V4
+// CSA attention kernels", "The top-k on the GPSIMD engine": the score and
+// the top-k run together chunk by chunk, and a last top-k merges the chunks'
+// results). Each workgroup scores chunk c of C interleaved chunks of its row
+// (see sweep_row), keeps every score's order key in LDS, and then keeps the
+// chunk's exact top KL under (value desc, position asc), written as 64-bit
+// composites, together with t_c, the smallest kept composite (0 when the
+// chunk kept every score it has). A merge kernel then selects the row's k-th
+// composite T* among the kept ones; when every t_c <= T*, no dropped score
+// can be in the row's top k and the merge's answer is exact.
+
+constexpr int kCutBins = 2048;  // buckets of a cut round (11 bits)
+
+struct CutScratch {
+  uint32_t wsum[kIsWaves];
+  uint32_t wmin[kIsWaves], wmax[kIsWaves];
+  uint64_t wcomp[kIsWaves];
+  uint32_t digit, above, in_bucket;
+};
+
+// Exclusive block-wide scan in thread order; *total gets the sum.
+__device__ __forceinline__ uint32_t cut_scan(uint32_t v, uint32_t* total, CutScratch& cs) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const uint32_t inc = wave_scan_incl(v);
+  if (lane == kWave - 1) cs.wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kIsWaves; ++w) {
+    const uint32_t x = cs.wsum[w];
+    before += (w < wave) ? x : 0u;
+    all += x;
+  }
+  __syncthreads();  // wsum is written again by the next scan
+  *total = all;
+  return before + inc - v;
+}
+
+// Wave 0 finds the bucket of hist[0..kCutBins) that holds the need-th
+// largest entry (buckets in ascending key order) and publishes it.
+__device__ __forceinline__ void cut_pick(const uint32_t* hist, uint32_t need, CutScratch& cs) {
+  constexpr int PER = kCutBins / kWave;  // 32 buckets per lane
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    // Lane l sums the buckets ending at kCutBins-1-PER*l, so lane order is
+    // descending bucket order.
+    const int base = kCutBins - PER * (tid + 1);
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(hist + base + 4 * j);
+      local += x[0] + x[1] + x[2] + x[3];
+    }
+    const uint32_t inc = wave_scan_incl(local);
+    const int first = __ffsll((long long)__ballot(inc >= need)) - 1;
+    const uint32_t run = lane_read(inc - local, first);
+    const int top = kCutBins - 1 - PER * first;
+    const uint32_t cj = tid < PER ? hist[top - tid] : 0u;
+    const uint32_t incj = wave_scan_incl(cj);
+    const int j = __ffsll((long long)__ballot(tid < PER && run + incj >= need)) - 1;
+    if (tid == j) {
+      cs.digit = (uint32_t)(top - j);
+      cs.above = run + incj - cj;
+      cs.in_bucket = cj;
+    }
+  }
+  __syncthreads();
+}
+
+// The chunk's exact top KL (or all of its valid keys when it has no more).
+// keep[0..M): order keys by local index, 0 = no score. The selection is
+// "key > t_gt, or key == t_eq among the first need_eq such keys by index",
+// found by range-adaptive 11-bit histogram rounds over the keys. Expects the
+// histogram clear and leaves it so.
+__device__ __noinline__ void chunk_cut_exact(const uint32_t* keep, int M, int valid, int KL, int b,
+                                             int c, int C, uint32_t* hist, CutScratch& cs,
+                                             uint64_t* __restrict__ cand,
+                                             uint32_t* __restrict__ cnt,
+                                             uint64_t* __restrict__ tcut) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  int64_t t_gt = 0;        // keys above it are in
+  uint32_t t_eq = 0, need_eq = 0;
+  const bool all = valid <= KL;
+  if (!all) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+    for (int i = tid; i < M; i += kIsThreads) {
+      const uint32_t x = keep[i];
+      if (x) {
+        lo = min(lo, x);
+        hi = max(hi, x);
+      }
+    }
+    lo = wave_reduce<OpMin>(lo);
+    hi = wave_reduce<OpMax>(hi);
+    if (lane == 0) {
+      cs.wmin[wave] = lo;
+      cs.wmax[wave] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kIsWaves; ++w) {
+      lo = min(lo, cs.wmin[w]);
+      hi = max(hi, cs.wmax[w]);
+    }
+    uint32_t need = (uint32_t)KL;
+    for (int round = 0; round < 4; ++round) {  // 11-bit rounds: 3 narrow any 32-bit range
+      if (lo == hi) {  // what is left ties on one key: take the first `need` of them
+        t_gt = lo;
+        t_eq = lo;
+        need_eq = need;
+        break;
+      }
+      const uint32_t range = hi - lo;
+      const int shift = max(0, 31 - __clz(range) - 10);
+      for (int i = tid; i < M; i += kIsThreads) {
+        const uint32_t x = keep[i];
+        if (x >= lo && x <= hi) atomicAdd(&hist[(x - lo) >> shift], 1u);
+      }
+      __syncthreads();
+      cut_pick(hist, need, cs);
+      const uint32_t digit = cs.digit, above = cs.above, in_bucket = cs.in_bucket;
+      for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
+      __syncthreads();  // every thread has read the pick; the histogram is clear
+      need -= above;
+      const uint32_t blo = lo + (digit << shift);
+      if (in_bucket == need) {  // the whole bucket is in: every key >= blo
+        t_gt = (int64_t)blo - 1;
+        need_eq = 0;
+        break;
+      }
+      const uint32_t bhi = blo + ((1u << shift) - 1u);
+      lo = blo;
+      hi = bhi < hi ? bhi : hi;
+    }
+  }
+  // Compaction in index order: thread t takes [t*per, t*per + per).
+  const int per = (M + kIsThreads - 1) / kIsThreads;
+  const int i0 = min(M, tid * per), i1 = min(M, i0 + per);
+  uint32_t ngt = 0, neq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = keep[i];
+    ngt += (x != 0u && (int64_t)x > t_gt) ? 1u : 0u;
+    neq += (x != 0u && x == t_eq && need_eq) ? 1u : 0u;
+  }
+  uint32_t totals;
+  const uint32_t before = cut_scan(ngt | (neq << 16), &totals, cs);
+  const uint32_t gt_before = before & 0xFFFFu, eq_before = before >> 16;
+  uint32_t eq_seen = eq_before;
+  uint32_t at = gt_before + min(need_eq, eq_before);
+  uint64_t* out = cand + ((size_t)b * C + c) * KL;
+  uint64_t least = ~(uint64_t)0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = keep[i];
+    if (x == 0u) continue;
+    bool sel = (int64_t)x > t_gt;
+    if (need_eq && x == t_eq) {
+      sel = sel || eq_seen < need_eq;
+      ++eq_seen;
+    }
+    if (sel && at < (uint32_t)KL) {
+      // local index i = 32 * (the group's rank in the chunk) + offset
+      const uint32_t pos = (uint32_t)(chunk_group(c, C, i >> 5) * kIsKeysPerStep + (i & 31));
+      const uint64_t cp = composite(x, pos);
+      out[at++] = cp;
+      least = cp < least ? cp : least;
+    }
+  }
+  least = wave_reduce64<true>(least);
+  if (lane == 0) cs.wcomp[wave] = least;
+  __syncthreads();
+  if (tid == 0) {
+#pragma unroll
+    for (int w = 0; w < kIsWaves; ++w) least = cs.wcomp[w] < least ? cs.wcomp[w] : least;
+    cnt[(size_t)b * C + c] = min((uint32_t)KL, (totals & 0xFFFFu) + min(need_eq, totals >> 16));
+    tcut[(size_t)b * C + c] = all ? 0ull : least;
+  }
+}
+
+// The chunk's cut: all of its scores at or above a bucket edge that leaves
+// at least `target` of them (one histogram round of 2048 buckets over the
+// chunk's key range), written in index order, with t_c = the edge as a
+// composite (every dropped composite lies below it). A chunk with at most
+// `cap` scores keeps them all (t_c = 0); when the edge would leave more than
+// `cap` (a heavy bucket of ties), the exact cut to `cap` takes over.
+__device__ void chunk_cut(const uint32_t* keep, int M, int valid, int target, int cap, int b,
+                          int c, int C, uint32_t* hist, CutScratch& cs,
+                          uint64_t* __restrict__ cand, uint32_t* __restrict__ cnt,
+                          uint64_t* __restrict__ tcut) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
+  uint32_t edge = 1;  // keys >= edge are kept (real keys are >= 1)
+  if (valid > cap) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+    for (int i = tid; i < M; i += kIsThreads) {
+      const uint32_t x = keep[i];
+      if (x) {
+        lo = min(lo, x);
+        hi = max(hi, x);
+      }
+    }
+    lo = wave_reduce<OpMin>(lo);
+    hi = wave_reduce<OpMax>(hi);
+    if (lane == 0) {
+      cs.wmin[wave] = lo;
+      cs.wmax[wave] = hi;
+    }
+    __syncthreads();  // also orders the histogram clearing
+#pragma unroll
+    for (int w = 0; w < kIsWaves; ++w) {
+      lo = min(lo, cs.wmin[w]);
+      hi = max(hi, cs.wmax[w]);
+    }
+    const uint32_t range = hi - lo;
+    const int shift = range == 0 ? 0 : max(0, 31 - __clz(range) - 10);
+    for (int i = tid; i < M; i += kIsThreads) {
+      const uint32_t x = keep[i];
+      if (x) atomicAdd(&hist[(x - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    cut_pick(hist, (uint32_t)target, cs);
+    const uint32_t digit = cs.digit, kept = cs.above + cs.in_bucket;
+    for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
+    __syncthreads();  // every thread has read the pick; the histogram is clear
+    if (kept > (uint32_t)cap) {  // uniform
+      chunk_cut_exact(keep, M, valid, cap, b, c, C, hist, cs, cand, cnt, tcut);
+      return;
+    }
+    edge = lo + (digit << shift);
+  }
+  // Compaction in index order: thread t takes [t*per, t*per + per).
+  const int per = (M + kIsThreads - 1) / kIsThreads;
+  const int i0 = min(M, tid * per), i1 = min(M, i0 + per);
+  uint32_t n = 0;
+  for (int i = i0; i < i1; ++i) n += keep[i] >= edge ? 1u : 0u;
+  uint32_t total;
+  uint32_t at = cut_scan(n, &total, cs);
+  uint64_t* out = cand + ((size_t)b * C + c) * cap;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t x = keep[i];
+    if (x >= edge && at < (uint32_t)cap) {
+      const uint32_t pos = (uint32_t)(chunk_group(c, C, i >> 5) * kIsKeysPerStep + (i & 31));
+      out[at++] = composite(x, pos);
+    }
+  }
+  if (tid == 0) {
+    cnt[(size_t)b * C + c] = min(total, (uint32_t)cap);
+    tcut[(size_t)b * C + c] = valid > cap ? ((uint64_t)edge << 32) : 0ull;
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kIsThreads) void indexer_score_cut_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ w, float* __restrict__ s, int N, int H, int C, int target,
+    int cap, uint64_t* __restrict__ cand, uint32_t* __restrict__ cnt,
+    uint64_t* __restrict__ tcut) {
+  __shared__ u32x4 stage_lds[kIsWaves][32 * 16];  // 8 KB per wave; the cut's histogram after
+  __shared__ CutScratch cs;
+  extern __shared__ uint32_t keep[];              // the chunk's order keys
+  const int b = blockIdx.y;
+  const int c = blockIdx.x;
+  sweep_row<MT, true>(q, k, w, s, b, N, H, 0, N, stage_lds[threadIdx.x / kWave], c, C, keep);
+  const int groups = (N + kIsKeysPerStep - 1) / kIsKeysPerStep;
+  const int M = chunk_group_count(c, C, groups) * kIsKeysPerStep;
+  // The row's last group may be partial: it is group (groups-1) mod C of
+  // super-group (groups-1) / C, which belongs to chunk (its slot - L) mod C.
+  const int lastL = (groups - 1) / C;
+  const int owner = (((groups - 1) % C - lastL) % C + C) % C;
+  const int valid = M - (c == owner ? groups * kIsKeysPerStep - N : 0);
+  __syncthreads();  // every key is in keep[]; the staging area is free
+  chunk_cut(keep, M, valid, target, cap, b, c, C, reinterpret_cast<uint32_t*>(&stage_lds[0][0]),
+            cs, cand, cnt, tcut);
 }
 
 // Ragged rows (lengths given): keys at or past a row's length are neither
@@ -358,6 +669,24 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_mt_kernel(
   }
 }
 
+// Keys per workgroup. Each wave keeps its query fragments (up to 16 KB per
+// batch row) in registers for its whole sweep. Aim for one round of about
+// 256 workgroups (one per CU measured fastest), each sweeping at most 32
+// rounds of 256 keys; large calls take at least 8 rounds per workgroup so
+// the query loads stay small next to the key stream, while small calls
+// (fewer than 256 * 8 rounds in all) spread over as many workgroups as they
+// can fill.
+int indexer_keys_per_wg(int B, int N) {
+  const long long per_row_rounds = (N + kIsKeysPerRound - 1) / kIsKeysPerRound;
+  const long long total_rounds = (long long)B * per_row_rounds;
+  long long rounds = (total_rounds + 255) / 256;
+  if (rounds < 8 && total_rounds >= 256 * 8) rounds = 8;
+  if (rounds > 32) rounds = 32;
+  if (rounds > per_row_rounds) rounds = per_row_rounds;
+  if (rounds < 1) rounds = 1;
+  return (int)rounds * kIsKeysPerRound;
+}
+
 template <int MT>
 hipError_t launch_mt(const uint16_t* q, const uint16_t* k, const float* w, float* s, int N, int H,
                      int T, int keys_per_wg, const int32_t* lengths, dim3 grid, hipStream_t st) {
@@ -377,20 +706,9 @@ hipError_t launch_mt(const uint16_t* q, const uint16_t* k, const float* w, float
 hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const float* w,
                                 float* s, int B, int N, int H, int tokens,
                                 const int32_t* lengths, hipStream_t st) {
-  // Each wave keeps its query fragments (up to 16 KB per batch row) in
-  // registers for its whole sweep. Aim for one round of about 256 workgroups
-  // (one per CU measured fastest), each sweeping at most 32 rounds of 256
-  // keys; large calls take at least 8 rounds per workgroup so the query
-  // loads stay small next to the key stream, while small calls (fewer than
-  // 256 * 8 rounds in all) spread over as many workgroups as they can fill.
   const long long per_row_rounds = (N + kIsKeysPerRound - 1) / kIsKeysPerRound;
   const long long total_rounds = (long long)B * per_row_rounds;
-  long long rounds = (total_rounds + 255) / 256;
-  if (rounds < 8 && total_rounds >= 256 * 8) rounds = 8;
-  if (rounds > 32) rounds = 32;
-  if (rounds > per_row_rounds) rounds = per_row_rounds;
-  if (rounds < 1) rounds = 1;
-  const int keys_per_wg = (int)rounds * kIsKeysPerRound;
+  const int keys_per_wg = indexer_keys_per_wg(B, N);
   dim3 grid((N + keys_per_wg - 1) / keys_per_wg, B);
   dim3 block(kIsThreads);
   const int mt = (H + 15) / 16;
@@ -419,6 +737,55 @@ hipError_t launch_indexer_score(const uint16_t* q, const uint16_t* k, const floa
     case 2: hipLaunchKernelGGL(indexer_score_kernel<2>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
     case 3: hipLaunchKernelGGL(indexer_score_kernel<3>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
     default: hipLaunchKernelGGL(indexer_score_kernel<4>, grid, block, 0, st, q, k, w, s, N, H, keys_per_wg); break;
+  }
+  return hipGetLastError();
+}
+
+CutPlan plan_cut(int B, int N, int k) {
+  CutPlan p{};
+  const int kpw = indexer_keys_per_wg(B, N);
+  const int C = (N + kpw - 1) / kpw;
+  const int groups = (N + kIsKeysPerStep - 1) / kIsKeysPerStep;
+  const int mcap = (groups + C - 1) / C * kIsKeysPerStep;  // keys of the largest chunk
+  // A chunk keeps at least its expected share of k plus 4 standard
+  // deviations of a random row's spread plus 16: a chunk then holds more of
+  // the row's top k than it keeps with a probability below 1e-4 even at
+  // k/C = 1 (rising rows spread evenly over interleaved chunks). Room for
+  // twice that, capped by the chunk.
+  const double share = (double)k / C;
+  long long target = (long long)(share + 4.0 * sqrt(share) + 16.0) + 1;
+  if (target > mcap) target = mcap;
+  long long cap = (2 * target + 7) / 8 * 8;
+  if (cap > mcap) cap = mcap;
+  p.chunks = C;
+  p.target = (int)target;
+  p.keep = (int)cap;
+  p.mcap = mcap;
+  // The merge holds at most 16384 candidates per row; the LDS copy of a
+  // chunk's keys at most 32 KB.
+  p.ok = (long long)C * target >= k && (long long)C * cap <= 16384 && mcap <= 8192 && C <= 1024;
+  return p;
+}
+
+hipError_t launch_indexer_cut(const uint16_t* q, const uint16_t* k, const float* w, float* s,
+                              int B, int N, int H, const CutPlan& p, uint64_t* cand,
+                              uint32_t* cnt, uint64_t* tcut, hipStream_t st) {
+  const dim3 grid((unsigned)p.chunks, (unsigned)B);
+  const dim3 block(kIsThreads);
+  const size_t lds = (size_t)p.mcap * sizeof(uint32_t);
+  const int mt = (H + 15) / 16;
+  // With the static staging area the workgroup holds more than 64 KB of LDS.
+  const void* kern = mt == 1 ? reinterpret_cast<const void*>(indexer_score_cut_kernel<1>)
+                   : mt == 2 ? reinterpret_cast<const void*>(indexer_score_cut_kernel<2>)
+                   : mt == 3 ? reinterpret_cast<const void*>(indexer_score_cut_kernel<3>)
+                             : reinterpret_cast<const void*>(indexer_score_cut_kernel<4>);
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  switch (mt) {
+    case 1: hipLaunchKernelGGL(indexer_score_cut_kernel<1>, grid, block, lds, st, q, k, w, s, N, H, p.chunks, p.target, p.keep, cand, cnt, tcut); break;
+    case 2: hipLaunchKernelGGL(indexer_score_cut_kernel<2>, grid, block, lds, st, q, k, w, s, N, H, p.chunks, p.target, p.keep, cand, cnt, tcut); break;
+    case 3: hipLaunchKernelGGL(indexer_score_cut_kernel<3>, grid, block, lds, st, q, k, w, s, N, H, p.chunks, p.target, p.keep, cand, cnt, tcut); break;
+    default: hipLaunchKernelGGL(indexer_score_cut_kernel<4>, grid, block, lds, st, q, k, w, s, N, H, p.chunks, p.target, p.keep, cand, cnt, tcut); break;
   }
   return hipGetLastError();
 }

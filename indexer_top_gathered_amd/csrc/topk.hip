@@ -985,16 +985,117 @@ __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t t
   pad_row<BF16, THREADS>(oi, out_val, out_off, nout, k);
 }
 
-template <bool BF16, int kPer>  // kPer: candidate slots per thread (segs * 2k <= 512 * kPer)
+// Exact top k of one float32 row read from global memory by one workgroup,
+// written to oi in ascending position order. The rows that the chunk cut of
+// the fused indexer could not settle come here: radix rounds over the value
+// keys (2048 buckets over the remaining key range, one pass over the row
+// each), then the ties at the k-th value taken by lowest position. Slow
+// (several passes over the row by one workgroup) and rare: a random row
+// never comes here at the production shape, a sorted one neither (the
+// chunks are interleaved), only rows built to pile their top k into few
+// chunks do.
+__device__ __noinline__ void row_topk_from_scores(const float* __restrict__ row, int N, int k,
+                                                  int32_t* __restrict__ oi, Scratch& sc) {
+  constexpr int T = kMergeThreads;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  auto key_at = [&](int i) { return f32_key(__float_as_uint(row[i])); };
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int i = tid; i < N; i += T) {
+    const uint32_t x = key_at(i);
+    lo = min(lo, x);
+    hi = max(hi, x);
+  }
+  lo = wave_reduce<OpMin>(lo);
+  hi = wave_reduce<OpMax>(hi);
+  if (lane == 0) {
+    sc.wmin[wave] = lo;
+    sc.wmax[wave] = hi;
+  }
+  for (int i = tid; i < kHBins; i += T) sc.hist[0][i] = 0;
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < T / kWave; ++w) {
+    lo = min(lo, sc.wmin[w]);
+    hi = max(hi, sc.wmax[w]);
+  }
+  // Selected: key > t_gt, or key == t_eq among the first need_eq such keys.
+  int64_t t_gt = -1;
+  uint32_t t_eq = 0, need_eq = 0;
+  uint32_t need = (uint32_t)k;
+  if (k < N) {
+    for (int round = 0; round < 4; ++round) {
+      if (lo == hi) {
+        t_gt = lo;
+        t_eq = lo;
+        need_eq = need;
+        break;
+      }
+      const uint32_t range = hi - lo;
+      const int shift = max(0, 31 - __clz(range) - (kHBinBits - 1));
+      for (int i = tid; i < N; i += T) {
+        const uint32_t x = key_at(i);
+        if (x >= lo && x <= hi) atomicAdd(&sc.hist[0][(x - lo) >> shift], 1u);
+      }
+      lds_barrier();
+      uint32_t digit, above, in_bucket;
+      pick_digit<kHBins>(sc.hist[0], need, sc, digit, above, in_bucket);
+      for (int i = tid; i < kHBins; i += T) sc.hist[0][i] = 0;
+      lds_barrier();
+      need -= above;
+      const uint32_t blo = lo + (digit << shift);
+      if (in_bucket == need) {
+        t_gt = (int64_t)blo - 1;
+        break;
+      }
+      const uint32_t bhi = blo + ((1u << shift) - 1u);
+      lo = blo;
+      hi = bhi < hi ? bhi : hi;
+    }
+  }
+  // Winners in position order, a block of 4 positions per thread at a time.
+  uint32_t gt_done = 0, eq_done = 0;
+  for (int base = 0; base < N; base += 4 * T) {
+    uint32_t x[4];
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = base + 4 * tid + e;
+      x[e] = i < N ? key_at(i) : 0u;
+      ngt += (i < N && (int64_t)x[e] > t_gt) ? 1u : 0u;
+      neq += (i < N && need_eq && x[e] == t_eq) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan<T>(ngt | (neq << 16), &tot, sc);
+    uint32_t eq_seen = eq_done + (before >> 16);
+    uint32_t at = gt_done + (before & 0xFFFFu) + min(need_eq, eq_seen);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = base + 4 * tid + e;
+      if (i >= N) continue;
+      bool sel = (int64_t)x[e] > t_gt;
+      if (need_eq && x[e] == t_eq) {
+        sel = sel || eq_seen < need_eq;
+        ++eq_seen;
+      }
+      if (sel && at < (uint32_t)k) oi[at++] = i;
+    }
+    gt_done += tot & 0xFFFFu;
+    eq_done += tot >> 16;
+    lds_barrier();  // wsum is written again by the next block's scan
+  }
+}
+
+template <bool BF16, int kPer, bool CUT = false>  // kPer: candidate slots per thread (segs * slots <= 512 * kPer)
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
-    const void* __restrict__ scores, int N, int k, int segs,
+    const void* __restrict__ scores, int N, int k, int segs, int slots,
     const uint64_t* __restrict__ cand_in, const uint32_t* __restrict__ cnt_in,
+    const uint64_t* __restrict__ tcut_in,
     int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index) {
   extern __shared__ uint32_t pos_lds[];  // k positions (sorted path)
   __shared__ Scratch sc;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  const int slots = 2 * k;  // per segment
   // Every slot of the row at once: slot q = tid + j*512 is entry q % slots
   // of segment q / slots, valid below that segment's count. All loads, the
   // counts included, are issued unconditionally (clamped into the row's
@@ -1096,6 +1197,39 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
       const uint64_t bhi = min((uint64_t)kmax, (uint64_t)blo + (((uint64_t)1 << shift) - 1));
       thr = select_exact_regs<kMergeThreads, kPer>(v, (int)need, sc, (uint64_t)blo << 32,
                                                    (bhi << 32) | 0xFFFFFFFFull);
+    }
+  }
+  if constexpr (CUT) {
+    // T*, the row's k-th largest kept composite: the smallest winner. Every
+    // chunk that dropped scores dropped only composites below its cut t_c;
+    // when all t_c <= T*, T* is at most the row's true k-th composite and
+    // nothing dropped can be in the top k, so the winners are exact.
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    uint64_t least = ~(uint64_t)0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) least = (v[j] && v[j] >= thr && v[j] < least) ? v[j] : least;
+    uint64_t cut = 0;
+    for (int j = tid; j < segs; j += kMergeThreads) {
+      const uint64_t t = tcut_in[(size_t)b * segs + j];
+      cut = t > cut ? t : cut;
+    }
+    least = wave_reduce64<true>(least);
+    cut = wave_reduce64<false>(cut);
+    if (lane == 0) {
+      sc.wlo[wave] = least;
+      sc.whi[wave] = cut;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < kMergeThreads / kWave; ++w) {
+      least = sc.wlo[w] < least ? sc.wlo[w] : least;
+      cut = sc.whi[w] > cut ? sc.whi[w] : cut;
+    }
+    lds_barrier();  // wlo/whi are written again below
+    if ((int)total < k || cut > least) {  // uniform
+      row_topk_from_scores(reinterpret_cast<const float*>(scores) + (size_t)b * N, N, k,
+                           out_idx + (size_t)b * k, sc);
+      return;
     }
   }
   // Winners in (thread, slot) order.
@@ -1279,7 +1413,8 @@ hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
     e = allow_lds(topk_merge_kernel<BF, PER>, merge_lds);                                       \
     if (e != hipSuccess) return e;                                                              \
     hipLaunchKernelGGL((topk_merge_kernel<BF, PER>), dim3(B), dim3(kMergeThreads), merge_lds, st, \
-                       scores, N, k, plan.segs, cand, cnt, out_idx, out_val, sorted_index);     \
+                       scores, N, k, plan.segs, 2 * k, cand, cnt, nullptr, out_idx, out_val,     \
+                       sorted_index);                                                           \
   } while (0)
   if (bf16) {
     if (per == 4) DSA_MERGE(true, 4); else if (per == 8) DSA_MERGE(true, 8);
@@ -1289,6 +1424,31 @@ hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
     else if (per == 16) DSA_MERGE(false, 16); else DSA_MERGE(false, 32);
   }
 #undef DSA_MERGE
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_cut_merge(const float* scores, int B, int N, int k, const CutPlan& p,
+                                 const uint64_t* cand, const uint32_t* cnt, const uint64_t* tcut,
+                                 int32_t* out_idx, hipStream_t st) {
+  int P = 1;
+  while (P < k) P <<= 1;
+  const size_t merge_lds = (size_t)P * sizeof(uint32_t);
+  const int slots = p.chunks * p.keep;
+  const int per = slots <= 512 * 4 ? 4 : slots <= 512 * 8 ? 8 : slots <= 512 * 16 ? 16 : 32;
+  hipError_t e;
+#define DSA_CUT_MERGE(PER)                                                                       \
+  do {                                                                                           \
+    e = allow_lds(topk_merge_kernel<false, PER, true>, merge_lds);                               \
+    if (e != hipSuccess) return e;                                                               \
+    hipLaunchKernelGGL((topk_merge_kernel<false, PER, true>), dim3(B), dim3(kMergeThreads),      \
+                       merge_lds, st, scores, N, k, p.chunks, p.keep, cand, cnt, tcut, out_idx,  \
+                       nullptr, 0);                                                              \
+  } while (0)
+  if (per == 4) DSA_CUT_MERGE(4);
+  else if (per == 8) DSA_CUT_MERGE(8);
+  else if (per == 16) DSA_CUT_MERGE(16);
+  else DSA_CUT_MERGE(32);
+#undef DSA_CUT_MERGE
   return hipGetLastError();
 }
 

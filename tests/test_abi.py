@@ -166,6 +166,26 @@ def test_sink_and_compress_argument_errors(lib):
     assert L.dsa_compress(v(P), v(P), v(P), 1, 1, 2048, None) == NOT_SUPPORTED
 
 
+def test_indexer_topk_argument_errors(lib):
+    L = lib.LIB
+    v = ctypes.c_void_p
+    need = L.dsa_indexer_topk_workspace_bytes(16, 32768, 64, 1024, 1)
+    assert need > 0 and L.dsa_indexer_topk_workspace_bytes(16, 32768, 64, 1024, 0) < need
+    assert L.dsa_indexer_topk_workspace_bytes(16, 32768, 64, 0, 1) == 0       # k < 1
+    assert L.dsa_indexer_topk_workspace_bytes(16, 32768, 65, 1024, 1) == 0    # H_I > 64
+    assert L.dsa_indexer_topk_chunks(16, 32768, 1024) == 16
+    assert L.dsa_indexer_topk_chunks(16, 32768, 0) == 0
+    args = (v(P), v(P), v(P), 16, 32768, 64, 128, 1024)
+    assert L.dsa_indexer_topk(*args, None, None, v(P), need, None) == INVALID          # no out
+    assert L.dsa_indexer_topk(*args, v(P + 2), None, v(P), need, None) == INVALID      # misaligned
+    assert L.dsa_indexer_topk(*args, v(P), v(P + 4), v(P), need, None) == INVALID      # scores
+    assert L.dsa_indexer_topk(*args, v(P), None, v(P), need - 1, None) == WS_SMALL
+    assert L.dsa_indexer_topk(v(P), v(P), v(P), 16, 32768, 64, 64, 1024, v(P), None, v(P), need,
+                              None) == NOT_SUPPORTED                                   # D_I != 128
+    assert L.dsa_indexer_topk(v(P), v(P), v(P), 16, 1000, 64, 128, 1001, v(P), None, v(P), need,
+                              None) == INVALID                                         # k > N
+
+
 def test_valid_call_without_device_reports_device_error(lib):
     import torch
     if torch.cuda.is_available():
@@ -176,6 +196,9 @@ def test_valid_call_without_device_reports_device_error(lib):
     assert L.dsa_decode_step_noalloc(*([v(P)] * 7), None, ctypes.byref(_dims(lib)),
                                      None) == DEVICE
     assert L.dsa_compress(v(P), v(P), v(P), 2, 3, 512, None) == DEVICE
+    need = L.dsa_indexer_topk_workspace_bytes(2, 1000, 8, 64, 1)
+    assert L.dsa_indexer_topk(v(P), v(P), v(P), 2, 1000, 8, 128, 64, v(P), None, v(P), need,
+                              None) == DEVICE
 
 
 def test_ragged_and_multi_token_argument_errors(lib):

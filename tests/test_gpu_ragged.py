@@ -230,9 +230,16 @@ def test_ragged_step_full_lengths_equal_dsa_decode_step():
     b, ib = dsa.dsa_decode_step_ragged(inp["q_idx"], inp["k_idx"], inp["w"], inp["q"],
                                        inp["kv_cmp"], inp["kv_win"], lens, s.k, s.scale,
                                        return_idx=True)
+    ra = dsa.dsa_sparse_attend(inp["q"], inp["kv_cmp"], ia, inp["kv_win"], s.scale)
+    rb = dsa.dsa_sparse_attend(inp["q"], inp["kv_cmp"], ib, inp["kv_win"], s.scale)
     torch.cuda.synchronize()
-    assert torch.equal(ia, ib)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the same selection (the plain step's indexer and top-k are fused, so
+    # its order differs), each step's output its own indices' attention
+    assert torch.equal(ia.sort(dim=1).values, ib.sort(dim=1).values)
+    assert torch.equal(a.view(torch.int16), ra.view(torch.int16))
+    assert torch.equal(b.view(torch.int16), rb.view(torch.int16))
+    lim = 1e-2 * float(b.float().abs().max()) + 1e-3
+    assert float((a.float() - b.float()).abs().max()) <= lim
 
 
 @pytest.mark.parametrize("B,N,zero_frac", [(150, 3000, 0.3), (200, 777, 0.9), (70, 40000, 0.0)])

@@ -5,8 +5,10 @@ top-k of the GPU's own indexer scores exactly (the indexer is
 deterministic, so the step's internal scores are those bits); (2) the index
 set differs from the all-oracle set only inside the near-tie band; (3) the
 attention output is within tolerance of the oracle evaluated on the GPU's
-indices; (4) the step equals the composition of the three single calls bit
-for bit."""
+indices; (4) the step equals the composition of its calls: its indices are
+dsa_indexer_topk's bit for bit and, as a set, dsa_topk's of
+dsa_indexer_score's scores, and its output is dsa_sparse_attend's on those
+indices bit for bit."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,11 +30,17 @@ def run_step(s: workloads.StepShape, inp: dict, where: str, rows=None):
     out, idx = dsa.dsa_decode_step(inp["q_idx"], inp["k_idx"], inp["w"], inp["q"],
                                    inp["kv_cmp"], inp["kv_win"], s.k, s.scale, return_idx=True)
     scores = dsa.dsa_indexer_score(inp["q_idx"], inp["k_idx"], inp["w"])
+    idx1, scores1 = dsa.dsa_indexer_topk(inp["q_idx"], inp["k_idx"], inp["w"], s.k,
+                                         return_scores=True)
     idx2 = dsa.dsa_topk(scores, s.k)
-    out2 = dsa.dsa_sparse_attend(inp["q"], inp["kv_cmp"], idx2, inp["kv_win"], s.scale)
+    out2 = dsa.dsa_sparse_attend(inp["q"], inp["kv_cmp"], idx, inp["kv_win"], s.scale)
     torch.cuda.synchronize()
     # (4) the fused step is the composition
-    assert torch.equal(idx, idx2), f"{where}: fused indices differ from the composition"
+    assert torch.equal(idx, idx1), f"{where}: step indices differ from dsa_indexer_topk's"
+    assert torch.equal(scores1.view(torch.int32), scores.view(torch.int32)), \
+        f"{where}: dsa_indexer_topk's scores differ from dsa_indexer_score's"
+    assert torch.equal(idx.sort(dim=1).values, idx2.sort(dim=1).values), \
+        f"{where}: fused index sets differ from dsa_topk's"
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), f"{where}: fused output differs"
     gidx = idx.cpu().numpy()
     # (1) exact top-k of the GPU's own scores
@@ -96,9 +104,10 @@ def test_stress_step_workload_full():
     say("    fused step done; composition of the three calls")
     scores = dsa.dsa_indexer_score(inp["q_idx"], inp["k_idx"], inp["w"])
     idx2 = dsa.dsa_topk(scores, s.k)
-    out2 = dsa.dsa_sparse_attend(inp["q"], inp["kv_cmp"], idx2, inp["kv_win"], s.scale)
+    out2 = dsa.dsa_sparse_attend(inp["q"], inp["kv_cmp"], idx, inp["kv_win"], s.scale)
     torch.cuda.synchronize()
-    assert torch.equal(idx, idx2), "stress step: fused indices differ from the composition"
+    assert torch.equal(idx.sort(dim=1).values, idx2.sort(dim=1).values), \
+        "stress step: fused index sets differ from the composition"
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), \
         "stress step: fused output differs from the composition"
     assert torch.equal(scores.view(torch.int32),

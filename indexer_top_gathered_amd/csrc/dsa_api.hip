@@ -169,7 +169,12 @@ StepLayout step_layout(const dsa_dims_t& d, int T, bool ragged) {
 
 extern "C" {
 
-const char* dsa_status_string(dsa_status_t s) {
+const char* dsa_status_string(dsa_status_t status) {
+  // Callers may pass any int (an unknown code must give a name too), and an
+  // out-of-range value may not be read as the enum in C++: take its bytes.
+  int s;
+  static_assert(sizeof(s) == sizeof(status), "dsa_status_t is an int-sized enum");
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case DSA_SUCCESS: return "DSA_SUCCESS";
     case DSA_ERROR_INVALID_VALUE: return "DSA_ERROR_INVALID_VALUE: invalid argument";

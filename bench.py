@@ -12,15 +12,23 @@ the 256 MB Infinity Cache.
 
 Printed: one JSON line. `value` is the step's effective bandwidth (its
 compulsory bytes - every input read once, the output written once - divided
-by the time per step), `us_per_step` the time per step, `roofline` the
-dominant kernel (indexer scoring) measured with HIP events on the stream it
-runs on (with `measured_hbm`, the rates of a plain torch row reduction
-and copy on 1 GiB, and the indexer's fraction of that read rate),
-`single_call_latency` the median, p10 and p90 of single steps each run
-after a 512 MiB cache-evicting write, `torch_step` the same step written
+by the time per step), `us_per_step` the time per step. `roofline` is the
+whole step against its own roofline (bytes at 8 TB/s; `frac_of_step_roofline`
+is that time over the measured one), with `kernels`: each stage timed alone
+with HIP events on the stream it runs on, in the step's launch configuration
+(the indexer alone, the fused indexer + top-k, attention + combine), each
+with its algorithmic bytes, flops, achieved rate and fraction of its own
+roofline; `traffic` fields carry HBM bytes per call from the rocprofv3
+FETCH_SIZE/WRITE_SIZE summary under profiles/ when it was taken on the
+current sources (else null). `measured_hbm` holds the rates of a plain torch
+row reduction and copy on 1 GiB. `graph` replays the step from one HIP
+graph. `single_call_latency` is the median, p10 and p90 of single steps each
+run after a 512 MiB cache-evicting write, `torch_step` the same step written
 with plain torch ops on this GPU (context), `topk` the top-k-only workload
-(bf16 64 x 131072, k=512), and `cpu_baseline` the CPU oracle timed on this
-host.
+(bf16 64 x 131072, k=512) with its fraction of the HBM roofline, and
+`cpu_baseline` the CPU oracle timed on this host over a bounded sample.
+Every timed output is checked: the last step's indices are k distinct
+in-range positions per row and both outputs equal an untimed call's.
 
 `--workload` times one of the other workloads instead (for profiling; one
 JSON line of its own, no CPU baseline): `tiny-step` (B=1, N=4096; also
@@ -34,7 +42,10 @@ timed with dsa_decode_step_ragged next to the same call at full length) or
 its keys, dsa_decode_step_mt, next to 1 and 4 tokens), `qproj` (the
 indexer query projection of 16 rows, 4096 wide, onto 64 x 128 channels) or
 `context-sweep` (the production step at N = 2K .. 32K compressed positions,
-8K .. 128K tokens at 4:1).
+8K .. 128K tokens at 4:1), `compress` (the 4-to-1 compressor at D = 512,
+one group and 1024 groups per batch row) or `sink-step` (the production
+step with a per-head attention sink, dsa_decode_step_sink, next to the same
+inputs without one).
 """
 from __future__ import annotations
 
@@ -67,7 +78,8 @@ def parse():
                    help="also run one device copy of this many MiB (for counter calibration)")
     p.add_argument("--workload", default="step",
                    choices=["step", "tiny-step", "topk-sampling", "topk-stress", "stress-step",
-                            "ragged-step", "mtp-step", "qproj", "context-sweep", "compress"])
+                            "ragged-step", "mtp-step", "qproj", "context-sweep", "compress",
+                            "sink-step"])
     return p.parse_args()
 
 
@@ -235,6 +247,42 @@ def other_workload(args):
                                 "W": s.W, "H_q": s.H_q, "D": s.D}})
         if args.workload == "tiny-step":
             line["graph"] = graph_replay_us(s, copies, out, ws, args.steps)
+        print(json.dumps(line), flush=True)
+        return
+    if args.workload == "sink-step":
+        # The production step with an attention sink per query head, next to
+        # the same inputs without one (the sink adds one logit per head to the
+        # normalisation and no bytes worth counting).
+        s = workloads.C4
+        R = max(1, min(256, -(-(1 << 30) // step_bytes(s))))
+        copies = [workloads.step_inputs(s, 6500 + 10 * r, device=dev) for r in range(R)]
+        gen = torch.Generator(device=dev).manual_seed(6599)
+        sink = torch.randn(s.H_q, generator=gen, device=dev, dtype=torch.float32)
+        dims = dsa.make_dims(s.B, s.N, s.H_I, s.D_I, s.k, s.W, s.H_q, s.D, s.scale)
+        ws = torch.empty(dsa.dsa_decode_step_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        out = torch.empty((s.B, s.H_q, s.D), dtype=torch.bfloat16, device=dev)
+
+        def call_sink(i):
+            c = copies[i % R]
+            dsa.dsa_decode_step_sink(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                     c["kv_win"], sink, s.k, s.scale, out=out, ws=ws,
+                                     stream=stream)
+
+        def call_plain(i):
+            c = copies[i % R]
+            dsa.dsa_decode_step(c["q_idx"], c["k_idx"], c["w"], c["q"], c["kv_cmp"],
+                                c["kv_win"], s.k, s.scale, out=out, ws=ws, stream=stream)
+        us = time_calls(call_sink, args.warmup, args.steps, stream)
+        us_plain = time_calls(call_plain, args.warmup, args.steps, stream)
+        one = step_bytes(s)
+        roof = step_roofline_us(s)
+        line.update({"us_per_step": round(us, 2), "value": round(one / (us * 1e-6) / 1e9, 1),
+                     "compulsory_bytes": one, "roofline_us": round(roof, 3),
+                     "frac_of_roofline": round(roof / us, 4),
+                     "without_sink_us_per_step": round(us_plain, 2),
+                     "rotating_input_copies": R,
+                     "config": {"B": s.B, "N": s.N, "H_I": s.H_I, "D_I": s.D_I, "k": s.k,
+                                "W": s.W, "H_q": s.H_q, "D": s.D, "sink": "N(0, 1) per head"}})
         print(json.dumps(line), flush=True)
         return
     if args.workload == "ragged-step":
@@ -490,6 +538,10 @@ def library_source_parts():
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "decode_step_b16_n32768_counters.md")
+# The production step's kernels, in launch order: the fused indexer + chunk
+# cut, the cut merge, attention over the splits and the split combine.
+ITK_KERNELS = ("indexer_score_cut_kernel<4>", "topk_merge_kernel<false, 8, true>")
+ATTEND_KERNELS = ("sparse_attend_kernel<512, 4, 2>", "attend_combine_kernel<512>")
 
 
 def traffic_from_profile():
@@ -727,15 +779,15 @@ def main():
         "indexer": stage("indexer", "indexer_score_kernel<4>", indexer_bytes(s), is_us,
                          flops=2 * s.B * s.N * s.H_I * s.D_I,
                          traffic=tsum("indexer_score_kernel<4>")),
-        "indexer_topk": stage("indexer_topk",
-                              "indexer_score_cut_kernel<4> + topk_merge_kernel<false, 8, true>",
+        "indexer_topk": stage("indexer_topk", " + ".join(ITK_KERNELS),
                               indexer_bytes(s) + s.B * s.k * 4, itk_us,
-                              flops=2 * s.B * s.N * s.H_I * s.D_I),
-        "attention": stage("attention", "sparse_attend_kernel<512, 4, 2> + attend_combine_kernel<512>",
-                           attend_bytes(s), sa_us, flops=attend_flops(s)),
+                              flops=2 * s.B * s.N * s.H_I * s.D_I, traffic=tsum(*ITK_KERNELS)),
+        "attention": stage("attention", " + ".join(ATTEND_KERNELS),
+                           attend_bytes(s), sa_us, flops=attend_flops(s),
+                           traffic=tsum(*ATTEND_KERNELS)),
     }
     roof_us = step_roofline_us(s)
-    step_traffic = tsum(*[k for k in traffic]) if traffic else None
+    step_traffic = tsum(*ITK_KERNELS, *ATTEND_KERNELS)
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": step_traffic,
                 "what": "the whole decode step: compulsory bytes per step / time per step",

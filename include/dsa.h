@@ -130,8 +130,10 @@ DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, i
  * top-k merges the chunks' results). The result is exactly
  * dsa_topk(dsa_indexer_score(...), k) as a set: the k positions with the
  * largest float32 score (the indexer's arithmetic, bit for bit), ties to the
- * lower index. Each row is scored in C interleaved chunks (every C-th group
- * of 32 positions); each chunk keeps its exact top few and the smallest
+ * lower index. Each row is scored in C interleaved chunks (every run of C
+ * consecutive groups of 32 positions holds one group of each chunk, in an
+ * order that rotates by one from run to run); each chunk keeps its exact
+ * top few and the smallest
  * score it kept, and a merge selects the row's k-th kept candidate T*. When
  * no chunk dropped a candidate at or above T*, the merge's answer is exact;
  * a row where some chunk did (only rows that pile their top scores into few
@@ -142,9 +144,10 @@ DSA_EXPORT dsa_status_t dsa_topk(const void* scores, dsa_dtype_t dtype, int B, i
  *   dsa_indexer_score writes them) or NULL to keep them in the workspace.
  * Requires the shapes of dsa_indexer_score and 1 <= k <= min(N, 4096).
  * ws: dsa_indexer_topk_workspace_bytes(B, N, H_I, k, scores == NULL) bytes;
- * its contents on entry do not matter. Shapes whose chunks would not fit
- * (dsa_indexer_topk_chunks returns 0) run the indexer and dsa_topk's
- * kernels instead, with the same result.
+ * its contents on entry do not matter. Shapes whose chunks would not fit,
+ * and rows short enough for dsa_topk's one-workgroup path (N <= 8192), run
+ * the indexer and dsa_topk's kernels instead (dsa_indexer_topk_chunks
+ * returns 0), with the same result.
  */
 DSA_EXPORT size_t dsa_indexer_topk_workspace_bytes(int B, int N, int H_I, int k,
                                                    int own_scores);
@@ -152,9 +155,10 @@ DSA_EXPORT dsa_status_t dsa_indexer_topk(const void* q_idx, const void* k_idx, c
                                          int B, int N, int H_I, int D_I, int k,
                                          int32_t* out_idx, float* scores, void* ws,
                                          size_t ws_bytes, void* stream);
-/* The number C of interleaved chunks dsa_indexer_topk splits each row into
- * (row position j belongs to chunk (j / 32) mod C), or 0 when the shape
- * takes the unfused kernels or is invalid. */
+/* The number C of interleaved chunks dsa_indexer_topk splits each row into,
+ * or 0 when the shape takes the unfused kernels or is invalid. Row position
+ * j lies in group g = j / 32, and group g belongs to chunk (g - g / C) mod C
+ * (integer division). */
 DSA_EXPORT int dsa_indexer_topk_chunks(int B, int N, int k);
 
 /*

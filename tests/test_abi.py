@@ -175,6 +175,10 @@ def test_indexer_topk_argument_errors(lib):
     assert L.dsa_indexer_topk_workspace_bytes(16, 32768, 65, 1024, 1) == 0    # H_I > 64
     assert L.dsa_indexer_topk_chunks(16, 32768, 1024) == 16
     assert L.dsa_indexer_topk_chunks(16, 32768, 0) == 0
+    # Rows that one top-k workgroup takes whole (N <= 8192) skip the cut.
+    assert L.dsa_indexer_topk_chunks(1, 4096, 256) == 0
+    assert L.dsa_indexer_topk_chunks(1, 8192, 256) == 0
+    assert L.dsa_indexer_topk_chunks(1, 8193, 256) > 1
     args = (v(P), v(P), v(P), 16, 32768, 64, 128, 1024)
     assert L.dsa_indexer_topk(*args, None, None, v(P), need, None) == INVALID          # no out
     assert L.dsa_indexer_topk(*args, v(P + 2), None, v(P), need, None) == INVALID      # misaligned

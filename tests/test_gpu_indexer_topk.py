@@ -5,7 +5,7 @@ oracle's top-k of those scores exactly. Rows are built through the exact
 construction of the stress workload (indexer query e_0, weights 1/H_I, key
 channel 0 = the wanted score, non-negative, exact in float32) when a given score pattern
 is wanted: sorted and reversed rows, ties, and rows whose top scores all
-sit in chunk 0 (positions with (j / 32) mod C == 0), which the chunk cut
+sit in chunk 0 (group g = j / 32 belongs to chunk (g - g / C) mod C), which the chunk cut
 cannot settle and the merge must select again from the score row.
 """
 from __future__ import annotations
@@ -63,7 +63,12 @@ def check(inp: dict, k: int, where: str, want_scores=None):
     (3, 257, 1, 256),           # one head
     (1, 40, 8, 40),             # k = N
     (2, 9000, 64, 1),           # k = 1
-    (1, 600000, 8, 2048),       # one long row: many chunks
+    (1, 600000, 8, 2048),       # one long row: more chunks than the merge holds (unfused)
+    # Chunk-cut shapes (rows longer than one top-k workgroup takes whole):
+    (3, 8193, 13, 77),          # one position past the whole-row path, ragged tail
+    (2, 12000, 64, 4096),       # the largest k over few chunk keys
+    (200, 9000, 8, 64),         # many rows of two chunks
+    (3, 10001, 1, 1),           # one head, k = 1
 ])
 def test_random_rows(B, N, H, k):
     s = workloads.StepShape(B=B, N=N, H_I=H, D_I=128, k=k, W=0, H_q=16, D=128)
@@ -89,12 +94,13 @@ def test_patterned_rows(order):
     check(exact_inputs(sc, 16, 82100), k, order, want_scores=sc)
 
 
-@pytest.mark.parametrize("B,N,k,levels", [(4, 32768, 1024, False), (3, 5000, 300, False),
-                                          (2, 20000, 2048, True), (1, 4096, 256, False)])
+@pytest.mark.parametrize("B,N,k,levels", [(4, 32768, 1024, False), (3, 9000, 300, False),
+                                          (2, 20000, 2048, True), (1, 12288, 256, False)])
 def test_rows_the_cut_cannot_settle(B, N, k, levels):
-    """The top scores of rows 0, 2, ... all sit in chunk 0's positions: that
-    chunk keeps only its top few, so the merge must select those rows again
-    from their score rows; odd rows are random and settle normally."""
+    """The top scores of rows 0, 2, ... all sit in chunk 0's positions (group
+    g = j / 32 belongs to chunk (g - g / C) mod C): that chunk keeps only its
+    top few, so the merge must select those rows again from their score
+    rows; odd rows are random and settle normally."""
     import indexer_top_gathered_amd as dsa
     C = dsa.dsa_indexer_topk_chunks(B, N, k)
     assert C >= 2, "the shape must take the chunk cut"
@@ -103,7 +109,12 @@ def test_rows_the_cut_cannot_settle(B, N, k, levels):
     if levels:
         x = torch.clamp(torch.floor((x - 4) * 8), 0, 63) / 8     # ties at every level
     pos = torch.arange(N, device=DEV)
-    in_chunk0 = ((pos // 32) % C) == 0
+    grp = pos // 32
+    in_chunk0 = ((grp - grp // C) % C) == 0
+    # More of the row's top k sit in chunk 0 than it can keep (a chunk keeps
+    # at most about twice its share k / C plus four standard deviations).
+    share = k / C
+    assert min(k, int(in_chunk0.sum())) > 2 * (share + 4 * share ** 0.5 + 17) + 8
     x[0::2, in_chunk0] += 16.0
     sc = x.to(torch.bfloat16)
     check(exact_inputs(sc, 8, 83100), k, f"piled into chunk 0 (C={C})", want_scores=sc)

@@ -453,6 +453,30 @@ dsa_status_t step_impl(const void* q_idx, const void* k_idx, const float* w, con
   const dsa_dims_t& d = *dims;
   hipError_t e;
   if (L.plain) {
+    // Where the attention kernel can select its own rows, the cut merge is
+    // folded into it: the indexer with the chunk cut, then attention.
+    const int per = L.itk.cut.ok ? attend_select_per(dq, L.at, L.itk.cut.chunks, L.itk.cut.keep) : 0;
+    if (per > 0) {
+      char* tb = base + L.topk_off;
+      SelectArgs sa{};
+      sa.cand = reinterpret_cast<const uint64_t*>(tb + L.itk.cand_off);
+      sa.cnt = reinterpret_cast<const uint32_t*>(tb + L.itk.cnt_off);
+      sa.tcut = reinterpret_cast<const uint64_t*>(tb + L.itk.tcut_off);
+      sa.scores = scores;
+      sa.idx_out = sel;
+      sa.chunks = L.itk.cut.chunks;
+      sa.keep = L.itk.cut.keep;
+      e = launch_indexer_cut(static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx),
+                             w, scores, d.batch, d.n, d.idx_heads, L.itk.cut,
+                             reinterpret_cast<uint64_t*>(tb + L.itk.cand_off),
+                             reinterpret_cast<uint32_t*>(tb + L.itk.cnt_off),
+                             reinterpret_cast<uint64_t*>(tb + L.itk.tcut_off), st);
+      if (e != hipSuccess) return DSA_ERROR_LAUNCH;
+      e = launch_attend_select(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv_cmp),
+                               static_cast<const uint16_t*>(kv_win), static_cast<uint16_t*>(out), sink,
+                               dq, L.at, sa, per, base + L.attend_off, st);
+      return to_status(e);
+    }
     e = launch_indexer_topk(q_idx, k_idx, w, scores, d.batch, d.n, d.idx_heads, d.topk, sel,
                             L.itk, base + L.topk_off, st);
     if (e != hipSuccess) return DSA_ERROR_LAUNCH;

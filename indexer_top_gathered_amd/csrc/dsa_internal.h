@@ -254,6 +254,31 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
                          const dsa_dims_t& d, const AttendPlan& plan, int tokens, void* ws,
                          hipStream_t st);
 
+// The chunk cut's candidates of the fused step, for an attention kernel that
+// selects its own rows (SEL > 0): per batch row, C lists of keep composites
+// with their counts and cuts (as the cut merge reads them), the score rows
+// for a row the cut cannot vouch for, and where the selection goes.
+struct SelectArgs {
+  const uint64_t* cand;  // [B, C, keep]
+  const uint32_t* cnt;   // [B, C]
+  const uint64_t* tcut;  // [B, C]
+  const float* scores;   // [B, N]
+  int32_t* idx_out;      // [B, k], written by the split-0, head-group-0 workgroup of each row
+  int chunks, keep;
+};
+// The attention kernel selecting its own rows (the cut merge folded in):
+// the candidate slots per thread it takes for this shape (4 or 8), or 0
+// when the shape has no such kernel (D = 512 with 64 heads per workgroup
+// and at most 4096 candidates per row only).
+int attend_select_per(const dsa_dims_t& d, const AttendPlan& p, int chunks, int keep);
+// Attention whose workgroups select their rows from the chunk cut's
+// candidates (sel), then the combine; the selection goes to sel.idx_out.
+hipError_t launch_attend_select(const uint16_t* q, const uint16_t* kv, const uint16_t* win,
+                                uint16_t* out, const float* sink, const dsa_dims_t& d,
+                                const AttendPlan& p, const SelectArgs& sel, int per, void* ws,
+                                hipStream_t st);
+
+
 // Compressor: out bf16 [groups, D] from x bf16 [groups, 4, D] and the gate
 // vector wg float [D]; D a multiple of 8, at most 1024.
 hipError_t launch_compress(const uint16_t* x, const float* wg, uint16_t* out, int groups, int D,

@@ -29,7 +29,7 @@
 // rule.
 #include <cfloat>
 
-#include "dsa_internal.h"
+#include "select_k.h"
 
 namespace dsa {
 namespace {
@@ -44,17 +44,20 @@ constexpr int kStages = 3;         // LDS tiles
 // Row-list entry of an empty slot (a negative index: no row, ragged rows).
 constexpr int kEmpty = -0x7FFFFFFF - 1;
 
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int D, int HG, int DSPLIT>
+// SEL > 0: the workgroup first selects its batch row's k rows itself from
+// the chunk cut's candidates (merge_candidates with SEL slots per thread,
+// the cut merge's selection, in the same order), instead of reading idx;
+// every workgroup of the row repeats the selection (it is latency, not
+// work), and one of them also writes it out.
+template <int D, int HG, int DSPLIT, int SEL = 0>
 __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
     uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
     const float* __restrict__ sink, int N, int k, int W, int Hq, float scale,
-    int rows_per_split, int splits, int nitems, int hgroups, int tokens) {
+    int rows_per_split, int splits, int nitems, int hgroups, int tokens, SelectArgs sel) {
+  static_assert(SEL == 0 || HG * DSPLIT * kWave == kMergeThreads,
+                "the selection runs on kMergeThreads threads");
   constexpr int WAVES = HG * DSPLIT;
   constexpr int THREADS = WAVES * kWave;
   constexpr int HW = HG * 16;           // query heads per workgroup
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   const int r1 = min(rows, r0 + rows_per_split);
 
   const int ntiles = (r1 - r0 + kTile - 1) / kTile;
-  const int32_t* irow = idx + (size_t)b * k;
+  const int32_t* irow = SEL == 0 ? idx + (size_t)b * k : nullptr;  // with SEL, idx is unused
   // Query row b is token b % tokens of batch row b / tokens, whose
   // compressed rows it gathers from.
   const uint16_t* kvb = kv + (size_t)(b / tokens) * N * D;
@@ -110,8 +113,9 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   // wave-uniform scalar loads (all issued before any is used), so they need
   // neither the row list in LDS nor a barrier. A row is copied by one
   // instruction, ROW_LANES lanes of 16 bytes each (at D = 128 the other
-  // lanes are masked off, so rows keep their padding).
-  {
+  // lanes are masked off, so rows keep their padding). (With SEL the rows
+  // are known only after the selection below.)
+  if constexpr (SEL == 0) {
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     int vr[2][kRowsPerWave];
 #pragma unroll
@@ -148,20 +152,57 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   // The split's source rows for the later tiles: >= 0 a compressed row,
   // kEmpty an empty slot (negative index), other negatives window row
   // -(v+1). Each wave notes whether it met an empty slot.
-  bool saw_empty = false;
-  for (int r = r0 + tid; r < r1; r += THREADS) {
-    int v;
-    if (r < k) {
-      v = irow[r];
-      saw_empty |= v < 0;
-      v = v < 0 ? kEmpty : (v >= N ? N - 1 : v);  // indices >= N are clamped
-    } else {
-      v = -(r - k) - 1;
+  if constexpr (SEL == 0) {
+    bool saw_empty = false;
+    for (int r = r0 + tid; r < r1; r += THREADS) {
+      int v;
+      if (r < k) {
+        v = irow[r];
+        saw_empty |= v < 0;
+        v = v < 0 ? kEmpty : (v >= N ? N - 1 : v);  // indices >= N are clamped
+      } else {
+        v = -(r - k) - 1;
+      }
+      srow[r - r0] = v;
     }
-    srow[r - r0] = v;
+    const bool wave_saw_empty = __ballot(saw_empty) != 0;  // all lanes take part
+    if (lane == 0) wempty[wave] = wave_saw_empty ? 1 : 0;
+  } else {
+    // The selection, in the tile slots before any copy goes out (the q
+    // loads above are in flight meanwhile). Winner number pos (in the cut
+    // merge's order) is row pos of the batch row's list; this split keeps
+    // [r0, r1) of it. The selection never leaves an empty slot.
+    Scratch& sc = *reinterpret_cast<Scratch*>(lds);
+    const size_t lists = (size_t)b * sel.chunks;
+    int32_t* const io = (split == 0 && hg == 0) ? sel.idx_out + (size_t)b * k : nullptr;
+    uint64_t cv[SEL];
+    uint64_t thr;
+    uint32_t pos, nkeep;
+    if (merge_candidates<SEL, true>(sel.cand + lists * sel.keep, sel.cnt + lists, sel.tcut + lists,
+                                    sel.chunks, sel.keep, k, sc, cv, thr, pos, nkeep)) {
+#pragma unroll
+      for (int j = 0; j < SEL; ++j) {
+        if (cv[j] && cv[j] >= thr && pos < (uint32_t)k) {
+          const int p = (int)min(composite_pos(cv[j]), (uint32_t)(N - 1));
+          if ((int)pos >= r0 && (int)pos < r1) srow[pos - r0] = p;
+          if (io) io[pos] = p;
+          ++pos;
+        }
+      }
+    } else {
+      int32_t* const sr = srow;
+      const int lo = r0, hi = r1;
+      row_topk_from_scores(sel.scores + (size_t)b * N, N, k,
+                           [sr, lo, hi, io](uint32_t at, int i) {
+                             if ((int)at >= lo && (int)at < hi) sr[at - lo] = i;
+                             if (io) io[at] = i;
+                           }, sc);
+    }
+    for (int r = max(r0, k) + tid; r < r1; r += THREADS) srow[r - r0] = -(r - k) - 1;
+    if (lane == 0) wempty[wave] = 0;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the selection's stores
+    lds_barrier();  // the row list is complete and the tile slots are free
   }
-  const bool wave_saw_empty = __ballot(saw_empty) != 0;  // all lanes take part
-  if (lane == 0) wempty[wave] = wave_saw_empty ? 1 : 0;
   // Settle the query loads here: otherwise the compiler places their waits
   // inside the tile loop, where they would also wait for the row copies in
   // flight.
@@ -218,6 +259,11 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       s1 = mfma16x16x32(a1, qf[kk], s1);
     }
   };
+
+  if constexpr (SEL > 0) {
+    if (ntiles > 0) dma(0);
+    if (ntiles > 1) dma(1);
+  }
 
   // Software pipeline over tiles: iteration t computes the (partial) logits
   // of tile t+1 while it finishes tile t (exchange, softmax, PV), so the
@@ -485,17 +531,17 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-template <int D, int HG, int DSPLIT>
+template <int D, int HG, int DSPLIT, int SEL = 0>
 hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                            const uint16_t* win, uint16_t* out, uint16_t* po, float* pml,
                            const float* sink, const dsa_dims_t& d, const AttendPlan& p,
-                           int tokens, hipStream_t st) {
+                           int tokens, hipStream_t st, const SelectArgs& sel = SelectArgs{}) {
   constexpr int WAVES = HG * DSPLIT;
   constexpr int ROW_WORDS = D / 2 + 4;
   constexpr int XWORDS = DSPLIT > 1 ? 2 * WAVES * kWave * 8 : 0;
   const size_t lds = ((size_t)kStages * kTile * ROW_WORDS + XWORDS) * sizeof(uint32_t) +
                      ((size_t)p.rows_per_split + WAVES) * sizeof(int32_t);
-  auto kern = sparse_attend_kernel<D, HG, DSPLIT>;
+  auto kern = sparse_attend_kernel<D, HG, DSPLIT, SEL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -504,7 +550,23 @@ hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t*
   const int grid = (nitems + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
                      pml, sink, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split,
-                     p.splits, nitems, hgroups, tokens);
+                     p.splits, nitems, hgroups, tokens, sel);
+  return hipGetLastError();
+}
+
+// The split combine (several splits only).
+hipError_t launch_combine(uint16_t* po, float* pml, const float* sink, uint16_t* out,
+                          const dsa_dims_t& d, const AttendPlan& p, hipStream_t st) {
+  const int Hq = d.q_heads;
+  const int hpw = 256 / (d.head_dim / 8);  // heads per combine workgroup
+  const int nitems = d.batch * Hq / hpw;
+  const int grid = (nitems + 7) / 8 * 8;
+  if (d.head_dim == 512)
+    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(grid), dim3(256), 0, st, po,
+                       reinterpret_cast<const float4*>(pml), sink, out, Hq, p.splits, nitems);
+  else
+    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(grid), dim3(256), 0, st, po,
+                       reinterpret_cast<const float4*>(pml), sink, out, Hq, p.splits, nitems);
   return hipGetLastError();
 }
 
@@ -553,17 +615,26 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
     else e = launch_attend_t<128, 1, 1>(q, kv, idx, win, out, po, pml, sink, d, p, tokens, st);
   }
   if (e != hipSuccess || p.splits == 1) return e;
-  const int Hq = d.q_heads;
-  const int hpw = 256 / (d.head_dim / 8);  // heads per combine workgroup
-  const int nitems = d.batch * Hq / hpw;
-  const int grid = (nitems + 7) / 8 * 8;
-  if (d.head_dim == 512)
-    hipLaunchKernelGGL((attend_combine_kernel<512>), dim3(grid), dim3(256), 0, st, po,
-                       reinterpret_cast<const float4*>(pml), sink, out, Hq, p.splits, nitems);
-  else
-    hipLaunchKernelGGL((attend_combine_kernel<128>), dim3(grid), dim3(256), 0, st, po,
-                       reinterpret_cast<const float4*>(pml), sink, out, Hq, p.splits, nitems);
-  return hipGetLastError();
+  return launch_combine(po, pml, sink, out, d, p, st);
+}
+
+int attend_select_per(const dsa_dims_t& d, const AttendPlan& p, int chunks, int keep) {
+  if (d.head_dim != 512 || p.heads_per_wg != 64) return 0;  // 512-thread workgroups only
+  const long long slots = (long long)chunks * keep;
+  return slots <= 512 * 4 ? 4 : slots <= 512 * 8 ? 8 : 0;
+}
+
+hipError_t launch_attend_select(const uint16_t* q, const uint16_t* kv, const uint16_t* win,
+                                uint16_t* out, const float* sink, const dsa_dims_t& d,
+                                const AttendPlan& p, const SelectArgs& sel, int per, void* ws,
+                                hipStream_t st) {
+  uint16_t* po = p.splits > 1 ? reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + p.part_o_off) : nullptr;
+  float* pml = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_ml_off) : nullptr;
+  hipError_t e = per == 4
+      ? launch_attend_t<512, 4, 2, 4>(q, kv, nullptr, win, out, po, pml, sink, d, p, 1, st, sel)
+      : launch_attend_t<512, 4, 2, 8>(q, kv, nullptr, win, out, po, pml, sink, d, p, 1, st, sel);
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_combine(po, pml, sink, out, d, p, st);
 }
 
 }  // namespace dsa

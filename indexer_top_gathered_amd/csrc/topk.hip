@@ -43,7 +43,7 @@
 // each round narrows it 1024-fold whatever the value distribution.
 #include <type_traits>
 
-#include "dsa_internal.h"
+#include "select_k.h"
 
 namespace dsa {
 namespace {
@@ -62,13 +62,7 @@ constexpr int kTkMaxVec = 8;       // vectors per thread per register block
 // every thread (THREADS * 8 bf16).
 template <int THREADS>
 constexpr int seg_cap() { return 4096 + THREADS * 8; }
-constexpr int kMergeThreads = 512;
 constexpr int kMergeCap = 16384;   // candidate slots per row in stage 2
-constexpr int kMaxWaves = 16;
-constexpr int kBins = 1024;        // buckets of an exact-select round
-constexpr int kBinBits = 10;
-constexpr int kHBins = 2048;       // buckets of a one-round histogram (11 bits)
-constexpr int kHBinBits = 11;
 
 // Per-half unsigned maximum of two words holding two 16-bit keys each: one
 // v_pk_max_u16. (Written as assembly: 16-bit vector element access was
@@ -80,95 +74,6 @@ __device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
   return r;
 }
 
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-struct Scratch {
-  alignas(16) uint32_t hist[2][kHBins];
-  uint64_t wlo[kMaxWaves], whi[kMaxWaves];
-  uint32_t wsum[kMaxWaves];                                 // block scans
-  uint32_t wcnt[kMaxWaves], wmin[kMaxWaves], wmax[kMaxWaves];  // count/min/max reductions
-  uint32_t digit, above, in_bucket;
-  uint32_t n_app;  // entries appended to an LDS list
-  uint64_t pick;   // a composite published to the block
-};
-
-// How many entries of list[0..n8) are above x; n8 is a multiple of 8 and
-// the list is zero-padded to it (real composites are non-zero). Every lane
-// reads the same 16-byte slots (broadcast reads), four at a time.
-typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t count_above(const uint64_t* list, uint32_t n8, uint64_t x) {
-  const u64x2* L = reinterpret_cast<const u64x2*>(list);
-  uint32_t r = 0;
-  for (uint32_t i = 0; i < n8 / 2; i += 4) {
-    const u64x2 a = L[i], b = L[i + 1], c = L[i + 2], d = L[i + 3];
-    r += (a.x > x ? 1u : 0u) + (a.y > x ? 1u : 0u) + (b.x > x ? 1u : 0u) + (b.y > x ? 1u : 0u) +
-         (c.x > x ? 1u : 0u) + (c.y > x ? 1u : 0u) + (d.x > x ? 1u : 0u) + (d.y > x ? 1u : 0u);
-  }
-  return r;
-}
-
-// Exclusive block-wide scan in thread order; *total gets the sum. One
-// barrier: every caller passes another barrier before wsum is written again.
-template <int THREADS>
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* total, Scratch& sc) {
-  constexpr int W = THREADS / kWave;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const uint32_t inc = wave_scan_incl(v);
-  if (lane == kWave - 1) sc.wsum[wave] = inc;
-  lds_barrier();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const uint32_t s = sc.wsum[w];
-    before += (w < wave) ? s : 0u;
-    all += s;
-  }
-  *total = all;
-  return before + inc - v;
-}
-
-// Wave 0 finds the digit whose bucket holds the need-th largest entry of
-// hist[0..NB) and publishes it; ends with a barrier. Two wave scans: one
-// over per-lane sums of PER bins, then one over the PER bins of the lane
-// that holds the answer (one bin per lane).
-template <int NB>
-__device__ void pick_digit(const uint32_t* hist, uint32_t need, Scratch& sc, uint32_t& digit,
-                           uint32_t& above, uint32_t& in_bucket) {
-  constexpr int PER = NB / kWave;
-  static_assert(PER % 4 == 0 && PER <= kWave, "lanes read their bins as 16-byte vectors");
-  const int tid = threadIdx.x;
-  if (tid < kWave) {
-    // Lane l owns the PER contiguous bins ending at NB-1-PER*l (read as
-    // 16-byte vectors; a scalar stride-PER pattern would hit one LDS bank
-    // many times over), so lane order is descending bin order.
-    const int base = NB - PER * (tid + 1);
-    uint32_t local = 0;
-#pragma unroll
-    for (int q = 0; q < PER / 4; ++q) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(hist + base + 4 * q);
-      local += x[0] + x[1] + x[2] + x[3];
-    }
-    const uint32_t inc = wave_scan_incl(local);
-    const int first = __ffsll((long long)__ballot(inc >= need)) - 1;  // uniform
-    const uint32_t run = (uint32_t)__builtin_amdgcn_readlane((int)(inc - local), first);
-    // Lane j takes bin NB-1-PER*first-j, again in descending order.
-    const int top = NB - 1 - PER * first;
-    const uint32_t cj = tid < PER ? hist[top - tid] : 0u;
-    const uint32_t incj = wave_scan_incl(cj);
-    const int j = __ffsll((long long)__ballot(tid < PER && run + incj >= need)) - 1;
-    if (tid == j) {
-      sc.digit = (uint32_t)(top - j);
-      sc.above = run + incj - cj;
-      sc.in_bucket = cj;
-    }
-  }
-  lds_barrier();
-  digit = sc.digit;
-  above = sc.above;
-  in_bucket = sc.in_bucket;
-}
 
 // Block-wide min and max of the entries of buf[0..cnt) inside [lo, hi];
 // every thread gets both. One barrier; the wlo/whi slots are reused only
@@ -247,72 +152,6 @@ __device__ __forceinline__ uint64_t select_exact(const uint64_t* buf, int cnt, i
   return result;
 }
 
-// The same exact select over entries held in registers: PER slots per
-// thread, 0 = empty (real composites are non-zero). No LDS reads per pass.
-template <int THREADS, int PER>
-__device__ void regs_range(const uint64_t (&v)[PER], uint64_t& lo, uint64_t& hi, Scratch& sc) {
-  constexpr int W = THREADS / kWave;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  uint64_t a = ~(uint64_t)0, z = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool in = v[j] && v[j] >= lo && v[j] <= hi;
-    a = (in && v[j] < a) ? v[j] : a;
-    z = (in && v[j] > z) ? v[j] : z;
-  }
-  a = wave_reduce64<true>(a);
-  z = wave_reduce64<false>(z);
-  if (lane == 0) {
-    sc.wlo[wave] = a;
-    sc.whi[wave] = z;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    a = sc.wlo[w] < a ? sc.wlo[w] : a;
-    z = sc.whi[w] > z ? sc.whi[w] : z;
-  }
-  lo = a;
-  hi = z;
-}
-
-template <int THREADS, int PER>
-__device__ uint64_t select_exact_regs(const uint64_t (&v)[PER], int K, Scratch& sc,
-                                      uint64_t lo = 1, uint64_t hi = ~(uint64_t)0) {
-  const int tid = threadIdx.x;
-  regs_range<THREADS, PER>(v, lo, hi, sc);
-  uint32_t need = (uint32_t)K;
-  uint64_t result = lo;
-  for (int round = 0; round < 8; ++round) {
-    const uint64_t range = hi - lo;
-    if (range == 0) {
-      result = lo;
-      break;
-    }
-    const int hb = 63 - __clzll((long long)range);
-    const int shift = hb >= kBinBits ? hb - (kBinBits - 1) : 0;
-    uint32_t* cur = sc.hist[round & 1];
-    uint32_t* nxt = sc.hist[(round + 1) & 1];
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (v[j] && v[j] >= lo && v[j] <= hi) atomicAdd(&cur[(uint32_t)((v[j] - lo) >> shift)], 1u);
-    for (int i = tid; i < kBins; i += THREADS) nxt[i] = 0;
-    lds_barrier();
-    uint32_t digit, above, in_bucket;
-    pick_digit<kBins>(cur, need, sc, digit, above, in_bucket);
-    for (int i = tid; i < kBins; i += THREADS) cur[i] = 0;  // ordered by the next barrier
-    need -= above;
-    const uint64_t blo = lo + ((uint64_t)digit << shift);
-    result = blo;
-    if (in_bucket == need) break;
-    const uint64_t bhi = blo + (((uint64_t)1 << shift) - 1);
-    lo = blo;
-    hi = bhi < hi ? bhi : hi;
-    regs_range<THREADS, PER>(v, lo, hi, sc);
-  }
-  lds_barrier();
-  return result;
-}
 
 // Keep the entries >= thr of buf[0..cnt), in order; returns the new count.
 template <int THREADS, int MAXPER>
@@ -985,107 +824,6 @@ __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t t
   pad_row<BF16, THREADS>(oi, out_val, out_off, nout, k);
 }
 
-// Exact top k of one float32 row read from global memory by one workgroup,
-// written to oi in ascending position order. The rows that the chunk cut of
-// the fused indexer could not settle come here: radix rounds over the value
-// keys (2048 buckets over the remaining key range, one pass over the row
-// each), then the ties at the k-th value taken by lowest position. Slow
-// (several passes over the row by one workgroup) and rare: a random row
-// never comes here at the production shape, a sorted one neither (the
-// chunks are interleaved), only rows built to pile their top k into few
-// chunks do.
-__device__ __noinline__ void row_topk_from_scores(const float* __restrict__ row, int N, int k,
-                                                  int32_t* __restrict__ oi, Scratch& sc) {
-  constexpr int T = kMergeThreads;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  auto key_at = [&](int i) { return f32_key(__float_as_uint(row[i])); };
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = tid; i < N; i += T) {
-    const uint32_t x = key_at(i);
-    lo = min(lo, x);
-    hi = max(hi, x);
-  }
-  lo = wave_reduce<OpMin>(lo);
-  hi = wave_reduce<OpMax>(hi);
-  if (lane == 0) {
-    sc.wmin[wave] = lo;
-    sc.wmax[wave] = hi;
-  }
-  for (int i = tid; i < kHBins; i += T) sc.hist[0][i] = 0;
-  lds_barrier();
-#pragma unroll
-  for (int w = 0; w < T / kWave; ++w) {
-    lo = min(lo, sc.wmin[w]);
-    hi = max(hi, sc.wmax[w]);
-  }
-  // Selected: key > t_gt, or key == t_eq among the first need_eq such keys.
-  int64_t t_gt = -1;
-  uint32_t t_eq = 0, need_eq = 0;
-  uint32_t need = (uint32_t)k;
-  if (k < N) {
-    for (int round = 0; round < 4; ++round) {
-      if (lo == hi) {
-        t_gt = lo;
-        t_eq = lo;
-        need_eq = need;
-        break;
-      }
-      const uint32_t range = hi - lo;
-      const int shift = max(0, 31 - __clz(range) - (kHBinBits - 1));
-      for (int i = tid; i < N; i += T) {
-        const uint32_t x = key_at(i);
-        if (x >= lo && x <= hi) atomicAdd(&sc.hist[0][(x - lo) >> shift], 1u);
-      }
-      lds_barrier();
-      uint32_t digit, above, in_bucket;
-      pick_digit<kHBins>(sc.hist[0], need, sc, digit, above, in_bucket);
-      for (int i = tid; i < kHBins; i += T) sc.hist[0][i] = 0;
-      lds_barrier();
-      need -= above;
-      const uint32_t blo = lo + (digit << shift);
-      if (in_bucket == need) {
-        t_gt = (int64_t)blo - 1;
-        break;
-      }
-      const uint32_t bhi = blo + ((1u << shift) - 1u);
-      lo = blo;
-      hi = bhi < hi ? bhi : hi;
-    }
-  }
-  // Winners in position order, a block of 4 positions per thread at a time.
-  uint32_t gt_done = 0, eq_done = 0;
-  for (int base = 0; base < N; base += 4 * T) {
-    uint32_t x[4];
-    uint32_t ngt = 0, neq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = base + 4 * tid + e;
-      x[e] = i < N ? key_at(i) : 0u;
-      ngt += (i < N && (int64_t)x[e] > t_gt) ? 1u : 0u;
-      neq += (i < N && need_eq && x[e] == t_eq) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t before = block_exclusive_scan<T>(ngt | (neq << 16), &tot, sc);
-    uint32_t eq_seen = eq_done + (before >> 16);
-    uint32_t at = gt_done + (before & 0xFFFFu) + min(need_eq, eq_seen);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = base + 4 * tid + e;
-      if (i >= N) continue;
-      bool sel = (int64_t)x[e] > t_gt;
-      if (need_eq && x[e] == t_eq) {
-        sel = sel || eq_seen < need_eq;
-        ++eq_seen;
-      }
-      if (sel && at < (uint32_t)k) oi[at++] = i;
-    }
-    gt_done += tot & 0xFFFFu;
-    eq_done += tot >> 16;
-    lds_barrier();  // wsum is written again by the next block's scan
-  }
-}
-
 template <bool BF16, int kPer, bool CUT = false>  // kPer: candidate slots per thread (segs * slots <= 512 * kPer)
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
     const void* __restrict__ scores, int N, int k, int segs, int slots,
@@ -1096,148 +834,17 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   __shared__ Scratch sc;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  // Every slot of the row at once: slot q = tid + j*512 is entry q % slots
-  // of segment q / slots, valid below that segment's count. All loads, the
-  // counts included, are issued unconditionally (clamped into the row's
-  // slots, which lie inside the workspace) so they overlap; validity is
-  // applied after.
-  const uint64_t* src = cand_in + (size_t)b * segs * slots;
-  const int nslots = segs * slots;
   uint64_t v[kPer];
-  uint32_t c[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int q = min(tid + j * kMergeThreads, nslots - 1);
-    v[j] = src[q];
-    c[j] = cnt_in[(size_t)b * segs + q / slots];
+  uint64_t thr;
+  uint32_t pos, nkeep;
+  if (!merge_candidates<kPer, CUT>(cand_in + (size_t)b * segs * slots, cnt_in + (size_t)b * segs,
+                                   CUT ? tcut_in + (size_t)b * segs : nullptr, segs, slots, k, sc,
+                                   v, thr, pos, nkeep)) {
+    int32_t* oi = out_idx + (size_t)b * k;
+    row_topk_from_scores(reinterpret_cast<const float*>(scores) + (size_t)b * N, N, k,
+                         [oi](uint32_t at, int i) { oi[at] = i; }, sc);
+    return;
   }
-  for (int i = tid; i < kHBins; i += kMergeThreads) {
-    sc.hist[0][i] = 0;
-    sc.hist[1][i] = 0;
-  }
-  if (tid == 0) sc.n_app = 0;
-  uint32_t nvalid = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int q = tid + j * kMergeThreads;
-    const bool ok = q < nslots && (uint32_t)(q % slots) < min((uint32_t)slots, c[j]);
-    v[j] = ok ? v[j] : 0;
-    nvalid += ok ? 1u : 0u;
-  }
-  // Count, smallest and largest value key of the valid entries.
-  uint32_t total, kmin, kmax;
-  {
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    uint32_t lo = 0xFFFFFFFFu, hi = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const uint32_t key = (uint32_t)(v[j] >> 32);
-      lo = v[j] ? min(lo, key) : lo;
-      hi = v[j] ? max(hi, key) : hi;
-    }
-    const uint32_t n = wave_reduce<OpAdd>(nvalid);
-    lo = wave_reduce<OpMin>(lo);
-    hi = wave_reduce<OpMax>(hi);
-    if (lane == 0) {  // wcnt/wmin/wmax: not written again in this kernel
-      sc.wcnt[wave] = n;
-      sc.wmin[wave] = lo;
-      sc.wmax[wave] = hi;
-    }
-    lds_barrier();
-    total = 0;
-    kmin = 0xFFFFFFFFu;
-    kmax = 0;
-#pragma unroll
-    for (int w = 0; w < kMergeThreads / kWave; ++w) {
-      total += sc.wcnt[w];
-      kmin = min(kmin, sc.wmin[w]);
-      kmax = max(kmax, sc.wmax[w]);
-    }
-  }
-  // The k-th largest composite. One histogram round over the value keys
-  // (2048 buckets over [kmin, kmax]) finds its bucket; if that bucket is not
-  // taken whole, its few entries are gathered in LDS and ranked against one
-  // another (composites are distinct, so exactly one has rank need-1). A
-  // bucket of more than 512 entries (heavy ties) takes the general select.
-  uint64_t thr = 0;
-  if ((int)total > k) {
-    const uint32_t range = kmax - kmin;
-    const int shift = range == 0 ? 0 : max(0, 31 - __clz(range) - (kHBinBits - 1));
-    uint32_t* h = sc.hist[0];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (v[j]) atomicAdd(&h[((uint32_t)(v[j] >> 32) - kmin) >> shift], 1u);
-    lds_barrier();
-    uint32_t digit, above, in_bucket;
-    pick_digit<kHBins>(h, (uint32_t)k, sc, digit, above, in_bucket);
-    const uint32_t need = (uint32_t)k - above;
-    const uint32_t blo = kmin + (digit << shift);
-    if (in_bucket == need) {
-      thr = (uint64_t)blo << 32;  // the whole bucket is in
-    } else if (in_bucket <= (uint32_t)kMergeThreads) {
-      uint64_t* list = reinterpret_cast<uint64_t*>(sc.hist[1]);  // 1024 entries
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (v[j] && (((uint32_t)(v[j] >> 32) - kmin) >> shift) == digit)
-          list[atomicAdd(&sc.n_app, 1u)] = v[j];
-      }
-      const uint32_t n8 = (in_bucket + 7u) & ~7u;
-      if ((uint32_t)tid >= in_bucket && (uint32_t)tid < n8) list[tid] = 0;
-      lds_barrier();
-      if (tid < (int)in_bucket) {
-        const uint64_t x = list[tid];
-        const uint32_t r = count_above(list, n8, x);
-        if (r == need - 1) sc.pick = x;
-      }
-      lds_barrier();
-      thr = sc.pick;
-    } else {
-      // Heavy bucket: start the exact select from its own entries.
-      for (int i = tid; i < kHBins; i += kMergeThreads) h[i] = 0;  // ordered by the next barrier
-      const uint64_t bhi = min((uint64_t)kmax, (uint64_t)blo + (((uint64_t)1 << shift) - 1));
-      thr = select_exact_regs<kMergeThreads, kPer>(v, (int)need, sc, (uint64_t)blo << 32,
-                                                   (bhi << 32) | 0xFFFFFFFFull);
-    }
-  }
-  if constexpr (CUT) {
-    // T*, the row's k-th largest kept composite: the smallest winner. Every
-    // chunk that dropped scores dropped only composites below its cut t_c;
-    // when all t_c <= T*, T* is at most the row's true k-th composite and
-    // nothing dropped can be in the top k, so the winners are exact.
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    uint64_t least = ~(uint64_t)0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) least = (v[j] && v[j] >= thr && v[j] < least) ? v[j] : least;
-    uint64_t cut = 0;
-    for (int j = tid; j < segs; j += kMergeThreads) {
-      const uint64_t t = tcut_in[(size_t)b * segs + j];
-      cut = t > cut ? t : cut;
-    }
-    least = wave_reduce64<true>(least);
-    cut = wave_reduce64<false>(cut);
-    if (lane == 0) {
-      sc.wlo[wave] = least;
-      sc.whi[wave] = cut;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int w = 0; w < kMergeThreads / kWave; ++w) {
-      least = sc.wlo[w] < least ? sc.wlo[w] : least;
-      cut = sc.whi[w] > cut ? sc.whi[w] : cut;
-    }
-    lds_barrier();  // wlo/whi are written again below
-    if ((int)total < k || cut > least) {  // uniform
-      row_topk_from_scores(reinterpret_cast<const float*>(scores) + (size_t)b * N, N, k,
-                           out_idx + (size_t)b * k, sc);
-      return;
-    }
-  }
-  // Winners in (thread, slot) order.
-  uint32_t keep = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) keep += (v[j] && v[j] >= thr) ? 1u : 0u;
-  uint32_t nkeep;
-  uint32_t pos = block_exclusive_scan<kMergeThreads>(keep, &nkeep, sc);
   int32_t* oi = out_idx + (size_t)b * k;
   const size_t esz = BF16 ? 2 : 4;
   const char* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;

@@ -21,6 +21,8 @@ DEV = "cuda"
 SHAPES = [
     workloads.StepShape(B=1, N=4096, H_I=8, D_I=128, k=256, W=64, H_q=16, D=128),
     workloads.StepShape(B=4, N=20000, H_I=64, D_I=128, k=1024, W=128, H_q=128, D=512),
+    # the attention kernel selects its rows from the chunk cut (no merge launch)
+    workloads.StepShape(B=3, N=12345, H_I=64, D_I=128, k=256, W=128, H_q=128, D=512),
 ]
 
 

@@ -76,6 +76,48 @@ def test_small_steps(shape):
     run_step(shape, inp, "small")
 
 
+# Shapes whose step lets the attention kernel select its rows from the chunk
+# cut's candidates (D = 512, 64 heads per attention workgroup, at most 4096
+# candidates per row), the cut merge's launch folded in: 8 and 4 candidate
+# slots per thread, a ragged N, no window, 64 and 128 query heads, few rows
+# per split, and the largest candidate count.
+@pytest.mark.parametrize("shape", [
+    workloads.StepShape(B=3, N=12345, H_I=64, D_I=128, k=256, W=128, H_q=128, D=512),
+    workloads.StepShape(B=16, N=16384, H_I=64, D_I=128, k=256, W=0, H_q=64, D=512),
+    workloads.StepShape(B=3, N=16000, H_I=16, D_I=128, k=64, W=5, H_q=128, D=512),
+    workloads.StepShape(B=12, N=16384, H_I=64, D_I=128, k=1024, W=128, H_q=128, D=512),
+])
+def test_steps_selecting_inside_attention(shape):
+    inp = workloads.step_inputs(shape, 32000 + shape.N + shape.k, device=DEV)
+    run_step(shape, inp, "selection inside attention")
+
+
+def test_step_rows_the_cut_cannot_settle():
+    """Rows 0 and 2 pile their top scores into chunk 0 (group g = j / 32
+    belongs to chunk (g - g / C) mod C), so the selection inside attention
+    takes the row again from its scores; the scores are exact (indexer query
+    e_0, weights 1/H_I, key channel 0 = the wanted score)."""
+    import indexer_top_gathered_amd as dsa
+    s = workloads.StepShape(B=4, N=16384, H_I=16, D_I=128, k=256, W=16, H_q=128, D=512)
+    C = dsa.dsa_indexer_topk_chunks(s.B, s.N, s.k)
+    assert C >= 2
+    inp = workloads.step_inputs(s, 33000, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(33100)
+    x = torch.randn(s.B, s.N, generator=g, device=DEV) + 8.0  # non-negative after rounding
+    grp = torch.arange(s.N, device=DEV) // 32
+    x[0::2, ((grp - grp // C) % C) == 0] += 16.0
+    sc = x.to(torch.bfloat16)
+    k_idx = inp["k_idx"].clone()
+    k_idx[:, :, 0] = sc
+    q_idx = torch.zeros_like(inp["q_idx"])
+    q_idx[:, :, 0] = 1.0
+    w = torch.full_like(inp["w"], 1.0 / s.H_I)
+    inp = dict(inp, q_idx=q_idx, k_idx=k_idx, w=w)
+    _, idx = run_step(s, inp, "rows piled into chunk 0")
+    ref = oracle.topk(host(sc), s.k)
+    assert_topk_equal(idx.cpu().numpy(), ref, False, "rows piled into chunk 0")
+
+
 def test_tiny_step_workload_full():
     s = workloads.C1
     run_step(s, workloads.step_inputs(s, 1000, device=DEV), "tiny step workload")

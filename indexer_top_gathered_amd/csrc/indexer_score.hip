@@ -421,12 +421,13 @@ __device__ void chunk_cut(const uint32_t* keep, int M, int valid, int target, in
     __syncthreads();
     cut_pick(hist, (uint32_t)target, cs);
     const uint32_t digit = cs.digit, kept = cs.above + cs.in_bucket;
-    for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
-    __syncthreads();  // every thread has read the pick; the histogram is clear
     if (kept > (uint32_t)cap) {  // uniform
+      for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
+      __syncthreads();  // every thread has read the pick; the histogram is clear
       chunk_cut_exact(keep, M, valid, cap, b, c, C, hist, cs, cand, cnt, tcut);
       return;
     }
+    // (The compaction below writes neither the pick nor the histogram.)
     edge = lo + (digit << shift);
   }
   // Compaction in index order: thread t takes [t*per, t*per + per).

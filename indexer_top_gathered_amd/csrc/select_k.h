@@ -313,6 +313,14 @@ __device__ __forceinline__ bool merge_candidates(const uint64_t* __restrict__ sr
     v[j] = src[q];
     c[j] = cnt_row[q / slots];
   }
+  // With CUT, the largest of the lists' cuts, loaded with them.
+  uint64_t cut = 0;
+  if constexpr (CUT) {
+    for (int j = tid; j < segs; j += kMergeThreads) {
+      const uint64_t t = tcut_row[j];
+      cut = t > cut ? t : cut;
+    }
+  }
   for (int i = tid; i < kHBins; i += kMergeThreads) {
     sc.hist[0][i] = 0;
     sc.hist[1][i] = 0;
@@ -340,10 +348,12 @@ __device__ __forceinline__ bool merge_candidates(const uint64_t* __restrict__ sr
     const uint32_t n = wave_reduce<OpAdd>(nvalid);
     lo = wave_reduce<OpMin>(lo);
     hi = wave_reduce<OpMax>(hi);
-    if (lane == 0) {  // wcnt/wmin/wmax: not written again in this kernel
+    if constexpr (CUT) cut = wave_reduce64<false>(cut);
+    if (lane == 0) {  // wcnt/wmin/wmax: not written again here; whi only behind later barriers
       sc.wcnt[wave] = n;
       sc.wmin[wave] = lo;
       sc.wmax[wave] = hi;
+      if constexpr (CUT) sc.whi[wave] = cut;
     }
     lds_barrier();
     total = 0;
@@ -354,6 +364,7 @@ __device__ __forceinline__ bool merge_candidates(const uint64_t* __restrict__ sr
       total += sc.wcnt[w];
       kmin = min(kmin, sc.wmin[w]);
       kmax = max(kmax, sc.wmax[w]);
+      if constexpr (CUT) cut = sc.whi[w] > cut ? sc.whi[w] : cut;
     }
   }
   // The k-th largest composite. One histogram round over the value keys
@@ -402,33 +413,15 @@ __device__ __forceinline__ bool merge_candidates(const uint64_t* __restrict__ sr
     }
   }
   if constexpr (CUT) {
-    // T*, the row's k-th largest kept composite: the smallest winner. Every
-    // chunk that dropped scores dropped only composites below its cut t_c;
-    // when all t_c <= T*, T* is at most the row's true k-th composite and
-    // nothing dropped can be in the top k, so the winners are exact.
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    uint64_t least = ~(uint64_t)0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) least = (v[j] && v[j] >= thr && v[j] < least) ? v[j] : least;
-    uint64_t cut = 0;
-    for (int j = tid; j < segs; j += kMergeThreads) {
-      const uint64_t t = tcut_row[j];
-      cut = t > cut ? t : cut;
-    }
-    least = wave_reduce64<true>(least);
-    cut = wave_reduce64<false>(cut);
-    if (lane == 0) {
-      sc.wlo[wave] = least;
-      sc.whi[wave] = cut;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int w = 0; w < kMergeThreads / kWave; ++w) {
-      least = sc.wlo[w] < least ? sc.wlo[w] : least;
-      cut = sc.whi[w] > cut ? sc.whi[w] : cut;
-    }
-    lds_barrier();  // wlo/whi are written again below
-    if ((int)total < k || cut > least) return false;  // uniform
+    // T*, the row's k-th largest kept composite, is the smallest winner,
+    // and every winner is >= thr (or, when all kept entries win, >= the
+    // smallest kept value key). Every chunk that dropped scores dropped only
+    // composites below its cut t_c, so when all t_c are at most that bound,
+    // nothing dropped can reach T*: T* is at most the row's true k-th
+    // composite and the winners are exact. (A bound below T* can only send a
+    // row to the fallback needlessly, never pass a wrong one.)
+    const uint64_t bound = (int)total > k ? thr : ((uint64_t)kmin << 32);
+    if ((int)total < k || cut > bound) return false;  // uniform
   }
   // Winners in (thread, slot) order.
   uint32_t keep = 0;

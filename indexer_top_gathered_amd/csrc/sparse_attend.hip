@@ -402,7 +402,36 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   // Full sum over the four lane groups that share head m.
   float l = lrun + lane_xor16(lrun);
   l += lane_xor32(l);
-  // Lane (m, g) holds O[h][dbase + 16*dt + 4g + i].
+  // Lane (m, g) holds O[h][dbase + 16*dt + 4g + i]. Results leave through
+  // LDS so that each store is 16 contiguous bytes per lane and whole head
+  // rows per instruction (straight from the MFMA layout, a store would put
+  // 8 bytes per lane into 16 rows 1 KiB apart). Every wave has passed the
+  // last tile's barrier, so the two tile slots other than the last tile's
+  // are free; each wave stages its own 16 rows there (no barrier needed).
+  // words(dt) gives the lane's two packed words of its 4 values at dt; row0
+  // is the wave's first head row of the destination (rows D apart).
+  constexpr int kPitch = DW * 2 + 8;        // bytes per staged head row (8 of padding)
+  constexpr int kSlotBytes = kTile * ROW_WORDS * 4;
+  constexpr int kPerSlot = kSlotBytes / (16 * kPitch);  // waves' rows per tile slot
+  static_assert(WAVES <= 2 * kPerSlot, "the staged rows fit two tile slots");
+  constexpr int CH = DW * 2 / 16;           // 16-byte chunks per head row
+  constexpr int HPI = kWave / CH;           // head rows per store instruction
+  static_assert(CH * HPI == kWave && 16 % HPI == 0, "whole head rows per store");
+  auto store_rows = [&](auto words, uint16_t* row0) __attribute__((always_inline)) {
+    const int last = (ntiles - 1) % kStages;
+    const int tslot = (last + 1 + wave / kPerSlot) % kStages;
+    char* wrows = reinterpret_cast<char*>(Rbuf) + tslot * kSlotBytes + (wave % kPerSlot) * 16 * kPitch;
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt)
+      *reinterpret_cast<uint2*>(wrows + m * kPitch + (dt * 16 + g * 4) * 2) = words(dt);
+#pragma unroll
+    for (int j = 0; j < 16 / HPI; ++j) {
+      const int hh = j * HPI + lane / CH, c = lane % CH;
+      const uint2 a0 = *reinterpret_cast<const uint2*>(wrows + hh * kPitch + c * 16);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(wrows + hh * kPitch + c * 16 + 8);
+      *reinterpret_cast<u32x4*>(row0 + (size_t)hh * D + c * 8) = u32x4{a0.x, a0.y, a1.x, a1.y};
+    }
+  };
   if (splits == 1) {
     // A sink (one logit of head h, no value vector) joins the normalisation:
     // with M = max(running max, sink), the sum becomes l 2^(mrun - M) +
@@ -416,13 +445,11 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       l = l * oscale + __builtin_amdgcn_exp2f(s2 - M);
     }
     const float inv = l > 0.0f ? oscale / l : 0.0f;  // no row at all: zeros
-    uint16_t* orow = out + ((size_t)b * Hq + h) * D + dbase;
-#pragma unroll
-    for (int dt = 0; dt < DTW; ++dt) {
-      const uint32_t lo = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-      const uint32_t hi = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-      *reinterpret_cast<uint2*>(orow + dt * 16 + g * 4) = make_uint2(lo, hi);
-    }
+    store_rows([&](int dt) __attribute__((always_inline)) {
+                 return make_uint2(pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv),
+                                   pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv));
+               },
+               out + ((size_t)b * Hq + (h - m)) * D + dbase);
   } else {
     // Partials in fp16, scaled by the largest magnitude of this wave's
     // share of O[h] (so every value lies in [-1, 1] and keeps 11 significant
@@ -437,13 +464,11 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const float sc = amax > 0.0f ? amax : 1.0f;
     const float inv = 1.0f / sc;
     const size_t slot = ((size_t)b * splits + split) * Hq + h;
-    uint16_t* po = part_o + slot * D + dbase;
-#pragma unroll
-    for (int dt = 0; dt < DTW; ++dt) {
-      const uint32_t lo = pack_f16x2(o[dt][0] * inv, o[dt][1] * inv);
-      const uint32_t hi = pack_f16x2(o[dt][2] * inv, o[dt][3] * inv);
-      *reinterpret_cast<uint2*>(po + dt * 16 + g * 4) = make_uint2(lo, hi);
-    }
+    store_rows([&](int dt) __attribute__((always_inline)) {
+                 return make_uint2(pack_f16x2(o[dt][0] * inv, o[dt][1] * inv),
+                                   pack_f16x2(o[dt][2] * inv, o[dt][3] * inv));
+               },
+               part_o + (slot - m) * D + dbase);
     if (g == 0) {
       float* ml = part_ml + slot * 4;
       if (dh == 0) {

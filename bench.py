@@ -538,10 +538,15 @@ def library_source_parts():
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "decode_step_b16_n32768_counters.md")
-# The production step's kernels, in launch order: the fused indexer + chunk
-# cut, the cut merge, attention over the splits and the split combine.
+# The production step's kernels, in launch order: the indexer with the chunk
+# cut, attention whose workgroups select their rows from the cut's candidates
+# (8 candidate slots per thread), and the split combine.
+STEP_KERNELS = ("indexer_score_cut_kernel<4>", "sparse_attend_kernel<512, 4, 2, 8>",
+                "attend_combine_kernel<512>")
+# The stage legs: dsa_indexer_topk (the cut and its merge kernel) and
+# dsa_sparse_attend on given indices (attention and the combine).
 ITK_KERNELS = ("indexer_score_cut_kernel<4>", "topk_merge_kernel<false, 8, true>")
-ATTEND_KERNELS = ("sparse_attend_kernel<512, 4, 2>", "attend_combine_kernel<512>")
+ATTEND_KERNELS = ("sparse_attend_kernel<512, 4, 2, 0>", "attend_combine_kernel<512>")
 
 
 def traffic_from_profile():
@@ -787,10 +792,11 @@ def main():
                            traffic=tsum(*ATTEND_KERNELS)),
     }
     roof_us = step_roofline_us(s)
-    step_traffic = tsum(*ITK_KERNELS, *ATTEND_KERNELS)
+    step_traffic = tsum(*STEP_KERNELS)
     roofline = {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(value / HBM_PEAK_GBPS, 4), "traffic": step_traffic,
                 "what": "the whole decode step: compulsory bytes per step / time per step",
+                "step_kernels": list(STEP_KERNELS),
                 "roofline_us": round(roof_us, 3), "us_per_step": round(us_step, 2),
                 "frac_of_step_roofline": round(roof_us / us_step, 4),
                 "bytes_per_step": sbytes, "kernels": kernels}

@@ -390,7 +390,9 @@ __device__ __noinline__ uint64_t select_k_lds(const uint64_t* buf, int cnt, int 
   const uint32_t range = hi - lo;
   const int shift = range == 0 ? 0 : max(0, 31 - __clz(range) - (kHBinBits - 1));
   uint32_t* h = sc.hist[0];
-  for (int i = tid; i < cnt; i += THREADS) atomicAdd(&h[((uint32_t)(buf[i] >> 32) - lo) >> shift], 1u);
+  // Wave-aggregated counts: an exact cut runs over rows of many tied scores
+  // (stress rows) as often as over others, and costs the same otherwise.
+  for (int i = tid; i < cnt; i += THREADS) hist_add(h, ((uint32_t)(buf[i] >> 32) - lo) >> shift);
   lds_barrier();
   uint32_t digit, above, in_bucket;
   pick_digit<kHBins>(h, (uint32_t)K, sc, digit, above, in_bucket);

@@ -296,9 +296,18 @@ __device__ uint32_t group_threshold(const uint32_t (&g)[G], int K, Scratch& sc) 
   const int hb = 31 - __clz(range);
   const int shift = hb >= kHBinBits ? hb - (kHBinBits - 1) : 0;
   uint32_t* h = sc.hist[0];
+  // A wave whose first maxima all tie (rows of quantised or sorted scores)
+  // takes wave-aggregated counts; checking once per wave keeps the other
+  // rows at plain atomics (bf16 stress rows 66.5 -> 62.0 us, float32 88.0 ->
+  // 78.6 us; per-count checks cost the bf16 64 x 131072 top-k 0.4-0.7 us).
+  if (__ballot(g[0] == (uint32_t)__builtin_amdgcn_readfirstlane(g[0])) == ~0ull) {  // uniform
 #pragma unroll
-  for (int e = 0; e < G; ++e)
-    if (g[e] >= lo) atomicAdd(&h[(g[e] - lo) >> shift], 1u);
+    for (int e = 0; e < G; ++e) hist_add(h, g[e] >= lo ? ((g[e] - lo) >> shift) : kNoBin);
+  } else {
+#pragma unroll
+    for (int e = 0; e < G; ++e)
+      if (g[e] >= lo) atomicAdd(&h[(g[e] - lo) >> shift], 1u);
+  }
   lds_barrier();
   uint32_t digit, above, in_bucket;
   pick_digit<kHBins>(h, (uint32_t)K, sc, digit, above, in_bucket);

@@ -83,6 +83,20 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x) {
   x = Op::f(x, dpp_all<dpp::kRowMirror>(x));  // every lane holds its row's result
   return Op::f(Op::f(lane_read(x, 0), lane_read(x, 16)), Op::f(lane_read(x, 32), lane_read(x, 48)));
 }
+// One count into LDS histogram h at bucket `bin` per lane (kNoBin: none).
+// When a whole wave hits one bucket (rows of tied scores), one lane adds 64:
+// the wave's 64 atomics to one address would otherwise run one after
+// another. Called by every lane of the wave.
+constexpr uint32_t kNoBin = 0xFFFFFFFFu;
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
+  const uint32_t first = __builtin_amdgcn_readfirstlane(bin);
+  if (__ballot(bin == first) == ~0ull) {  // uniform
+    if ((threadIdx.x & (kWave - 1)) == 0 && first != kNoBin) atomicAdd(&h[first], (uint32_t)kWave);
+  } else if (bin != kNoBin) {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
 __device__ __forceinline__ uint64_t u64_of(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_all64(uint64_t v) {

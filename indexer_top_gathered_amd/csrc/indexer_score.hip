@@ -270,41 +270,50 @@ __device__ __forceinline__ void cut_pick(const uint32_t* hist, uint32_t need, Cu
 // The chunk's exact top KL (or all of its valid keys when it has no more).
 // keep[0..M): order keys by local index, 0 = no score. The selection is
 // "key > t_gt, or key == t_eq among the first need_eq such keys by index",
-// found by range-adaptive 11-bit histogram rounds over the keys. Expects the
-// histogram clear and leaves it so.
+// found by range-adaptive 11-bit histogram rounds over the keys, starting
+// from keys [lo, hi], which hold the KL-th largest, with need of the KL
+// inside it (every key above hi is in). Each round first takes the actual
+// range of the keys inside [lo, hi], so a range that holds one tied value
+// ends the search at once (quantised scores: one round of contended
+// histogram atomics less per cut). Expects the histogram clear and leaves
+// it so.
 __device__ __noinline__ void chunk_cut_exact(const uint32_t* keep, int M, int valid, int KL, int b,
                                              int c, int C, uint32_t* hist, CutScratch& cs,
                                              uint64_t* __restrict__ cand,
                                              uint32_t* __restrict__ cnt,
-                                             uint64_t* __restrict__ tcut) {
+                                             uint64_t* __restrict__ tcut, uint32_t lo = 1u,
+                                             uint32_t hi = 0xFFFFFFFFu, uint32_t need = 0u) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   int64_t t_gt = 0;        // keys above it are in
   uint32_t t_eq = 0, need_eq = 0;
   const bool all = valid <= KL;
   if (!all) {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0;
-    for (int i = tid; i < M; i += kIsThreads) {
-      const uint32_t x = keep[i];
-      if (x) {
-        lo = min(lo, x);
-        hi = max(hi, x);
+    if (need == 0u) need = (uint32_t)KL;
+    for (int round = 0; round < 5; ++round) {  // 11-bit rounds: 3 narrow any 32-bit range
+      uint32_t a = 0xFFFFFFFFu, z = 0;
+      for (int i = tid; i < M; i += kIsThreads) {
+        const uint32_t x = keep[i];
+        if (x >= lo && x <= hi) {
+          a = min(a, x);
+          z = max(z, x);
+        }
       }
-    }
-    lo = wave_reduce<OpMin>(lo);
-    hi = wave_reduce<OpMax>(hi);
-    if (lane == 0) {
-      cs.wmin[wave] = lo;
-      cs.wmax[wave] = hi;
-    }
-    __syncthreads();
+      a = wave_reduce<OpMin>(a);
+      z = wave_reduce<OpMax>(z);
+      if (lane == 0) {
+        cs.wmin[wave] = a;
+        cs.wmax[wave] = z;
+      }
+      __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kIsWaves; ++w) {
-      lo = min(lo, cs.wmin[w]);
-      hi = max(hi, cs.wmax[w]);
-    }
-    uint32_t need = (uint32_t)KL;
-    for (int round = 0; round < 4; ++round) {  // 11-bit rounds: 3 narrow any 32-bit range
+      for (int w = 0; w < kIsWaves; ++w) {
+        a = min(a, cs.wmin[w]);
+        z = max(z, cs.wmax[w]);
+      }
+      __syncthreads();  // wmin/wmax are written again by the next round
+      lo = a;
+      hi = z;
       if (lo == hi) {  // what is left ties on one key: take the first `need` of them
         t_gt = lo;
         t_eq = lo;
@@ -315,7 +324,7 @@ __device__ __noinline__ void chunk_cut_exact(const uint32_t* keep, int M, int va
       const int shift = max(0, 31 - __clz(range) - 10);
       for (int i = tid; i < M; i += kIsThreads) {
         const uint32_t x = keep[i];
-        if (x >= lo && x <= hi) atomicAdd(&hist[(x - lo) >> shift], 1u);
+        hist_add(hist, (x >= lo && x <= hi) ? ((x - lo) >> shift) : kNoBin);
       }
       __syncthreads();
       cut_pick(hist, need, cs);
@@ -422,9 +431,14 @@ __device__ void chunk_cut(const uint32_t* keep, int M, int valid, int target, in
     cut_pick(hist, (uint32_t)target, cs);
     const uint32_t digit = cs.digit, kept = cs.above + cs.in_bucket;
     if (kept > (uint32_t)cap) {  // uniform
+      // The cap-th largest key lies in this bucket too (above < target <=
+      // cap < kept): the exact cut starts there.
       for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
       __syncthreads();  // every thread has read the pick; the histogram is clear
-      chunk_cut_exact(keep, M, valid, cap, b, c, C, hist, cs, cand, cnt, tcut);
+      const uint32_t blo = lo + (digit << shift);
+      const uint32_t bhi = min(hi, blo + ((1u << shift) - 1u));
+      chunk_cut_exact(keep, M, valid, cap, b, c, C, hist, cs, cand, cnt, tcut, blo, bhi,
+                      (uint32_t)cap - cs.above);
       return;
     }
     // (The compaction below writes neither the pick nor the histogram.)
@@ -752,11 +766,18 @@ CutPlan plan_cut(int B, int N, int k) {
   // deviations of a random row's spread plus 16: a chunk then holds more of
   // the row's top k than it keeps with a probability below 1e-4 even at
   // k/C = 1 (rising rows spread evenly over interleaved chunks). Room for
-  // twice that, capped by the chunk.
+  // twice that, rounded up to 8 and capped by the chunk: a heavier bucket at
+  // the cut's edge (tied scores) takes the exact cut. Where an eighth more
+  // (at least 8) brings a row's slots down to 2048, 4 per merging thread,
+  // the keep is that tight instead: at B = 16, N = 32768, k = 1024 (C = 16,
+  // target 113) keep 128 instead of 232 took the step from 59.5 to 57.5 us.
+  // (At B = 64, N = 262144, k = 2048 the tight keep sent 16 % of the stress
+  // rows' chunks to the exact cut, and it would not reach 4 per thread.)
   const double share = (double)k / C;
   long long target = (long long)(share + 4.0 * sqrt(share) + 16.0) + 1;
   if (target > mcap) target = mcap;
-  long long cap = (2 * target + 7) / 8 * 8;
+  long long cap = (target + (target / 8 > 8 ? target / 8 : 8) + 7) / 8 * 8;
+  if ((long long)C * cap > 2048) cap = (2 * target + 7) / 8 * 8;
   if (cap > mcap) cap = mcap;
   p.chunks = C;
   p.target = (int)target;

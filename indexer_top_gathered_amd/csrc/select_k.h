@@ -26,20 +26,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// One count into LDS histogram h at bucket `bin` per lane (kNoBin: none).
-// When a whole wave hits one bucket (rows of tied scores), one lane adds 64:
-// the wave's 64 atomics to one address would otherwise run one after
-// another. Called by every lane of the wave.
-constexpr uint32_t kNoBin = 0xFFFFFFFFu;
-__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
-  const uint32_t first = __builtin_amdgcn_readfirstlane(bin);
-  if (__ballot(bin == first) == ~0ull) {  // uniform
-    if ((threadIdx.x & (kWave - 1)) == 0 && first != kNoBin) atomicAdd(&h[first], (uint32_t)kWave);
-  } else if (bin != kNoBin) {
-    atomicAdd(&h[bin], 1u);
-  }
-}
-
 struct Scratch {
   alignas(16) uint32_t hist[2][kHBins];
   uint64_t wlo[kMaxWaves], whi[kMaxWaves];

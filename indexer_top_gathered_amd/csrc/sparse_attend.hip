@@ -645,6 +645,14 @@ hipError_t launch_attend(const uint16_t* q, const uint16_t* kv, const int32_t* i
 
 int attend_select_per(const dsa_dims_t& d, const AttendPlan& p, int chunks, int keep) {
   if (d.head_dim != 512 || p.heads_per_wg != 64) return 0;  // 512-thread workgroups only
+  // Every workgroup repeats its row's selection; that is free only while all
+  // of them run at once (one per CU of the 256). With more, the selection's
+  // latency comes once per round of workgroups, and the merge kernel, which
+  // selects each row once, is faster (B = 64, N = 262144, k = 2048: 1024
+  // workgroups, the step 869 us with the merge kernel, 915 with the selection
+  // inside attention).
+  const long long wgs = (long long)d.batch * p.splits * (d.q_heads / p.heads_per_wg);
+  if (wgs > 256) return 0;
   const long long slots = (long long)chunks * keep;
   return slots <= 512 * 4 ? 4 : slots <= 512 * 8 ? 8 : 0;
 }

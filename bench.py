@@ -540,12 +540,12 @@ def library_source_parts():
 COUNTERS = os.path.join(ROOT, "profiles", "decode_step_b16_n32768_counters.md")
 # The production step's kernels, in launch order: the indexer with the chunk
 # cut, attention whose workgroups select their rows from the cut's candidates
-# (8 candidate slots per thread), and the split combine.
-STEP_KERNELS = ("indexer_score_cut_kernel<4>", "sparse_attend_kernel<512, 4, 2, 8>",
+# (4 candidate slots per thread), and the split combine.
+STEP_KERNELS = ("indexer_score_cut_kernel<4>", "sparse_attend_kernel<512, 4, 2, 4>",
                 "attend_combine_kernel<512>")
 # The stage legs: dsa_indexer_topk (the cut and its merge kernel) and
 # dsa_sparse_attend on given indices (attention and the combine).
-ITK_KERNELS = ("indexer_score_cut_kernel<4>", "topk_merge_kernel<false, 8, true>")
+ITK_KERNELS = ("indexer_score_cut_kernel<4>", "topk_merge_kernel<false, 4, true>")
 ATTEND_KERNELS = ("sparse_attend_kernel<512, 4, 2, 0>", "attend_combine_kernel<512>")
 
 

@@ -19,10 +19,14 @@
 // scores are >= T, so T may reject everything below it; one histogram round
 // over about 2k group maxima gives such a T. Random rows let a few percent
 // through and sorted rows about k, because the spread-out groups see the
-// whole range. Each vector is first tested by its maximum, so most are
-// dismissed with a handful of instructions; survivors go to an LDS list in
-// thread order (block prefix sum). A later block of a long segment is
-// filtered by the exact k-th candidate so far; if its survivors would
+// whole range. The first block's groups also take in the blocks already
+// loaded behind it (up to two more), so its T covers all of them whatever
+// their order, and those blocks are admitted against it. Each vector is
+// first tested by its maximum, so most are dismissed with a handful of
+// instructions; survivors go to an LDS list in thread order (block prefix
+// sum). A later block of a long segment is filtered by the exact k-th
+// candidate so far (after the blocks the first T covers, the list is cut
+// to its exact top k); if its survivors would
 // overflow the list (a row rising along the segment), the block's own group
 // maxima give a higher bound, the list is cut to it, and later blocks are
 // held to it. Only if that overflows too is the block taken one vector at a
@@ -529,6 +533,13 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   bool have_thr = false;
   uint64_t thr = 0;  // once set: admit only composites > thr
   uint32_t t_floor = 0;  // raw key that the segment's k-th largest is known to reach
+  // The first block's threshold is taken over the group maxima of every
+  // block already loaded (up to three): a group then spans those blocks, so
+  // the bound does not depend on their order (a row rising along the
+  // segment no longer sets it from its lowest block), and the following
+  // blocks it covers are admitted against it with no threshold of their own.
+  int cover = 0;        // following blocks the first block's threshold covers
+  uint32_t pair_t = 0;  // that threshold (raw key)
 
   // Register blocks of THREADS*V*E scores. The first block sets a threshold
   // from its group maxima and is cut to its exact top k; later blocks are
@@ -555,9 +566,13 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   };
   // Takes up the block held in kv, at row position base; true when the
   // segment is finished (its survivors written straight to the workspace).
-  auto take_block = [&](u32x4 (&kv)[V], int64_t base) __attribute__((always_inline)) -> bool {
+  // fold: how many of the loaded blocks nx, nx2 (raw scores) the first
+  // block's threshold also covers.
+  auto take_block = [&](u32x4 (&kv)[V], int64_t base, const u32x4 (&nx)[V], const u32x4 (&nx2)[V],
+                        int fold) __attribute__((always_inline)) -> bool {
 #pragma unroll
     for (int v = 0; v < V; ++v) to_keys<BF16>(kv[v]);
+    const int fold_now = (!have_thr && cover == 0) ? fold : 0;
     // The E group maxima over vectors [v0, v1) of this thread, as raw keys,
     // into g[0..E).
     auto group_maxima = [&](uint32_t* g, int v0, int v1) __attribute__((always_inline)) {
@@ -569,6 +584,18 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
         for (int v = v0 + 1; v < v1; ++v)
 #pragma unroll
           for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], kv[v][j]);
+        if (fold_now > 0) {  // uniform
+#pragma unroll
+          for (int v = v0; v < v1; ++v)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], bf16_pair_keys(nx[v][j]));
+        }
+        if (fold_now > 1) {  // uniform
+#pragma unroll
+          for (int v = v0; v < v1; ++v)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = max_u16x2(m[j], bf16_pair_keys(nx2[v][j]));
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           g[2 * j] = m[j] & 0xFFFFu;
@@ -580,6 +607,14 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
           g[e] = kv[v0][e];
 #pragma unroll
           for (int v = v0 + 1; v < v1; ++v) g[e] = max(g[e], kv[v][e]);
+          if (fold_now > 0) {  // uniform
+#pragma unroll
+            for (int v = v0; v < v1; ++v) g[e] = max(g[e], f32_raw_key(nx[v][e]));
+          }
+          if (fold_now > 1) {  // uniform
+#pragma unroll
+            for (int v = v0; v < v1; ++v) g[e] = max(g[e], f32_raw_key(nx2[v][e]));
+          }
         }
       }
     };
@@ -645,8 +680,15 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       t0 = BF16 ? (key32 >> 16) : key32;
       if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
       t0 = max(t0, t_floor);
+    } else if (cover > 0) {
+      t0 = pair_t;  // the first block's threshold holds for this block too
+      --cover;
     } else {
       t0 = block_threshold();
+      if (fold_now > 0) {
+        pair_t = t0;
+        cover = fold_now;
+      }
     }
     // Admission: raw key >= t0. Once an exact threshold exists, t0 is its
     // value key, so ties at that value are admitted too (harmless extra
@@ -711,7 +753,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     }
     // After the first block: cut to the exact top k so that later blocks
     // are filtered by the k-th composite.
-    if (base + kBlock < seg_end && cnt > k && !have_thr) {
+    if (base + kBlock < seg_end && cnt > k && !have_thr && cover == 0) {
       const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
       cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
       for (int i = threadIdx.x; i < kHBins; i += THREADS) {
@@ -728,20 +770,20 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     // A whole row is one register block (the plan sizes V so).
     u32x4 ka[V];
     load_block(ka, seg_start);
-    take_block(ka, seg_start);
+    take_block(ka, seg_start, ka, ka, 0);
   } else {
     u32x4 ka[V], kb[V], kc[V];
     load_block(ka, seg_start);
     if (seg_start + kBlock < seg_end) load_block(kb, seg_start + kBlock);
     for (int64_t base = seg_start; base < seg_end; base += 3 * kBlock) {
       if (base + 2 * kBlock < seg_end) load_block(kc, base + 2 * kBlock);
-      if (take_block(ka, base)) return;
+      if (take_block(ka, base, kb, kc, base != seg_start ? 0 : (base + 2 * kBlock < seg_end ? 2 : (base + kBlock < seg_end ? 1 : 0)))) return;
       if (base + kBlock >= seg_end) break;
       if (base + 3 * kBlock < seg_end) load_block(ka, base + 3 * kBlock);
-      if (take_block(kb, base + kBlock)) return;
+      if (take_block(kb, base + kBlock, kc, ka, 0)) return;
       if (base + 2 * kBlock >= seg_end) break;
       if (base + 4 * kBlock < seg_end) load_block(kb, base + 4 * kBlock);
-      if (take_block(kc, base + 2 * kBlock)) return;
+      if (take_block(kc, base + 2 * kBlock, ka, kb, 0)) return;
     }
   }
   if (FUSED) {

@@ -238,8 +238,17 @@ struct TopkPlan {
   int segs;         // segments per row
   int seg_len;      // elements per segment (all but the last segment)
   int vec;          // 16-byte vectors per thread per register block (1..16)
+  // Full rows (no lengths) split into a power-of-two number of segments may
+  // take the quota form: segment s holds the interleaved 128-byte pieces
+  // that the rotation assigns it, keeps its `quota` largest scores (about
+  // its share of the row's top k) in `slots` slots instead of its own top
+  // k, and reports the cut below which it dropped everything; the merge
+  // then checks that no cut reaches the row's k-th kept score. 0: off.
+  int quota;
+  int slots;        // candidate slots per segment in quota form
   size_t cand_off;  // byte offsets inside the workspace
   size_t cnt_off;
+  size_t tcut_off;  // per-(row, segment) cuts, quota form only
   size_t bytes;     // total workspace bytes
 };
 TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt);

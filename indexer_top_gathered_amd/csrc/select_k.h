@@ -179,23 +179,27 @@ __device__ uint64_t select_exact_regs(const uint64_t (&v)[PER], int K, Scratch& 
   return result;
 }
 
-// Exact top k of one float32 row read from global memory by one workgroup:
-// emit(at, i) is called for the at-th winner i, at = 0, 1, ... in ascending
-// position order. The rows that the chunk cut of
-// the fused indexer could not settle come here: radix rounds over the value
-// keys (2048 buckets over the remaining key range, one pass over the row
-// each), then the ties at the k-th value taken by lowest position. Slow
-// (several passes over the row by one workgroup) and rare: a random row
-// never comes here at the production shape, a sorted one neither (the
-// chunks are interleaved), only rows built to pile their top k into few
-// chunks do.
-template <typename Emit>
-__device__ __noinline__ void row_topk_from_scores(const float* __restrict__ row, int N, int k,
+// Exact top k of one float32 (or bf16) row read from global memory by one
+// workgroup: emit(at, i) is called for the at-th winner i, at = 0, 1, ...
+// in ascending position order. The rows that a chunk cut (the fused
+// indexer's) or a segment quota (the top-k's) could not settle come here:
+// radix rounds over the value keys (2048 buckets over the remaining key
+// range, one pass over the row each), then the ties at the k-th value taken
+// by lowest position. Slow (several passes over the row by one workgroup)
+// and rare: a random row never comes here at the benchmarked shapes, a
+// sorted one neither (chunks and segments are interleaved), only rows built
+// to pile their top k into few chunks do.
+template <bool BF16 = false, typename Emit>
+__device__ __noinline__ void row_topk_from_scores(const void* __restrict__ row, int N, int k,
                                                   Emit emit, Scratch& sc) {
   constexpr int T = kMergeThreads;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  auto key_at = [&](int i) { return f32_key(__float_as_uint(row[i])); };
+  // A bf16 value is the float32 with its bits in the high half.
+  auto key_at = [&](int i) {
+    return BF16 ? f32_key((uint32_t)reinterpret_cast<const uint16_t*>(row)[i] << 16)
+                : f32_key(reinterpret_cast<const uint32_t*>(row)[i]);
+  };
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
   for (int i = tid; i < N; i += T) {
     const uint32_t x = key_at(i);

@@ -45,6 +45,8 @@
 // position through a bitmap; any other goes to a radix select whose 10-bit
 // digits split the remaining range into 1024 equal buckets per round, so
 // each round narrows it 1024-fold whatever the value distribution.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "select_k.h"
@@ -67,6 +69,28 @@ constexpr int kTkMaxVec = 8;       // vectors per thread per register block
 template <int THREADS>
 constexpr int seg_cap() { return 4096 + THREADS * 8; }
 constexpr int kMergeCap = 16384;   // candidate slots per row in stage 2
+
+// Quota form of the segmented path: the row is cut into pieces of 128 bytes
+// (64 bf16 or 32 float32 scores), and run r of S consecutive pieces gives
+// its piece at slot (s + r) mod S to segment s. Every run holds one piece
+// of each segment and the order rotates from run to run, so a row sorted
+// along its positions spreads its top k evenly over the segments. S is a
+// power of two. Positions inside a segment ("local") keep the row's order.
+__host__ __device__ __forceinline__ int64_t piece_pos(int64_t l, int s, int log_s, int log_p) {
+  const int64_t r = l >> log_p;
+  const int64_t j = (s + r) & (((int64_t)1 << log_s) - 1);
+  return (((r << log_s) | j) << log_p) | (l & (((int64_t)1 << log_p) - 1));
+}
+// The number of positions of a row of N that segment s holds.
+__host__ __device__ __forceinline__ int64_t piece_seg_len(int64_t N, int s, int log_s, int log_p) {
+  const int64_t run = (int64_t)1 << (log_s + log_p);
+  const int64_t full = N / run, rem = N % run;
+  const int64_t j = (s + full) & (((int64_t)1 << log_s) - 1);
+  int64_t extra = rem - (j << log_p);
+  extra = extra < 0 ? 0 : extra;
+  extra = extra > ((int64_t)1 << log_p) ? ((int64_t)1 << log_p) : extra;
+  return (full << log_p) + extra;
+}
 
 // Per-half unsigned maximum of two words holding two 16-bit keys each: one
 // v_pk_max_u16. (Written as assembly: 16-bit vector element access was
@@ -228,23 +252,24 @@ __device__ __forceinline__ u32x4 load_raw_full(const void* row, int64_t p0) {
   return __builtin_nontemporal_load(src);
 }
 // The same for any vector: positions past `end` get the padding pattern
-// (all ones), whose key is 0.
+// (all ones), whose key is 0. p0 is the vector's position in the segment's
+// order (checked against end), g0 the row position it is read from.
 template <bool BF16, bool ALIGNED>
-__device__ __forceinline__ u32x4 load_raw(const void* row, int64_t p0, int64_t end) {
+__device__ __forceinline__ u32x4 load_raw(const void* row, int64_t p0, int64_t end, int64_t g0) {
   constexpr int E = BF16 ? 8 : 4;
   u32x4 r;
   if (ALIGNED && p0 + E <= end) {
-    r = load_raw_full<BF16>(row, p0);
+    r = load_raw_full<BF16>(row, g0);
   } else {
     r = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (p0 + e < end) {
         if (BF16) {
-          const uint32_t h = reinterpret_cast<const uint16_t*>(row)[p0 + e];
+          const uint32_t h = reinterpret_cast<const uint16_t*>(row)[g0 + e];
           r[e >> 1] = (e & 1) ? ((r[e >> 1] & 0xFFFFu) | (h << 16)) : ((r[e >> 1] & 0xFFFF0000u) | h);
         } else {
-          r[e] = reinterpret_cast<const uint32_t*>(row)[p0 + e];
+          r[e] = reinterpret_cast<const uint32_t*>(row)[g0 + e];
         }
       }
     }
@@ -319,14 +344,20 @@ __device__ uint32_t group_threshold(const uint32_t (&g)[G], int K, Scratch& sc) 
   return lo + (digit << shift);
 }
 
-template <bool BF16, int V, int THREADS>
+// The admitted scores of this thread's vectors as composites at cand[at...],
+// in (vector, element) order; pos_of maps a vector's position in the
+// segment's order to the one the composite carries.
+struct SamePos {
+  __device__ int64_t operator()(int64_t p) const { return p; }
+};
+template <bool BF16, int V, int THREADS, typename PosOf = SamePos>
 __device__ __forceinline__ void write_admitted(uint64_t* cand, uint32_t at, const u32x4 (&kv)[V],
-                                               uint64_t adm, int64_t base) {
+                                               uint64_t adm, int64_t base, PosOf pos_of = PosOf{}) {
   constexpr int E = BF16 ? 8 : 4;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     uint32_t m = (uint32_t)(adm >> (v * E)) & ((1u << E) - 1u);
-    const int64_t p0 = base + ((int64_t)v * THREADS + threadIdx.x) * E;
+    const int64_t p0 = pos_of(base + ((int64_t)v * THREADS + threadIdx.x) * E);
     while (m) {
       const int e = __ffs(m) - 1;
       m &= m - 1;
@@ -499,29 +530,52 @@ __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t t
                                        int N, int k, int32_t* oi, void* out_val, size_t out_off,
                                        int sorted_index, uint32_t* pos_lds, Scratch& sc);
 
-template <bool BF16, bool ALIGNED, int V, int THREADS, bool FUSED>
+// QUOTA (full rows, segs a power of two): segment sidx takes the pieces the
+// rotation assigns it (positions in the kernel are local to the segment),
+// keeps at least its `quota` largest scores, at most `slots`, and writes its
+// cut to tcut_out: every composite it dropped lies below it.
+template <bool BF16, bool ALIGNED, int V, int THREADS, bool FUSED, bool QUOTA>
 __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     const void* __restrict__ scores, int N, int k, int seg_len, int segs,
     uint64_t* __restrict__ cand_out, uint32_t* __restrict__ cnt_out,
     int32_t* __restrict__ out_idx, void* __restrict__ out_val, int sorted_index,
-    const int32_t* __restrict__ lengths) {
+    const int32_t* __restrict__ lengths, int quota, int slots, uint64_t* __restrict__ tcut_out) {
   constexpr int E = BF16 ? 8 : 4;
   constexpr int CAP = seg_cap<THREADS>();
+  constexpr int kLogPiece = BF16 ? 6 : 5;
   static_assert(V * E <= 64, "the admission mask holds 64 bits");
+  static_assert(!(FUSED && QUOTA), "a whole row has no segments");
   extern __shared__ uint64_t cand[];  // CAP entries
   __shared__ Scratch sc;
   const int b = blockIdx.y;
   const int sidx = blockIdx.x;
   const size_t esz = BF16 ? 2 : 4;
   const void* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;
-  const int64_t seg_start = (int64_t)sidx * seg_len;
+  const int log_s = QUOTA ? __ffs(segs) - 1 : 0;
+  const int64_t seg_start = QUOTA ? 0 : (int64_t)sidx * seg_len;
   // Ragged rows: positions at or past the row's length take no part.
   const int64_t row_end = lengths ? (int64_t)min(max(lengths[b], 0), N) : (int64_t)N;
-  const int64_t seg_end = min(row_end, seg_start + seg_len);
+  const int64_t seg_end = QUOTA ? piece_seg_len(N, sidx, log_s, kLogPiece) : min(row_end, seg_start + seg_len);
+  // The row position of a segment position.
+  auto row_pos = [sidx, log_s](int64_t p) -> int64_t {
+    return QUOTA ? piece_pos(p, sidx, log_s, kLogPiece) : p;
+  };
+  // The count a segment keeps above its cut, and its output slots.
+  const int kk = QUOTA ? quota : k;
+  const int out_cap = QUOTA ? slots : 2 * k;
+  // The raw-key threshold t as the smallest composite of its value.
+  auto value_floor = [](uint32_t t) -> uint64_t {
+    return (uint64_t)(BF16 ? key32_of_key16(canon16(t)) : canon32(t)) << 32;
+  };
+  // QUOTA: the largest bound below which composites were dropped so far.
+  uint64_t tc = 0;
   constexpr int64_t kBlock = (int64_t)THREADS * V * E;
   if (seg_end <= seg_start) {  // nothing valid in this segment (uniform)
     if (FUSED) pad_row<BF16, THREADS>(out_idx + (size_t)b * k, out_val, (size_t)b * k, 0, k);
-    else if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = 0;
+    else if (threadIdx.x == 0) {
+      cnt_out[(size_t)b * segs + sidx] = 0;
+      if (QUOTA) tcut_out[(size_t)b * segs + sidx] = 0;
+    }
     return;
   }
 
@@ -557,11 +611,13 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   auto load_block = [&](u32x4 (&r)[V], int64_t at) __attribute__((always_inline)) {
     if (ALIGNED && at + kBlock <= seg_end) {  // uniform
 #pragma unroll
-      for (int v = 0; v < V; ++v) r[v] = load_raw_full<BF16>(row, at + ((int64_t)v * THREADS + threadIdx.x) * E);
+      for (int v = 0; v < V; ++v) r[v] = load_raw_full<BF16>(row, row_pos(at + ((int64_t)v * THREADS + threadIdx.x) * E));
     } else {
 #pragma unroll
-      for (int v = 0; v < V; ++v)
-        r[v] = load_raw<BF16, ALIGNED>(row, at + ((int64_t)v * THREADS + threadIdx.x) * E, seg_end);
+      for (int v = 0; v < V; ++v) {
+        const int64_t p = at + ((int64_t)v * THREADS + threadIdx.x) * E;
+        r[v] = load_raw<BF16, ALIGNED>(row, p, seg_end, row_pos(p));
+      }
     }
   };
   // Takes up the block held in kv, at row position base; true when the
@@ -628,7 +684,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       uint32_t gs[S * E];
 #pragma unroll
       for (int p = 0; p < S; ++p) group_maxima(gs + p * E, p * (V / S), (p + 1) * (V / S));
-      uint32_t t = group_threshold<THREADS, S * E>(gs, k, sc);
+      uint32_t t = group_threshold<THREADS, S * E>(gs, kk, sc);
       if (t == kNegZero) t -= 1;
       return t;
     };
@@ -637,8 +693,10 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       // and still leave a threshold near the k-th largest score; with fewer
       // than k groups the threshold would admit the whole block. (With
       // k <= 4096 and 512 threads, 2k groups take at most 4E per thread for
-      // float32 and 2E for bf16.)
-      const int gpt = (2 * k + THREADS - 1) / THREADS;  // wanted groups per thread
+      // float32 and 2E for bf16.) bf16 segments in quota form take about 4k
+      // groups: a finer threshold on rows of tied levels (bf16 stress rows 34.7 -> 28.8 us; float32 rows,
+      // which would need the split, were 1 us slower with it).
+      const int gpt = ((BF16 && QUOTA ? 4 : 2) * kk + THREADS - 1) / THREADS;  // wanted groups per thread
       if constexpr (!BF16 && V >= 4) {
         if (gpt > 2 * E) return split_threshold(std::integral_constant<int, 4>{});  // uniform
       }
@@ -659,7 +717,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
           }
         }
       }
-      uint32_t t = group_threshold<THREADS, E>(g, k, sc);
+      uint32_t t = group_threshold<THREADS, E>(g, kk, sc);
       // Raw keys place -0 one below +0; admitting from one lower keeps the tie.
       if (t == kNegZero) t -= 1;
       return t;
@@ -708,16 +766,21 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
         adm = admit_block(t0);
         excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
         lds_barrier();  // every thread has read the scan's totals
-        const uint32_t vk = BF16 ? key32_of_key16(canon16(t2)) : canon32(t2);
-        cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, (uint64_t)vk << 32, sc);
+        cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, value_floor(t2), sc);
       }
     }
-    if (!FUSED && base == seg_start && base + kBlock >= seg_end && (int)total <= 2 * k) {
+    // Everything this block drops lies below t0's value (or below an exact
+    // cut already taken into tc).
+    if (QUOTA) tc = max(tc, value_floor(t0));
+    if (!FUSED && base == seg_start && base + kBlock >= seg_end && (int)total <= out_cap) {
       // The whole segment in one block and its survivors fit the output
       // slots: write them straight to the workspace.
-      write_admitted<BF16, V, THREADS>(cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k), excl, kv,
-                                       adm, base);
-      if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = total;
+      write_admitted<BF16, V, THREADS>(cand_out + ((size_t)b * segs + sidx) * (size_t)out_cap, excl, kv,
+                                       adm, base, row_pos);
+      if (threadIdx.x == 0) {
+        cnt_out[(size_t)b * segs + sidx] = total;
+        if (QUOTA) tcut_out[(size_t)b * segs + sidx] = tc;  // a value bound: no position to map
+      }
       return true;
     }
     if (cnt + (int)total <= CAP) {
@@ -731,8 +794,9 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       // turn.
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        if (cnt + THREADS * E > CAP && cnt > k) {
-          const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
+        if (cnt + THREADS * E > CAP && cnt > kk) {
+          const uint64_t t = select_k_lds<THREADS>(cand, cnt, kk, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
+          if (QUOTA) tc = max(tc, t);
           cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
           for (int i = threadIdx.x; i < kHBins; i += THREADS) {
             sc.hist[0][i] = 0;
@@ -753,8 +817,9 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     }
     // After the first block: cut to the exact top k so that later blocks
     // are filtered by the k-th composite.
-    if (base + kBlock < seg_end && cnt > k && !have_thr && cover == 0) {
-      const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
+    if (base + kBlock < seg_end && cnt > kk && !have_thr && cover == 0) {
+      const uint64_t t = select_k_lds<THREADS>(cand, cnt, kk, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
+      if (QUOTA) tc = max(tc, t);
       cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
       for (int i = threadIdx.x; i < kHBins; i += THREADS) {
         sc.hist[0][i] = 0;
@@ -794,15 +859,28 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
         (size_t)b * k, sorted_index, reinterpret_cast<uint32_t*>(cand + CAP), sc);
     return;
   }
-  // At most 2k candidates leave the segment.
-  if (cnt > 2 * k) {
-    const uint64_t t = select_k_lds<THREADS>(cand, cnt, k, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
+  // At most 2k candidates leave the segment (more are cut to exactly k); in
+  // quota form at most `slots` (more are cut to exactly that many).
+  if (cnt > out_cap) {
+    const uint64_t t = select_k_lds<THREADS>(cand, cnt, QUOTA ? out_cap : k, sc, (uint32_t)seg_start,
+                                             (uint32_t)(seg_end - seg_start));
     cnt = block_compact<THREADS, CAP / THREADS>(cand, cnt, t, sc);
+    if (QUOTA) tc = max(tc, t);
   }
-  cnt = min(cnt, 2 * k);
-  uint64_t* out = cand_out + ((size_t)b * segs + sidx) * (size_t)(2 * k);
-  for (int i = threadIdx.x; i < cnt; i += THREADS) out[i] = cand[i];
-  if (threadIdx.x == 0) cnt_out[(size_t)b * segs + sidx] = (uint32_t)cnt;
+  cnt = min(cnt, out_cap);
+  // Quota form: composites leave with row positions (the map keeps the
+  // order of a segment's positions, so every comparison inside the segment,
+  // the cut's included, comes out the same).
+  auto to_row = [&](uint64_t x) -> uint64_t {
+    if (!QUOTA || (uint32_t)x == 0u) return x;  // a value bound carries no position
+    return (x & 0xFFFFFFFF00000000ull) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row_pos(composite_pos(x)));
+  };
+  uint64_t* out = cand_out + ((size_t)b * segs + sidx) * (size_t)out_cap;
+  for (int i = threadIdx.x; i < cnt; i += THREADS) out[i] = to_row(cand[i]);
+  if (threadIdx.x == 0) {
+    cnt_out[(size_t)b * segs + sidx] = (uint32_t)cnt;
+    if (QUOTA) tcut_out[(size_t)b * segs + sidx] = to_row(tc);
+  }
 }
 
 // The winners (entries >= thr, exactly k of them, or all cnt <= k) of an
@@ -890,17 +968,25 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
   uint64_t v[kPer];
   uint64_t thr;
   uint32_t pos, nkeep;
-  if (!merge_candidates<kPer, CUT>(cand_in + (size_t)b * segs * slots, cnt_in + (size_t)b * segs,
-                                   CUT ? tcut_in + (size_t)b * segs : nullptr, segs, slots, k, sc,
-                                   v, thr, pos, nkeep)) {
-    int32_t* oi = out_idx + (size_t)b * k;
-    row_topk_from_scores(reinterpret_cast<const float*>(scores) + (size_t)b * N, N, k,
-                         [oi](uint32_t at, int i) { oi[at] = i; }, sc);
-    return;
-  }
   int32_t* oi = out_idx + (size_t)b * k;
   const size_t esz = BF16 ? 2 : 4;
   const char* row = reinterpret_cast<const char*>(scores) + (size_t)b * (size_t)N * esz;
+  if (!merge_candidates<kPer, CUT>(cand_in + (size_t)b * segs * slots, cnt_in + (size_t)b * segs,
+                                   CUT ? tcut_in + (size_t)b * segs : nullptr, segs, slots, k, sc,
+                                   v, thr, pos, nkeep)) {
+    // The row again from its scores; winners come in ascending position
+    // order, which is also the sorted-by-index order.
+    row_topk_from_scores<BF16>(row, N, k,
+                               [oi, out_val, row, b, k](uint32_t at, int i) {
+                                 oi[at] = i;
+                                 if (out_val) {
+                                   if (BF16) reinterpret_cast<uint16_t*>(out_val)[(size_t)b * k + at] = reinterpret_cast<const uint16_t*>(row)[i];
+                                   else reinterpret_cast<uint32_t*>(out_val)[(size_t)b * k + at] = reinterpret_cast<const uint32_t*>(row)[i];
+                                 }
+                               },
+                               sc);
+    return;
+  }
   if (!sorted_index) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -963,42 +1049,51 @@ hipError_t allow_lds(K kernel, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <bool BF16, bool AL, int V, int THREADS, bool FUSED>
-hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
-                      uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
-                      const int32_t* lengths, hipStream_t st) {
+// Stage-1 launch state: the workspace lists and the launch's options.
+struct Stage1Args {
+  uint64_t* cand;
+  uint32_t* cnt;
+  uint64_t* tcut;  // quota form only
+  int32_t* out_idx;
+  void* out_val;
+  int sorted_index;
+  const int32_t* lengths;
+};
+
+template <bool BF16, bool AL, int V, int THREADS, bool FUSED, bool QUOTA>
+hipError_t launch_seg(const void* scores, int B, int N, int k, const TopkPlan& p, const Stage1Args& a,
+                      hipStream_t st) {
   int P = 1;
   while (P < k) P <<= 1;
   const size_t lds = (size_t)seg_cap<THREADS>() * sizeof(uint64_t) + (FUSED ? (size_t)P * sizeof(uint32_t) : 0);
-  auto kern = topk_segment_kernel<BF16, AL, V, THREADS, FUSED>;
+  auto kern = topk_segment_kernel<BF16, AL, V, THREADS, FUSED, QUOTA>;
   hipError_t e = allow_lds(kern, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(p.segs, B), dim3(THREADS), lds, st, scores, N, k, p.seg_len, p.segs,
-                     cand, cnt, out_idx, out_val, sorted_index, lengths);
+                     a.cand, a.cnt, a.out_idx, a.out_val, a.sorted_index, a.lengths, p.quota, p.slots,
+                     a.tcut);
   return hipGetLastError();
 }
 
-template <bool BF16, bool AL, int THREADS, bool FUSED>
-hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
-                        uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
-                        const int32_t* lengths, hipStream_t st) {
+template <bool BF16, bool AL, int THREADS, bool FUSED, bool QUOTA>
+hipError_t launch_seg_v(const void* scores, int B, int N, int k, const TopkPlan& p, const Stage1Args& a,
+                        hipStream_t st) {
   switch (p.vec) {
-    case 1: return launch_seg<BF16, AL, 1, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
-    case 2: return launch_seg<BF16, AL, 2, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
-    case 4: return launch_seg<BF16, AL, 4, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
-    default: return launch_seg<BF16, AL, 8, THREADS, FUSED>(scores, B, N, k, p, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
+    case 1: return launch_seg<BF16, AL, 1, THREADS, FUSED, QUOTA>(scores, B, N, k, p, a, st);
+    case 2: return launch_seg<BF16, AL, 2, THREADS, FUSED, QUOTA>(scores, B, N, k, p, a, st);
+    case 4: return launch_seg<BF16, AL, 4, THREADS, FUSED, QUOTA>(scores, B, N, k, p, a, st);
+    default: return launch_seg<BF16, AL, 8, THREADS, FUSED, QUOTA>(scores, B, N, k, p, a, st);
   }
 }
 
 template <bool BF16, bool AL>
-hipError_t launch_stage1(const void* scores, int B, int N, int k, const TopkPlan& p, uint64_t* cand,
-                         uint32_t* cnt, int32_t* out_idx, void* out_val, int sorted_index,
-                         const int32_t* lengths, hipStream_t st) {
-  if (p.fused)
-    return launch_seg_v<BF16, AL, kRowThreads, true>(scores, B, N, k, p, cand, cnt, out_idx, out_val,
-                                                     sorted_index, lengths, st);
-  return launch_seg_v<BF16, AL, kTkThreads, false>(scores, B, N, k, p, cand, cnt, out_idx, out_val,
-                                                   sorted_index, lengths, st);
+hipError_t launch_stage1(const void* scores, int B, int N, int k, const TopkPlan& p, const Stage1Args& a,
+                         bool quota, hipStream_t st) {
+  if (p.fused) return launch_seg_v<BF16, AL, kRowThreads, true, false>(scores, B, N, k, p, a, st);
+  if constexpr (AL) {
+    if (quota) return launch_seg_v<BF16, AL, kTkThreads, false, true>(scores, B, N, k, p, a, st);
+  }
+  return launch_seg_v<BF16, AL, kTkThreads, false, false>(scores, B, N, k, p, a, st);
 }
 
 }  // namespace
@@ -1043,46 +1138,86 @@ TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
   p.vec = v;
   p.segs = (int)segs;
   p.seg_len = (int)seg_len;
+  // Quota form: segment s keeps about its share of the row's top k, the
+  // share's mean plus four standard deviations of a random row's spread
+  // plus 17 (the indexer's chunk cut uses the same margin), in twice that
+  // many slots, so the group-maxima threshold (which admits a little more
+  // than the count it is set for) rarely needs an exact cut. It needs a
+  // power-of-two segment count and slots within the lists' 2k stride, and a
+  // segment of at most 65536 positions keeps the tie select's position
+  // bitmap. It pays with four or more segments (the merge's candidates
+  // shrink: bf16 64 x 131072, k = 512: 15.9 -> 14.6 us) or segments of
+  // several register blocks (fewer exact cuts: float32 128 x 129280,
+  // k = 1024: 37.3 -> 36.4 us); two one-block segments per row gain nothing
+  // in the merge and were 0.2-0.6 us slower (float32 16-64 x 32768,
+  // k = 1024), so they keep every segment's top k.
+  p.quota = 0;
+  p.slots = 2 * k;
+  const bool one_block = seg_len <= (long long)kTkThreads * kTkMaxVec * E;
+  if (segs >= 2 && (segs & (segs - 1)) == 0 && (segs >= 4 || !one_block)) {
+    const double share = (double)k / (double)segs;
+    const int quota = (int)ceil(share + 4.0 * sqrt(share) + 17.0);
+    const int slots = (2 * quota + 7) / 8 * 8;
+    const int log_s = __builtin_ctzll((unsigned long long)segs), log_p = dt == DSA_BF16 ? 6 : 5;
+    int64_t longest = 0;
+    for (int sg = 0; sg < (int)segs; ++sg) longest = std::max(longest, piece_seg_len(N, sg, log_s, log_p));
+    if (slots <= 2 * k && quota < k && longest <= 65536) {
+      p.quota = quota;
+      p.slots = slots;
+    }
+  }
   p.cand_off = 0;
   p.cnt_off = align_up((size_t)B * p.segs * (size_t)(2 * k) * sizeof(uint64_t), 256);
-  p.bytes = align_up(p.cnt_off + (size_t)B * p.segs * sizeof(uint32_t), 256);
+  p.tcut_off = align_up(p.cnt_off + (size_t)B * p.segs * sizeof(uint32_t), 256);
+  p.bytes = align_up(p.tcut_off + (size_t)(p.quota ? B * p.segs : 0) * sizeof(uint64_t), 256);
   return p;
 }
 
 hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
                        int32_t* out_idx, void* out_val, int sorted_index, const int32_t* lengths,
                        const TopkPlan& plan, void* ws, hipStream_t st) {
-  uint64_t* cand = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(ws) + plan.cand_off);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + plan.cnt_off);
+  char* base = reinterpret_cast<char*>(ws);
+  uint64_t* cand = reinterpret_cast<uint64_t*>(base + plan.cand_off);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(base + plan.cnt_off);
+  uint64_t* tcut = plan.quota ? reinterpret_cast<uint64_t*>(base + plan.tcut_off) : nullptr;
   const bool bf16 = dt == DSA_BF16;
   const int E = bf16 ? 8 : 4;
   const bool aligned = (N % E) == 0 && (reinterpret_cast<uintptr_t>(scores) % 16) == 0;
+  // The quota form takes full, aligned rows; ragged or unaligned ones keep
+  // every segment's top k.
+  const bool quota = !plan.fused && plan.quota > 0 && lengths == nullptr && aligned;
+  const Stage1Args a{cand, cnt, tcut, out_idx, out_val, sorted_index, lengths};
   hipError_t e;
-  if (bf16) e = aligned ? launch_stage1<true, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st)
-                        : launch_stage1<true, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
-  else e = aligned ? launch_stage1<false, true>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st)
-                   : launch_stage1<false, false>(scores, B, N, k, plan, cand, cnt, out_idx, out_val, sorted_index, lengths, st);
+  if (bf16) e = aligned ? launch_stage1<true, true>(scores, B, N, k, plan, a, quota, st)
+                        : launch_stage1<true, false>(scores, B, N, k, plan, a, quota, st);
+  else e = aligned ? launch_stage1<false, true>(scores, B, N, k, plan, a, quota, st)
+                   : launch_stage1<false, false>(scores, B, N, k, plan, a, quota, st);
   if (e != hipSuccess || plan.fused) return e;
   int P = 1;
   while (P < k) P <<= 1;
   const size_t merge_lds = (size_t)P * sizeof(uint32_t);
-  const int slots = plan.segs * 2 * k;
+  const int stride = quota ? plan.slots : 2 * k;  // slots per segment list
+  const int slots = plan.segs * stride;
   const int per = slots <= 512 * 4 ? 4 : slots <= 512 * 8 ? 8 : slots <= 512 * 16 ? 16 : 32;
-#define DSA_MERGE(BF, PER)                                                                      \
+#define DSA_MERGE(BF, PER, CUT)                                                                 \
   do {                                                                                          \
-    e = allow_lds(topk_merge_kernel<BF, PER>, merge_lds);                                       \
+    e = allow_lds(topk_merge_kernel<BF, PER, CUT>, merge_lds);                                  \
     if (e != hipSuccess) return e;                                                              \
-    hipLaunchKernelGGL((topk_merge_kernel<BF, PER>), dim3(B), dim3(kMergeThreads), merge_lds, st, \
-                       scores, N, k, plan.segs, 2 * k, cand, cnt, nullptr, out_idx, out_val,     \
-                       sorted_index);                                                           \
+    hipLaunchKernelGGL((topk_merge_kernel<BF, PER, CUT>), dim3(B), dim3(kMergeThreads), merge_lds, \
+                       st, scores, N, k, plan.segs, stride, cand, cnt, CUT ? tcut : nullptr,    \
+                       out_idx, out_val, sorted_index);                                         \
+  } while (0)
+#define DSA_MERGE_PER(BF, CUT)                                                                  \
+  do {                                                                                          \
+    if (per == 4) DSA_MERGE(BF, 4, CUT); else if (per == 8) DSA_MERGE(BF, 8, CUT);              \
+    else if (per == 16) DSA_MERGE(BF, 16, CUT); else DSA_MERGE(BF, 32, CUT);                    \
   } while (0)
   if (bf16) {
-    if (per == 4) DSA_MERGE(true, 4); else if (per == 8) DSA_MERGE(true, 8);
-    else if (per == 16) DSA_MERGE(true, 16); else DSA_MERGE(true, 32);
+    if (quota) DSA_MERGE_PER(true, true); else DSA_MERGE_PER(true, false);
   } else {
-    if (per == 4) DSA_MERGE(false, 4); else if (per == 8) DSA_MERGE(false, 8);
-    else if (per == 16) DSA_MERGE(false, 16); else DSA_MERGE(false, 32);
+    if (quota) DSA_MERGE_PER(false, true); else DSA_MERGE_PER(false, false);
   }
+#undef DSA_MERGE_PER
 #undef DSA_MERGE
   return hipGetLastError();
 }

@@ -162,3 +162,61 @@ def test_deterministic_and_workspace_contents_do_not_matter():
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(b, c)
     assert torch.equal(av, bv)
+
+
+def _segment_zero_positions(N: int, segs: int, piece: int) -> torch.Tensor:
+    """Positions of the pieces that the rotating interleave gives segment 0:
+    piece g (of `piece` scores) sits in run g // segs at slot g % segs, and
+    segment s owns slot (s + run) mod segs."""
+    g = torch.arange((N + piece - 1) // piece, device=DEV)
+    mine = g[(g % segs - g // segs) % segs == 0]
+    pos = (mine[:, None] * piece + torch.arange(piece, device=DEV)[None, :]).reshape(-1)
+    return pos[pos < N]
+
+
+# (N, k, segments, quota) of full rows split for the quota form at B = 3:
+# 8 one-block segments keeping 113 each of k = 512, and 2 segments of
+# several blocks keeping 2246 each of k = 4096.
+QUOTA_SHAPES = [(131072, 512, 8, 113), (131072, 4096, 2, 2246)]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N,k,segs,quota", QUOTA_SHAPES)
+def test_rows_whose_top_k_sits_in_one_segment(dtype, N, k, segs, quota):
+    # Full rows split into a power-of-two number of segments keep only about
+    # their share of the top k each. Rows 0 and 2 put every large score into
+    # the pieces of one segment, so that segment drops scores of the row's top
+    # k: the merge must see it through the cuts and select those rows again
+    # from their scores. Row 1 is random (settled by the segments' quotas).
+    B = 3
+    piece = 64 if dtype == torch.bfloat16 else 32
+    g = torch.Generator(device=DEV).manual_seed(41)
+    x = torch.randn((B, N), generator=g, device=DEV)
+    pos = _segment_zero_positions(N, segs, piece)
+    x[0, pos] += 100.0
+    # row 2: ties on the boosted level, so the fallback also breaks ties
+    x[2, pos] = 7.0
+    x = x.to(dtype)
+    run_case(x, k, where=f"top k in one segment N={N}")
+    run_case(x, k, values=True, where=f"top k in one segment N={N}, values")
+    idx = run_case(x, k, sorted_index=True, values=True, where=f"top k in one segment N={N}, sorted")
+    assert idx[2].cpu().tolist() == pos[:k].cpu().tolist()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("N,k,segs,quota", QUOTA_SHAPES)
+def test_segment_quota_edges(dtype, N, k, segs, quota):
+    # quota, quota + 1 and 3.5 quota boosted scores in one segment's pieces,
+    # the rest of the row random: with its random share the segment holds
+    # more of the row's top k than its quota in every row, by a little or a
+    # lot; the results must be exact either way.
+    B = 3
+    piece = 64 if dtype == torch.bfloat16 else 32
+    g = torch.Generator(device=DEV).manual_seed(43)
+    x = torch.randn((B, N), generator=g, device=DEV)
+    pos = _segment_zero_positions(N, segs, piece)
+    for row, n in ((0, quota), (1, quota + 1), (2, min(k, 7 * quota // 2))):
+        x[row, pos[:n]] += 50.0
+    x = x.to(dtype)
+    run_case(x, k, values=True, where=f"segment quota edges N={N}")
+    run_case(x, k, sorted_index=True, where=f"segment quota edges N={N} sorted")

@@ -33,6 +33,16 @@
 // time with exact selects in between. At most 2k candidates leave the
 // segment; more are first cut to exactly k.
 //
+// Quota form (full rows in a power-of-two number of segments): a segment
+// only has to pass on its part of the row's top k, about k/S. It takes
+// interleaved 128-byte pieces of the row (so a sorted row spreads its top k
+// over all segments), runs everything above with a quota q (about k/S plus
+// four standard deviations of a random row's spread) in place of k, keeps at
+// most 2q candidates, and reports its cut: every composite it dropped lies
+// below it. Stage 2 checks that no cut reaches the row's k-th kept
+// composite, which makes the kept set exact, and otherwise selects the row
+// again from its scores.
+//
 // Stage 2, one workgroup per row: load every segment's candidates into
 // registers at once, select the row's k-th composite exactly, and write the
 // k winners (indices, optional value copies), in buffer order or sorted by

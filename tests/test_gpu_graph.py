@@ -110,3 +110,44 @@ def test_captured_step_replays_equal_eager(variant, si):
         assert _same(out, ref_out), f"replay {rep}: output differs from the eager call"
         say(f"    replay {rep}: equal to eager")
     del g
+
+
+# Full rows of these shapes take the top-k's quota form (segment cuts in the
+# workspace, checked by the merge).
+TOPK_SHAPES = [(16, 131072, 512, torch.bfloat16, False, False),
+               (8, 129280, 1024, torch.float32, True, True)]
+
+
+@pytest.mark.parametrize("ti", range(len(TOPK_SHAPES)))
+def test_captured_topk_replays_equal_eager(ti):
+    import indexer_top_gathered_amd as dsa
+    B, N, k, dt, values, sorted_index = TOPK_SHAPES[ti]
+    say(f"[graph] topk B={B} N={N} k={k} dtype={dt} values={values} sorted={sorted_index}")
+    tag = "bf16" if dt == torch.bfloat16 else "f32"
+    x = workloads.normal_rows(B, N, tag, 9500 + ti, device=DEV)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    val = torch.empty((B, k), dtype=dt, device=DEV) if values else None
+    ws = torch.empty(max(dsa.dsa_topk_workspace_bytes(B, N, k, dt), 256), dtype=torch.uint8, device=DEV)
+
+    def call(o, v, w):
+        dsa.dsa_topk(x, k, return_values=values, sorted_index=sorted_index, out_idx=o, out_val=v, ws=w)
+
+    g = _capture(lambda: call(idx, val, ws))
+    ref_idx = torch.empty_like(idx)
+    ref_val = torch.empty_like(val) if values else None
+    ref_ws = torch.empty_like(ws)
+    for rep in range(3):
+        fresh = workloads.normal_rows(B, N, tag, 9600 + 10 * ti + rep, device=DEV)
+        if rep == 2:  # a row whose top k sits in few segments: the merge's fallback
+            fresh[0, : 4 * k] += 50.0
+        x.copy_(fresh)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        call(ref_idx, ref_val, ref_ws)  # eager, on the same inputs
+        torch.cuda.synchronize()
+        assert _same(idx, ref_idx), f"replay {rep}: indices differ from the eager call"
+        if values:
+            assert _same(val, ref_val), f"replay {rep}: values differ from the eager call"
+        say(f"    replay {rep}: equal to eager")
+    del g

@@ -704,8 +704,9 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       // than k groups the threshold would admit the whole block. (With
       // k <= 4096 and 512 threads, 2k groups take at most 4E per thread for
       // float32 and 2E for bf16.) bf16 segments in quota form take about 4k
-      // groups: a finer threshold on rows of tied levels (bf16 stress rows 34.7 -> 28.8 us; float32 rows,
-      // which would need the split, were 1 us slower with it).
+      // groups: a finer threshold on rows of tied levels (bf16 stress rows
+      // 34.7 -> 28.8 us; float32 rows, which would need the split, were 1 us
+      // slower with it).
       const int gpt = ((BF16 && QUOTA ? 4 : 2) * kk + THREADS - 1) / THREADS;  // wanted groups per thread
       if constexpr (!BF16 && V >= 4) {
         if (gpt > 2 * E) return split_threshold(std::integral_constant<int, 4>{});  // uniform

@@ -236,6 +236,21 @@ __device__ __forceinline__ uint32_t f32_raw_key(uint32_t bits) {
 }
 __device__ __forceinline__ uint32_t canon32(uint32_t k) { return k == 0x7FFFFFFFu ? 0x80000000u : k; }
 
+// The raw score bits of a winner, from its composite's value key (the
+// inverse of the order key) without reading the row again. Only a zero
+// score is read back: the key merged -0 into +0.
+template <bool BF16>
+__device__ __forceinline__ uint32_t winner_bits(uint64_t c, const char* row, uint32_t p) {
+  const uint32_t key = (uint32_t)(c >> 32);
+  if (key == 0x80000000u)
+    return BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(row)[p] : reinterpret_cast<const uint32_t*>(row)[p];
+  if (BF16) {
+    const uint32_t k16 = key >> 16;
+    return k16 >= 0x8000u ? (k16 & 0x7FFFu) : (~k16 & 0xFFFFu);
+  }
+  return key >= 0x80000000u ? (key & 0x7FFFFFFFu) : ~key;
+}
+
 template <bool BF16>
 __device__ __forceinline__ uint32_t elem_key32(const u32x4& kv, int e) {
   if (BF16) {
@@ -603,6 +618,9 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
   // segment no longer sets it from its lowest block), and the following
   // blocks it covers are admitted against it with no threshold of their own.
   int cover = 0;        // following blocks the first block's threshold covers
+  // QUOTA: the first threshold was extended over every block of the segment
+  // (no exact cut after the blocks it was taken on; see below).
+  bool extended = false;
   uint32_t pair_t = 0;  // that threshold (raw key)
 
   // Register blocks of THREADS*V*E scores. The first block sets a threshold
@@ -750,7 +768,9 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
       if (t0 == (BF16 ? 0x8000u : 0x80000000u)) t0 -= 1;
       t0 = max(t0, t_floor);
     } else if (cover > 0) {
-      t0 = pair_t;  // the first block's threshold holds for this block too
+      // The first block's threshold holds for this block too (raised by a
+      // later block's own threshold, if one was taken).
+      t0 = max(pair_t, t_floor);
       --cover;
     } else {
       t0 = block_threshold();
@@ -765,7 +785,7 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     uint64_t adm = admit_block(t0);
     uint32_t total;
     uint32_t excl = block_exclusive_scan<THREADS>((uint32_t)__popcll(adm), &total, sc);
-    if (__builtin_expect(have_thr && cnt + (int)total > CAP, 0)) {
+    if (__builtin_expect((have_thr || extended) && cnt + (int)total > CAP, 0)) {
       // A later block that beats the running threshold almost everywhere
       // (a row rising along the segment): its own group maxima give a
       // higher bound, and the segment's k-th largest is at least that.
@@ -828,6 +848,19 @@ __global__ __launch_bounds__(THREADS) void topk_segment_kernel(
     }
     // After the first block: cut to the exact top k so that later blocks
     // are filtered by the k-th composite.
+    // Quota form: when the candidates listed so far, scaled to the whole
+    // segment, still fit the output slots, the first threshold is kept for
+    // the remaining blocks instead (it is a bound for the segment: at least
+    // kk of the blocks it was taken on reach it), which saves the exact cut;
+    // the final cut to the slots runs only if the list outgrows them.
+    if (QUOTA && !have_thr && cover == 0 && !extended && base + kBlock < seg_end) {
+      const int64_t done = (base - seg_start) / kBlock + 1;
+      const int64_t all = (seg_end - seg_start + kBlock - 1) / kBlock;
+      if ((int64_t)cnt * all <= (int64_t)out_cap * done) {  // uniform
+        cover = (int)(all - done);
+        extended = true;
+      }
+    }
     if (base + kBlock < seg_end && cnt > kk && !have_thr && cover == 0) {
       const uint64_t t = select_k_lds<THREADS>(cand, cnt, kk, sc, (uint32_t)seg_start, (uint32_t)(seg_end - seg_start));
       if (QUOTA) tc = max(tc, t);
@@ -923,8 +956,9 @@ __device__ void write_winners_from_lds(const uint64_t* cand, int cnt, uint64_t t
         const uint32_t p = min(composite_pos(v[j]), (uint32_t)(N - 1));
         oi[pos] = (int32_t)p;
         if (out_val) {
-          if (BF16) reinterpret_cast<uint16_t*>(out_val)[out_off + pos] = reinterpret_cast<const uint16_t*>(row)[p];
-          else reinterpret_cast<uint32_t*>(out_val)[out_off + pos] = reinterpret_cast<const uint32_t*>(row)[p];
+          const uint32_t bits = winner_bits<BF16>(v[j], row, p);
+          if (BF16) reinterpret_cast<uint16_t*>(out_val)[out_off + pos] = (uint16_t)bits;
+          else reinterpret_cast<uint32_t*>(out_val)[out_off + pos] = bits;
         }
         ++pos;
       }
@@ -1005,8 +1039,9 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(
         const uint32_t p = min(composite_pos(v[j]), (uint32_t)(N - 1));
         oi[pos] = (int32_t)p;
         if (out_val) {
-          if (BF16) reinterpret_cast<uint16_t*>(out_val)[(size_t)b * k + pos] = reinterpret_cast<const uint16_t*>(row)[p];
-          else reinterpret_cast<uint32_t*>(out_val)[(size_t)b * k + pos] = reinterpret_cast<const uint32_t*>(row)[p];
+          const uint32_t bits = winner_bits<BF16>(v[j], row, p);
+          if (BF16) reinterpret_cast<uint16_t*>(out_val)[(size_t)b * k + pos] = (uint16_t)bits;
+          else reinterpret_cast<uint32_t*>(out_val)[(size_t)b * k + pos] = bits;
         }
         ++pos;
       }
@@ -1168,7 +1203,14 @@ TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
   if (segs >= 2 && (segs & (segs - 1)) == 0 && (segs >= 4 || !one_block)) {
     const double share = (double)k / (double)segs;
     const int quota = (int)ceil(share + 4.0 * sqrt(share) + 17.0);
-    const int slots = (2 * quota + 7) / 8 * 8;
+    int slots = (2 * quota + 7) / 8 * 8;
+    // The merge holds 4, 8, 16 or 32 slots per thread: the lists take all
+    // of the slots that count gives them, so a segment cuts its list only
+    // when it outgrows that (stage 1 then skips exact cuts it would
+    // otherwise take; the merge's per-thread work is the same).
+    const long long need = segs * (long long)slots;
+    const int per = need <= kMergeThreads * 4 ? 4 : need <= kMergeThreads * 8 ? 8 : need <= kMergeThreads * 16 ? 16 : 32;
+    slots = std::max(slots, std::min(2 * k, (int)((long long)kMergeThreads * per / segs) / 8 * 8));
     const int log_s = __builtin_ctzll((unsigned long long)segs), log_p = dt == DSA_BF16 ? 6 : 5;
     int64_t longest = 0;
     for (int sg = 0; sg < (int)segs; ++sg) longest = std::max(longest, piece_seg_len(N, sg, log_s, log_p));

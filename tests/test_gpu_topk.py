@@ -82,6 +82,24 @@ def test_rising_and_falling_long_rows(dtype):
     run_case(rows, 777, sorted_index=True, where="rising/falling long rows sorted")
 
 
+@pytest.mark.parametrize("lift", [0.75, 10.0])
+def test_segments_outgrowing_their_first_threshold(lift):
+    # float32 rows of 262144 with k = 2048 take the quota form in 4 segments
+    # of 4 register blocks. A random first three blocks set the threshold
+    # and predict a list that fits the segment's slots, so the threshold is
+    # kept for the last block; lifting the last quarter of the row (most of
+    # each segment's last block) makes that block overflow the prediction
+    # (0.75: the final cut to the slots) or the whole LDS list (10: the
+    # block takes its own threshold).
+    N = 262144
+    g = torch.Generator(device=DEV).manual_seed(61)
+    x = torch.randn((3, N), generator=g, device=DEV)
+    x[:, 3 * N // 4:] += lift
+    x[2] = x[2].round(decimals=1)  # ties across the lifted and plain parts
+    run_case(x, 2048, values=True, where=f"last quarter lifted by {lift}")
+    run_case(x, 2048, sorted_index=True, where=f"last quarter lifted by {lift}, sorted")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_heavy_bucket_of_several_values(dtype):
     # A few huge scores stretch the candidates' range, so one histogram

@@ -61,7 +61,8 @@ __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
                                           const uint16_t* __restrict__ k,
                                           const float* __restrict__ w, float* __restrict__ s,
                                           int b, int N, int H, int start, int end, u32x4* st,
-                                          int c = 0, int C = 1, uint32_t* keep = nullptr) {
+                                          int c = 0, int C = 1, uint32_t* keep = nullptr,
+                                          uint32_t* key_lo = nullptr, uint32_t* key_hi = nullptr) {
   // The thread index passes through an empty asm statement, so that the
   // values derived from it are formed per call: a caller that sweeps
   // several rows in a loop does not keep them live across its iterations.
@@ -98,6 +99,8 @@ __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
 
   const uint16_t* krow = k + (size_t)b * N * kDI;
   float* srow = s + (size_t)b * N;
+  // CUT: the smallest and largest order key this lane wrote to keep[].
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 
   // Keys are loaded with whole 1 KB runs per instruction (4 keys x 256 B,
   // lane l: key 4j + l/16, 16-byte chunk l%16), then written to this wave's
@@ -153,7 +156,14 @@ __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
     if (g < 2) {
       const int key = key0 + g * 16 + m;
       if (key < end) srow[key] = mine;
-      if constexpr (CUT) keep[local0 + g * 16 + m] = key < end ? f32_key(__float_as_uint(mine)) : 0u;
+      if constexpr (CUT) {
+        const uint32_t kx = f32_key(__float_as_uint(mine));
+        keep[local0 + g * 16 + m] = key < end ? kx : 0u;
+        if (key < end) {
+          klo = min(klo, kx);
+          khi = max(khi, kx);
+        }
+      }
     }
   };
   // Three register buffers in turn: two steps of loads in flight while one
@@ -183,6 +193,10 @@ __device__ __forceinline__ void sweep_row(const uint16_t* __restrict__ q,
     if (i + 2 >= nsteps) break;
     if (i + 4 < nsteps) load_step(rb, key_at(i + 4));
     score_step(rc, key_at(i + 2), local_at(i + 2));
+  }
+  if constexpr (CUT) {  // the wave's key range, for the cut's histogram
+    *key_lo = wave_reduce<OpMin>(klo);
+    *key_hi = wave_reduce<OpMax>(khi);
   }
 }
 
@@ -359,6 +373,8 @@ __device__ __noinline__ void chunk_cut_exact(const uint32_t* keep, int M, int va
   uint32_t at = gt_before + min(need_eq, eq_before);
   uint64_t* out = cand + ((size_t)b * C + c) * KL;
   uint64_t least = ~(uint64_t)0;
+  int grp = i0 >> 5;  // the row offset of the group of 32 holding key i
+  int grp_row = chunk_group(c, C, grp) * kIsKeysPerStep;
   for (int i = i0; i < i1; ++i) {
     const uint32_t x = keep[i];
     if (x == 0u) continue;
@@ -369,8 +385,11 @@ __device__ __noinline__ void chunk_cut_exact(const uint32_t* keep, int M, int va
     }
     if (sel && at < (uint32_t)KL) {
       // local index i = 32 * (the group's rank in the chunk) + offset
-      const uint32_t pos = (uint32_t)(chunk_group(c, C, i >> 5) * kIsKeysPerStep + (i & 31));
-      const uint64_t cp = composite(x, pos);
+      if ((i >> 5) != grp) {
+        grp = i >> 5;
+        grp_row = chunk_group(c, C, grp) * kIsKeysPerStep;
+      }
+      const uint64_t cp = composite(x, (uint32_t)(grp_row + (i & 31)));
       out[at++] = cp;
       least = cp < least ? cp : least;
     }
@@ -392,30 +411,16 @@ __device__ __noinline__ void chunk_cut_exact(const uint32_t* keep, int M, int va
 // composite (every dropped composite lies below it). A chunk with at most
 // `cap` scores keeps them all (t_c = 0); when the edge would leave more than
 // `cap` (a heavy bucket of ties), the exact cut to `cap` takes over.
+// Expects the histogram clear and cs.wmin/wmax holding each wave's smallest
+// and largest key, behind a barrier.
 __device__ void chunk_cut(const uint32_t* keep, int M, int valid, int target, int cap, int b,
                           int c, int C, uint32_t* hist, CutScratch& cs,
                           uint64_t* __restrict__ cand, uint32_t* __restrict__ cnt,
                           uint64_t* __restrict__ tcut) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  for (int i = tid; i < kCutBins; i += kIsThreads) hist[i] = 0;
   uint32_t edge = 1;  // keys >= edge are kept (real keys are >= 1)
   if (valid > cap) {
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
-    for (int i = tid; i < M; i += kIsThreads) {
-      const uint32_t x = keep[i];
-      if (x) {
-        lo = min(lo, x);
-        hi = max(hi, x);
-      }
-    }
-    lo = wave_reduce<OpMin>(lo);
-    hi = wave_reduce<OpMax>(hi);
-    if (lane == 0) {
-      cs.wmin[wave] = lo;
-      cs.wmax[wave] = hi;
-    }
-    __syncthreads();  // also orders the histogram clearing
 #pragma unroll
     for (int w = 0; w < kIsWaves; ++w) {
       lo = min(lo, cs.wmin[w]);
@@ -452,11 +457,16 @@ __device__ void chunk_cut(const uint32_t* keep, int M, int valid, int target, in
   uint32_t total;
   uint32_t at = cut_scan(n, &total, cs);
   uint64_t* out = cand + ((size_t)b * C + c) * cap;
+  int grp = i0 >> 5;  // a thread's keys lie in one or two groups of 32: their row offset is kept
+  int grp_row = chunk_group(c, C, grp) * kIsKeysPerStep;
   for (int i = i0; i < i1; ++i) {
     const uint32_t x = keep[i];
     if (x >= edge && at < (uint32_t)cap) {
-      const uint32_t pos = (uint32_t)(chunk_group(c, C, i >> 5) * kIsKeysPerStep + (i & 31));
-      out[at++] = composite(x, pos);
+      if ((i >> 5) != grp) {
+        grp = i >> 5;
+        grp_row = chunk_group(c, C, grp) * kIsKeysPerStep;
+      }
+      out[at++] = composite(x, (uint32_t)(grp_row + (i & 31)));
     }
   }
   if (tid == 0) {
@@ -476,7 +486,21 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_cut_kernel(
   extern __shared__ uint32_t keep[];              // the chunk's order keys
   const int b = blockIdx.y;
   const int c = blockIdx.x;
-  sweep_row<MT, true>(q, k, w, s, b, N, H, 0, N, stage_lds[threadIdx.x / kWave], c, C, keep);
+  uint32_t klo, khi;
+  sweep_row<MT, true>(q, k, w, s, b, N, H, 0, N, stage_lds[threadIdx.x / kWave], c, C, keep, &klo,
+                      &khi);
+  // Each wave's key range goes to LDS, and wave 0 clears its staging area
+  // (its own LDS operations run in order), which the cut's histogram takes,
+  // before the barrier that ends the sweep.
+  const int wave = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    cs.wmin[wave] = klo;
+    cs.wmax[wave] = khi;
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 32 * 16 / kWave; ++i) stage_lds[0][i * kWave + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+  }
   const int groups = (N + kIsKeysPerStep - 1) / kIsKeysPerStep;
   const int M = chunk_group_count(c, C, groups) * kIsKeysPerStep;
   // The row's last group may be partial: it is group (groups-1) mod C of
@@ -484,7 +508,7 @@ __global__ __launch_bounds__(kIsThreads) void indexer_score_cut_kernel(
   const int lastL = (groups - 1) / C;
   const int owner = (((groups - 1) % C - lastL) % C + C) % C;
   const int valid = M - (c == owner ? groups * kIsKeysPerStep - N : 0);
-  __syncthreads();  // every key is in keep[]; the staging area is free
+  __syncthreads();  // every key is in keep[], the key ranges and the clear histogram are in place
   chunk_cut(keep, M, valid, target, cap, b, c, C, reinterpret_cast<uint32_t*>(&stage_lds[0][0]),
             cs, cand, cnt, tcut);
 }

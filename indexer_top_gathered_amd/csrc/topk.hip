@@ -1204,13 +1204,18 @@ TopkPlan plan_topk(int B, int N, int k, dsa_dtype_t dt) {
     const double share = (double)k / (double)segs;
     const int quota = (int)ceil(share + 4.0 * sqrt(share) + 17.0);
     int slots = (2 * quota + 7) / 8 * 8;
-    // The merge holds 4, 8, 16 or 32 slots per thread: the lists take all
-    // of the slots that count gives them, so a segment cuts its list only
-    // when it outgrows that (stage 1 then skips exact cuts it would
-    // otherwise take; the merge's per-thread work is the same).
-    const long long need = segs * (long long)slots;
-    const int per = need <= kMergeThreads * 4 ? 4 : need <= kMergeThreads * 8 ? 8 : need <= kMergeThreads * 16 ? 16 : 32;
-    slots = std::max(slots, std::min(2 * k, (int)((long long)kMergeThreads * per / segs) / 8 * 8));
+    // The merge holds 4, 8, 16 or 32 slots per thread: segments of three or
+    // more blocks take all of the slots that count gives them, so they cut
+    // their lists only when these outgrow that (stage 1 then skips the exact
+    // cut it would otherwise take after its first blocks; the merge's
+    // per-thread work is the same). Shorter segments take no such cut and
+    // keep 2q (the larger lists cost the bf16 64 x 131072 rows 0.15 us and
+    // the bf16 stress rows 0.1 us in the merge's loads).
+    if (seg_len > 2LL * kTkThreads * v * E) {
+      const long long need = segs * (long long)slots;
+      const int per = need <= kMergeThreads * 4 ? 4 : need <= kMergeThreads * 8 ? 8 : need <= kMergeThreads * 16 ? 16 : 32;
+      slots = std::max(slots, std::min(2 * k, (int)((long long)kMergeThreads * per / segs) / 8 * 8));
+    }
     const int log_s = __builtin_ctzll((unsigned long long)segs), log_p = dt == DSA_BF16 ? 6 : 5;
     int64_t longest = 0;
     for (int sg = 0; sg < (int)segs; ++sg) longest = std::max(longest, piece_seg_len(N, sg, log_s, log_p));

@@ -260,7 +260,8 @@ hipError_t launch_topk(const void* scores, dsa_dtype_t dt, int B, int N, int k,
 
 struct AttendPlan {
   int splits;        // row splits per (batch, head group)
-  int rows_per_split;
+  int rows_per_split; // the most rows any split holds (its row list in LDS)
+  int sel_rows;       // selected rows per split (a multiple of 32; the last split may hold fewer)
   int heads_per_wg;  // 16 * waves per workgroup
   size_t part_o_off; // fp16 [B, splits, Hq, D]: O / scale of its dim half
   size_t part_ml_off; // float4 [B, splits, Hq]: (running max, running sum, scale of dims

@@ -8,7 +8,8 @@
 //   out[b,h,:] = softmax_r(scale * q[b,h,:] . R_b[r,:]) @ R_b
 //
 // Each workgroup takes one batch row, a group of 16*HG query heads and a
-// contiguous split of the rows; each 16-head group is served by DSPLIT waves
+// split of the rows (a share of the selected rows, and on some splits first a
+// tile of the window); each 16-head group is served by DSPLIT waves
 // that own 1/DSPLIT of the head dims each (they add up their halves of the
 // logits through LDS). Rows are copied 32 at a time from HBM straight into
 // LDS (row-major, padded), and each staged row is used twice:
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ win,
     uint16_t* __restrict__ out, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
     const float* __restrict__ sink, int N, int k, int W, int Hq, float scale,
-    int rows_per_split, int splits, int nitems, int hgroups, int tokens, SelectArgs sel) {
+    int rows_per_split, int sel_rows, int splits, int nitems, int hgroups, int tokens,
+    SelectArgs sel) {
   static_assert(SEL == 0 || HG * DSPLIT * kWave == kMergeThreads,
                 "the selection runs on kMergeThreads threads");
   constexpr int WAVES = HG * DSPLIT;
@@ -98,12 +100,41 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   const int dh = wave / HG;
   const int h = hg * HW + hq * 16 + m;  // the head this lane owns
   const int dbase = dh * DW;
-  const int rows = k + W;
-  const int r0 = split * rows_per_split;
-  const int r1 = min(rows, r0 + rows_per_split);
-
-  const int ntiles = (r1 - r0 + kTile - 1) / kTile;
+  // This split's rows, in local order: first its tiles of the window (the
+  // window's tiles are dealt round robin to the splits, starting after the
+  // last split that holds selected rows), then its share of the k selected
+  // rows, sel_rows per split in selection order. Slots past the window or
+  // past k are empty. A split that starts with a window tile can copy it
+  // before its selected rows are known.
+  const int tiles_sel = (k + kTile - 1) / kTile;
+  const int tps = sel_rows / kTile;                   // selected tiles per split
+  const int s_sel = (tiles_sel + tps - 1) / tps;      // splits that hold selected rows
+  const int nwt = (W + kTile - 1) / kTile;            // window tiles
+  const int j0 = ((split - s_sel) % splits + splits) % splits;  // this split's first window tile
+  const int wt = j0 < nwt ? (nwt - 1 - j0) / splits + 1 : 0;
+  const int wrows = wt * kTile;
+  const int sbase = split * sel_rows;
+  const int nsel = max(0, min(k, sbase + sel_rows) - sbase);
+  const int ntiles = wt + (nsel + kTile - 1) / kTile;
+  const int r0 = 0, r1 = ntiles * kTile;  // local rows; every tile is full, empty slots are masked
+  const bool has_pad = nsel % kTile != 0 || (wt > 0 && (j0 + (wt - 1) * splits + 1) * kTile > W);
+  // Encoded source of local window row i (< wrows): -(j+1) for window row j,
+  // kEmpty past the window.
+  auto win_enc = [&](int i) -> int {
+    const int j = (j0 + (i / kTile) * splits) * kTile + (i % kTile);
+    return j < W ? -j - 1 : kEmpty;
+  };
   const int32_t* irow = SEL == 0 ? idx + (size_t)b * k : nullptr;  // with SEL, idx is unused
+  // SEL == 0: the encoded source of local row i: >= 0 a compressed row
+  // (indices >= N clamped), kEmpty an empty slot, other negatives window
+  // row -(v+1).
+  auto src_enc = [&](int i) -> int {
+    if (i < wrows) return win_enc(i);
+    const int r = sbase + (i - wrows);
+    if (r >= sbase + nsel) return kEmpty;
+    const int v = irow[r];
+    return v < 0 ? kEmpty : (v >= N ? N - 1 : v);
+  };
   // Query row b is token b % tokens of batch row b / tokens, whose
   // compressed rows it gathers from.
   const uint16_t* kvb = kv + (size_t)(b / tokens) * N * D;
@@ -121,10 +152,7 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile)
 #pragma unroll
-      for (int i = 0; i < kRowsPerWave; ++i) {
-        const int r = min(r0 + tile * kTile + wv * kRowsPerWave + i, r1 - 1);
-        vr[tile][i] = irow[min(r, k - 1)];
-      }
+      for (int i = 0; i < kRowsPerWave; ++i) vr[tile][i] = src_enc(min(tile * kTile + wv * kRowsPerWave + i, r1 - 1));
     const uint32_t rbase = lds_byte_addr(Rbuf);  // tile slot j starts at rbase + j*kTile*ROW_WORDS*4
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
@@ -132,9 +160,9 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
           const int rr = wv * kRowsPerWave + i;
-          const int r = min(r0 + tile * kTile + rr, r1 - 1);
-          const int v = vr[tile][i] < 0 ? 0 : (vr[tile][i] >= N ? N - 1 : vr[tile][i]);
-          const uint16_t* src = r < k ? kvb + (size_t)v * D : winb + (size_t)(r - k) * D;
+          const int v = vr[tile][i];
+          // An empty slot copies row 0 (finite data; its weight is zero).
+          const uint16_t* src = v >= 0 ? kvb + (size_t)v * D : (v == kEmpty ? kvb : winb + (size_t)(-v - 1) * D);
           const uint32_t at = __builtin_amdgcn_readfirstlane(
               rbase + (uint32_t)((tile * kTile + rr) * ROW_WORDS * 4));
           if (ROW_LANES == kWave || lane < ROW_LANES) dma_row16(src + (lane % ROW_LANES) * 8, at);
@@ -154,25 +182,41 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
   // -(v+1). Each wave notes whether it met an empty slot.
   if constexpr (SEL == 0) {
     bool saw_empty = false;
-    for (int r = r0 + tid; r < r1; r += THREADS) {
-      int v;
-      if (r < k) {
-        v = irow[r];
-        saw_empty |= v < 0;
-        v = v < 0 ? kEmpty : (v >= N ? N - 1 : v);  // indices >= N are clamped
-      } else {
-        v = -(r - k) - 1;
-      }
-      srow[r - r0] = v;
+    for (int i = tid; i < r1; i += THREADS) {
+      const int v = src_enc(i);
+      saw_empty |= v == kEmpty;
+      srow[i] = v;
     }
     const bool wave_saw_empty = __ballot(saw_empty) != 0;  // all lanes take part
     if (lane == 0) wempty[wave] = wave_saw_empty ? 1 : 0;
   } else {
-    // The selection, in the tile slots before any copy goes out (the q
-    // loads above are in flight meanwhile). Winner number pos (in the cut
-    // merge's order) is row pos of the batch row's list; this split keeps
-    // [r0, r1) of it. The selection never leaves an empty slot.
-    Scratch& sc = *reinterpret_cast<Scratch*>(lds);
+    // A split that starts with window tiles copies the first two of them
+    // now (their rows are known), so they land while the selection runs.
+    // The selection then works in the third tile slot, which the tile loop
+    // takes only after its first barrier; the q loads are in flight too.
+    // Winner number pos (in the cut merge's order) is selected row pos of
+    // the batch row; this split keeps [sbase, sbase + nsel) of them. The
+    // selection never leaves an empty slot.
+    {
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const uint32_t rbase = lds_byte_addr(Rbuf);
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        if (tile < wt) {
+#pragma unroll
+          for (int i = 0; i < kRowsPerWave; ++i) {
+            const int rr = wv * kRowsPerWave + i;
+            const int v = win_enc(tile * kTile + rr);
+            const uint16_t* src = v == kEmpty ? kvb : winb + (size_t)(-v - 1) * D;
+            const uint32_t at = __builtin_amdgcn_readfirstlane(
+                rbase + (uint32_t)((tile * kTile + rr) * ROW_WORDS * 4));
+            if (ROW_LANES == kWave || lane < ROW_LANES) dma_row16(src + (lane % ROW_LANES) * 8, at);
+          }
+        }
+      }
+    }
+    static_assert(sizeof(Scratch) <= kTile * ROW_WORDS * sizeof(uint32_t), "the selection fits a tile slot");
+    Scratch& sc = *reinterpret_cast<Scratch*>(lds + 2 * kTile * ROW_WORDS);
     const size_t lists = (size_t)b * sel.chunks;
     int32_t* const io = (split == 0 && hg == 0) ? sel.idx_out + (size_t)b * k : nullptr;
     uint64_t cv[SEL];
@@ -184,22 +228,23 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       for (int j = 0; j < SEL; ++j) {
         if (cv[j] && cv[j] >= thr && pos < (uint32_t)k) {
           const int p = (int)min(composite_pos(cv[j]), (uint32_t)(N - 1));
-          if ((int)pos >= r0 && (int)pos < r1) srow[pos - r0] = p;
+          if ((int)pos >= sbase && (int)pos < sbase + nsel) srow[wrows + (int)pos - sbase] = p;
           if (io) io[pos] = p;
           ++pos;
         }
       }
     } else {
-      int32_t* const sr = srow;
-      const int lo = r0, hi = r1;
+      int32_t* const sr = srow + wrows;
+      const int lo = sbase, hi = sbase + nsel;
       row_topk_from_scores(sel.scores + (size_t)b * N, N, k,
                            [sr, lo, hi, io](uint32_t at, int i) {
                              if ((int)at >= lo && (int)at < hi) sr[at - lo] = i;
                              if (io) io[at] = i;
                            }, sc);
     }
-    for (int r = max(r0, k) + tid; r < r1; r += THREADS) srow[r - r0] = -(r - k) - 1;
-    if (lane == 0) wempty[wave] = 0;
+    for (int i = tid; i < wrows; i += THREADS) srow[i] = win_enc(i);
+    for (int i = wrows + nsel + tid; i < r1; i += THREADS) srow[i] = kEmpty;
+    if (lane == 0) wempty[wave] = has_pad ? 1 : 0;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the selection's stores
     lds_barrier();  // the row list is complete and the tile slots are free
   }
@@ -260,9 +305,9 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     }
   };
 
-  if constexpr (SEL > 0) {
-    if (ntiles > 0) dma(0);
-    if (ntiles > 1) dma(1);
+  if constexpr (SEL > 0) {  // the first two tiles, less the window tiles already copied
+    if (ntiles > 0 && wt < 1) dma(0);
+    if (ntiles > 1 && wt < 2) dma(1);
   }
 
   // Software pipeline over tiles: iteration t computes the (partial) logits
@@ -285,34 +330,30 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
     xbuf[(0 * WAVES + wave) * 2 * kWave + kWave + lane] = s1;
   }
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = r0 + t * kTile;
-    // Tile t+1 has landed once no copy issued after it is outstanding (tile
-    // t+2 is issued below). The barrier also publishes the partial logits of
-    // tile t and tells that every wave finished tile t-1, whose slot then
-    // takes tile t+2.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    if (t + 2 < ntiles) dma(t + 2);
+  // Adds the partner wave's half of tile t's logits to s0, s1: the two
+  // waves of a head group each hold half of the dot products, and both form
+  // the same sums (addition is commutative), so they run identical softmax
+  // states.
+  auto exchange = [&](int t) __attribute__((always_inline)) {
     if (DSPLIT > 1) {
-      // The two waves of a head group each hold half of the dot products;
-      // each adds the other's half. Both form the same sums (addition is
-      // commutative), so they run identical softmax states.
       const int partner = (DSPLIT - 1 - dh) * HG + hq;
       const f32x4* xb = xbuf + ((t & 1) * WAVES + partner) * 2 * kWave;
       s0 += xb[lane];
       s1 += xb[kWave + lane];
     }
-    const f32x4 c0 = s0, c1 = s1;  // logits of tile t
-    if (t + 1 < ntiles) {
-      partial_s(t + 1, s0, s1);
-      if (DSPLIT > 1) {
-        f32x4* xw = xbuf + (((t + 1) & 1) * WAVES + wave) * 2 * kWave;
-        xw[lane] = s0;
-        xw[kWave + lane] = s1;
-      }
+  };
+  // This wave's partial logits of tile t into s0, s1, and to its partner.
+  auto next_logits = [&](int t) __attribute__((always_inline)) {
+    partial_s(t, s0, s1);
+    if (DSPLIT > 1) {
+      f32x4* xw = xbuf + ((t & 1) * WAVES + wave) * 2 * kWave;
+      xw[lane] = s0;
+      xw[kWave + lane] = s1;
     }
-
+  };
+  // Softmax and O^T += R^T P^T of tile t, from its logits c0, c1.
+  auto finish = [&](int t, const f32x4 c0, const f32x4 c1) __attribute__((always_inline)) {
+    const int t0 = r0 + t * kTile;
     float z[8];
     float mx = -INFINITY;
     if (t0 + kTile <= r1) {  // a full tile (uniform)
@@ -397,6 +438,36 @@ __global__ __launch_bounds__(HG * DSPLIT * kWave) void sparse_attend_kernel(
       const i16x8 cat = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, cat), pb, o[dt]);
     }
+  };
+
+  int t_first = 0;
+  if (SEL > 0 && wt > 0 && ntiles > 1) {
+    // A split that starts with a window tile copied it before its selection;
+    // it finishes that tile before waiting for tile 1, whose copies went out
+    // after the selection, so their latency overlaps tile 0's softmax and
+    // P.V instead of delaying them.
+    lds_barrier();  // publishes tile 0's partial logits
+    exchange(0);
+    const f32x4 c0 = s0, c1 = s1;
+    finish(0, c0, c1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // tile 1 visible; every wave is done with tile 0's logits
+    if (2 < ntiles) dma(2);
+    next_logits(1);
+    t_first = 1;
+  }
+  for (int t = t_first; t < ntiles; ++t) {
+    // Tile t+1 has landed once no copy issued after it is outstanding (tile
+    // t+2 is issued below). The barrier also publishes the partial logits of
+    // tile t and tells that every wave finished tile t-1, whose slot then
+    // takes tile t+2.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (t + 2 < ntiles) dma(t + 2);
+    exchange(t);
+    const f32x4 c0 = s0, c1 = s1;  // logits of tile t
+    if (t + 1 < ntiles) next_logits(t + 1);
+    finish(t, c0, c1);
   }
 
   // Full sum over the four lane groups that share head m.
@@ -575,7 +646,7 @@ hipError_t launch_attend_t(const uint16_t* q, const uint16_t* kv, const int32_t*
   const int grid = (nitems + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(WAVES * kWave), lds, st, q, kv, idx, win, out, po,
                      pml, sink, d.n, d.topk, d.window, d.q_heads, d.scale, p.rows_per_split,
-                     p.splits, nitems, hgroups, tokens, sel);
+                     p.sel_rows, p.splits, nitems, hgroups, tokens, sel);
   return hipGetLastError();
 }
 
@@ -599,18 +670,32 @@ hipError_t launch_combine(uint16_t* po, float* pml, const float* sink, uint16_t*
 
 AttendPlan plan_attend(const dsa_dims_t& d) {
   AttendPlan p{};
-  const int rows = d.topk + d.window;
   p.heads_per_wg = (d.q_heads % 64 == 0) ? 64 : (d.q_heads % 32 == 0 ? 32 : 16);
   const int hgroups = d.q_heads / p.heads_per_wg;
-  const int tiles = (rows + kTile - 1) / kTile;
-  // About 256 workgroups in total, at least one tile per split.
+  // About 256 workgroups in total. The selected rows are shared out in whole
+  // tiles, the same number per split, and the window's tiles are dealt round
+  // robin to the splits after the last one that holds selected rows; every
+  // split holds at least one tile, and at most kMaxSplitTiles (the row list
+  // in LDS). At the production shape (k = 1024, W = 128, 8 splits) each
+  // split holds 4 tiles of selected rows and splits 0-3 one window tile
+  // more, which they copy while they select their rows.
+  const int tiles_sel = (d.topk + kTile - 1) / kTile;
+  const int tiles_win = (d.window + kTile - 1) / kTile;
   long long want = (256 + (long long)d.batch * hgroups - 1) / ((long long)d.batch * hgroups);
-  if (want > tiles) want = tiles;
+  if (want > tiles_sel + tiles_win) want = tiles_sel + tiles_win;
   if (want < 1) want = 1;
-  int tiles_per_split = (tiles + (int)want - 1) / (int)want;
-  if (tiles_per_split > kMaxSplitTiles) tiles_per_split = kMaxSplitTiles;  // bounds the row list in LDS
-  p.rows_per_split = tiles_per_split * kTile;
-  p.splits = (rows + p.rows_per_split - 1) / p.rows_per_split;
+  for (int S = (int)want;; ++S) {
+    const int tps = (tiles_sel + S - 1) / S;
+    const int s_sel = (tiles_sel + tps - 1) / tps;
+    const int splits = S < s_sel + tiles_win ? S : s_sel + tiles_win;
+    const int wmax = (tiles_win + splits - 1) / splits;
+    if (tps + wmax <= kMaxSplitTiles || S >= tiles_sel + tiles_win) {
+      p.sel_rows = tps * kTile;
+      p.splits = splits;
+      p.rows_per_split = (tps + wmax) * kTile;
+      break;
+    }
+  }
   if (p.splits > 1) {
     p.part_o_off = 0;
     p.part_ml_off = align_up((size_t)d.batch * p.splits * d.q_heads * d.head_dim * sizeof(uint16_t), 256);

@@ -86,6 +86,12 @@ def test_small_steps(shape):
     workloads.StepShape(B=16, N=16384, H_I=64, D_I=128, k=256, W=0, H_q=64, D=512),
     workloads.StepShape(B=3, N=16000, H_I=16, D_I=128, k=64, W=5, H_q=128, D=512),
     workloads.StepShape(B=12, N=16384, H_I=64, D_I=128, k=1024, W=128, H_q=128, D=512),
+    # two window tiles on every split (both copied before the selection)
+    workloads.StepShape(B=16, N=16384, H_I=64, D_I=128, k=1024, W=512, H_q=128, D=512),
+    # a last window tile of 4 rows (the rest empty slots)
+    workloads.StepShape(B=16, N=16384, H_I=64, D_I=128, k=1024, W=100, H_q=128, D=512),
+    # 16 splits of 64 selected rows, the last holding 40; window tiles on splits 0 and 1
+    workloads.StepShape(B=8, N=16384, H_I=64, D_I=128, k=1000, W=40, H_q=128, D=512),
 ])
 def test_steps_selecting_inside_attention(shape):
     inp = workloads.step_inputs(shape, 32000 + shape.N + shape.k, device=DEV)
